@@ -1,0 +1,182 @@
+/*
+ * tsr.h - C ABI of the batched logits-to-token sampler for AMD Instinct MI355X
+ * (gfx950): temperature, softmax, top-k, top-p, min-p, renormalisation and a
+ * Philox draw per row, and the speculative-decoding verify step.
+ *
+ * Pages this interface implements:
+ *  [P1] fareedkhan-dev.github.io "Inference: Sampling, the KV Cache,
+ *       Speculative Decoding and int8" - "Picking the next token" (the knobs
+ *       and their order, the min-p rule), "Speculative decoding".
+ *  [P2] gowda.ai "Chapter 39 Decoding & Speculative Sampling" - 39.1 (greedy),
+ *       39.2 (filters as transforms, eq. 39.2, Listing 39.2), 39.3 (an empty
+ *       allowed set is an invalid state), 39.4 (eqs. 39.3-39.4, Listing 39.4).
+ *  [P3] brentwoodlivery.com "Speculative decoding - Hinglish notes" - "The
+ *       Algorithm (Step-by-Step)", "Batching Speculation", "Temperature and
+ *       Sampling".
+ *  [P4] scratchllm.com "Efficient Inference & Compression" - "Speculative
+ *       decoding".
+ *  [P5] legost.in "Choosing the next word" - "Temperature", "Cutting off the
+ *       tail: top-k and top-p", "Where the randomness comes from".
+ *
+ * Conventions shared by every call
+ *  - All tensors are caller-owned DEVICE memory on the handle's device. The
+ *    library never allocates, frees or retains them.
+ *  - Calls enqueue work on `hip_stream` (a hipStream_t; NULL = the default
+ *    stream) and return without waiting. Outputs are valid once the stream
+ *    has reached that point.
+ *  - Argument errors are returned synchronously and nothing is enqueued.
+ *    Per-row data errors (NaN/+inf logits, an all -inf row, a draft token out
+ *    of range) are reported per row through a status array, with token -1.
+ *    A failed launch returns TSR_EDEVICE. No C++ exception crosses this ABI.
+ *  - Logits are float32 or bfloat16, row-major; each row holds `vocab`
+ *    elements. Pointers must be aligned to the element size; rows whose
+ *    address is 16-byte aligned are read with 128-bit loads.
+ *  - A handle is not thread-safe. Two calls on one handle may run on different
+ *    streams only if they are not verify calls (verify uses per-handle
+ *    workspace).
+ */
+#ifndef TSR_H_
+#define TSR_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tsr_ctx* tsr_handle;
+
+/* Return codes. */
+enum {
+  TSR_OK = 0,
+  TSR_EINVAL = 1,        /* bad argument: null pointer, size or parameter out of range */
+  TSR_ENOMEM = 2,        /* workspace allocation failed in sampler_init */
+  TSR_EDEVICE = 3,       /* HIP runtime error (device selection, launch) */
+  TSR_EUNSUPPORTED = 4   /* a size this build has no kernel for */
+};
+
+/* Element types of the logits. */
+enum { TSR_F32 = 0, TSR_BF16 = 1 };
+
+/* How top-p combines with top-k [P2 Listing 39.2 vs P5's generation loop].
+ * JOINT: every filter reads the same post-temperature p; the kept set is the
+ *   intersection of the filters' sets and is renormalised once (eq. 39.2).
+ * SEQUENTIAL: top-p measures mass relative to the tokens top-k kept. */
+enum { TSR_JOINT = 0, TSR_SEQUENTIAL = 1 };
+
+/* Per-row status. */
+enum {
+  TSR_ROW_OK = 0,
+  TSR_ROW_NONFINITE = 1, /* the row holds NaN or +inf */
+  TSR_ROW_EMPTY = 2,     /* every logit is -inf: the kept set is empty [P2 39.3] */
+  TSR_ROW_BADTOKEN = 3   /* verify only: a draft token outside [0, vocab) */
+};
+
+/* Sampling parameters, one set per call [P1 "Picking the next token"].
+ *  temperature: 0 = greedy (the lowest token id among the maximal logits);
+ *               otherwise >= 1e-30, and p = softmax(logits / temperature).
+ *               Not clamped. Negative or non-finite values are TSR_EINVAL.
+ *  top_k:       keep every token with fewer than top_k strictly larger
+ *               logits (ties with the k-th value stay); <= 0 or >= vocab: off.
+ *  top_p:       keep the tie groups, in descending logit order, whose mass
+ *               strictly above them is below top_p (times the top-k kept mass
+ *               in SEQUENTIAL mode); the top group always stays. >= 1: off;
+ *               < 0 or non-finite: TSR_EINVAL.
+ *  min_p:       keep p_i >= min_p * max_j p_j; active iff 0 < min_p < 1.
+ *  filter_mode: TSR_JOINT or TSR_SEQUENTIAL.
+ * The kept set S always has the form {i : logit_i >= tau} and excludes -inf
+ * logits; the draw renormalises over S (eq. 39.2). */
+typedef struct {
+  double temperature;
+  int32_t top_k;
+  double top_p;
+  double min_p;
+  int32_t filter_mode;
+} tsr_params;
+
+/* Optional per-row diagnostics for sample_rows; every pointer may be NULL.
+ *  status      [rows]        TSR_ROW_* per row.
+ *  kept_count  [rows]        |S| (0 on greedy or bad rows).
+ *  threshold   [rows]        the smallest kept logit (as float32).
+ *  kept_mass   [rows]        sum over S of softmax(logits / T), in (0, 1].
+ *  probs       [rows][vocab] the renormalised distribution p~ (eq. 39.2),
+ *                            0 outside S. Written by an extra pass: meant for
+ *                            validation, not for the timed hot path. */
+typedef struct {
+  int32_t* status;
+  int32_t* kept_count;
+  float* threshold;
+  double* kept_mass;
+  float* probs;
+} tsr_diag;
+
+/* Create a handle on `device` and allocate its workspace once.
+ *  max_rows, max_vocab, max_k bound later calls (max_k: the largest draft
+ *  length K of spec_verify). The Philox4x32-10 key is `seed` (low word first);
+ *  the counter of each draw is (row, position | domain << 16, step low, step
+ *  high), so a token depends only on (seed, row, position, step) and the
+ *  parameters [P5 "Where the randomness comes from"].
+ *  Returns TSR_OK and writes *out, or an error code with *out = NULL. */
+int sampler_init(tsr_handle* out, int device, int max_rows, int max_vocab, int max_k,
+                 uint64_t seed);
+
+/* Free the handle and its workspace. NULL is accepted. Waits for the device. */
+int sampler_destroy(tsr_handle h);
+
+/* Greedy decoding [P2 39.1]: out_tokens[r] = the lowest id among the maximal
+ * logits of row r. logits[r] starts at logits + r * row_stride elements.
+ * out_status (nullable, [rows]) gets TSR_ROW_*; bad rows get token -1. */
+int greedy_argmax(tsr_handle h, const void* logits, int dtype, int rows, int vocab,
+                  int64_t row_stride, int32_t* out_tokens, int32_t* out_status,
+                  void* hip_stream);
+
+/* The sampler [P1 "Picking the next token"; P2 39.2; P5]. For each row r:
+ * z = logits[r] / T, p = softmax(z), the kept set S by top-k, top-p and
+ * min-p (see tsr_params), p~ = p 1{S} / sum_S p (eq. 39.2), then one draw by
+ * inverse CDF: u = w0 * 2^-32 with w0 the first Philox word of counter
+ * (r, 0, step), and the token is the first kept id, in ascending id order,
+ * whose running total of p~ exceeds u. temperature 0 gives greedy_argmax.
+ * logits[r] starts at logits + r * row_stride elements (row_stride >= vocab).
+ * diag may be NULL. */
+int sample_rows(tsr_handle h, const void* logits, int dtype, int rows, int vocab,
+                int64_t row_stride, const tsr_params* params, uint64_t step,
+                int32_t* out_tokens, const tsr_diag* diag, void* hip_stream);
+
+/* The speculative verify step [P3 "The Algorithm"; P1, P4 "Speculative
+ * decoding"; P2 39.4] for `rows` sequences with K drafted tokens each.
+ *  target_logits [rows][K+1][vocab]: the target's logits at the K draft
+ *      positions and at the position after them.
+ *  draft_logits  [rows][K][vocab]:   the draft's logits (not read when the
+ *      temperature is 0).
+ *  draft_tokens  [rows][K] int32:    the drafted ids.
+ * Both distributions go through the same chain (temperature and filters),
+ * p~ and q~. For j = 0..K-1 in order, with (w0, w1) the Philox words of
+ * counter (row, j | 1 << 16, step): keep x_j iff w0 * 2^-32 <
+ * min(1, p~(x_j) / max(q~(x_j), 1e-300)) (eq. 39.3); at the first rejection
+ * emit a draw from max(0, p~ - q~) / Z with w1 (eq. 39.4) and stop; if every
+ * draft is kept emit a bonus draw from the target's row K with w0 of
+ * position K. Greedy (temperature 0): keep x_j iff it is the target's argmax,
+ * emit the argmax at the first mismatch, the bonus is row K's argmax.
+ *  out_tokens   [rows][K+1]: emitted ids, -1 after the last one.
+ *  out_accepted [rows]:      number of drafts kept (0..K).
+ *  out_status   [rows] (nullable): TSR_ROW_*; a bad sequence gets all -1 and 0.
+ * 1 <= K <= max_k (set by sampler_init) and K <= 32. */
+int spec_verify(tsr_handle h, const void* target_logits, const void* draft_logits,
+                int dtype, const int32_t* draft_tokens, int rows, int K, int vocab,
+                const tsr_params* params, uint64_t step, int32_t* out_tokens,
+                int32_t* out_accepted, int32_t* out_status, void* hip_stream);
+
+/* Test hook: out_words[i][0..3] = Philox4x32-10(counters[i][0..3], key = the
+ * handle's seed) for i < n, computed on the device by the same function the
+ * sampler uses. counters and out_words are device memory. */
+int sampler_philox(tsr_handle h, const uint32_t* counters, int n, uint32_t* out_words,
+                   void* hip_stream);
+
+/* Static description of a return code. */
+const char* sampler_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSR_H_ */

@@ -1,0 +1,262 @@
+"""GPU parity of greedy_argmax and sample_rows against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+from tests.gpu_common import (BAND, Tally, compare, device, gpu_available, run_sample, to_dev,
+                              torch)
+
+import oracle
+import token_sampling_row_amd as tsr
+from token_sampling_row_amd import workloads as wl
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def sampler():
+    s = tsr.Sampler(0, max_rows=1 << 17, max_vocab=1 << 18, max_k=8, seed=0x5EED0001)
+    yield s
+    s.close()
+
+
+def make_sampler(seed):
+    return tsr.Sampler(0, max_rows=1 << 17, max_vocab=1 << 18, max_k=8, seed=seed)
+
+
+def vals(data, dtype):
+    return oracle.values_from_stored(data, dtype)
+
+
+def print_case(name, **kw):
+    print(f"[case] {name} " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+# ---------------------------------------------------------------- Philox
+
+def test_philox_words_bit_exact():
+    seed = 0x0123456789ABCDEF
+    rng = np.random.default_rng(1)
+    ctr = rng.integers(0, 2 ** 32, (4096, 4), dtype=np.uint64).astype(np.uint32)
+    print_case("philox", n=4096)
+    with make_sampler(seed) as s:
+        got = s.philox(torch.from_numpy(ctr.view(np.int32)).to(device())).cpu().numpy()
+    want = oracle.philox4x32_10(ctr, oracle.philox.seed_key(seed))
+    assert np.array_equal(got.view(np.uint32), want)
+
+
+# ---------------------------------------------------------------- greedy
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_greedy_configs(sampler, cfg):
+    w = wl.config(cfg)
+    print_case("greedy", cfg=cfg, rows=w.rows, vocab=w.vocab)
+    x = to_dev(w.data, w.dtype)
+    ref = oracle.greedy_batch(vals(w.data, w.dtype))
+    st = torch.empty(w.rows, dtype=torch.int32, device=device())
+    got = sampler.greedy_argmax(x, status=st).cpu().numpy()
+    assert np.array_equal(got, np.array([t for t, _ in ref]))
+    assert (st.cpu().numpy() == 0).all()
+    res = run_sample(sampler, x, {"temperature": 0.0}, 0, diag=True)
+    assert np.array_equal(res["token"], got)
+
+
+def edge_rows(V, rng):
+    rows = []
+    r = rng.normal(0, 1, V).astype(np.float32)
+    rows.append(r.copy())                                  # plain
+    t = np.round(rng.normal(0, 1, V), 1).astype(np.float32)
+    t[V // 3] = t[V - 1] = t.max() + 1                     # tied maximum: lowest id wins
+    rows.append(t)
+    n = r.copy(); n[V // 2] = np.nan; rows.append(n)       # NaN
+    p = r.copy(); p[V - 1] = np.inf; rows.append(p)        # +inf
+    rows.append(np.full(V, -np.inf, np.float32))           # empty
+    m = np.full(V, -np.inf, np.float32); m[V - 1] = -3.0   # one finite logit at the end
+    rows.append(m)
+    z = np.zeros(V, np.float32); z[::2] = -0.0             # +0 and -0 tie
+    rows.append(z)
+    h = np.full(V, -1e30, np.float32); h[0] = 3e38         # extreme finite values
+    rows.append(h)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 8, 63, 64, 1000, 4097, 8192, 32000, 65537, 128256])
+def test_greedy_edges(sampler, dtype, V):
+    rng = np.random.default_rng(V)
+    rows = edge_rows(V, rng)
+    data = wl.f32_to_bf16_bits(rows) if dtype == "bf16" else rows
+    print_case("greedy_edges", dtype=dtype, V=V)
+    x = to_dev(data, dtype)
+    ref = oracle.greedy_batch(vals(data, dtype))
+    st = torch.empty(rows.shape[0], dtype=torch.int32, device=device())
+    got = sampler.greedy_argmax(x, status=st).cpu().numpy()
+    assert got.tolist() == [t for t, _ in ref]
+    assert st.cpu().numpy().tolist() == [s for _, s in ref]
+
+
+def test_greedy_strided_and_unaligned(sampler):
+    rng = np.random.default_rng(3)
+    V = 1001
+    base = rng.normal(0, 1, (16, V + 3)).astype(np.float32)
+    x = to_dev(base, "f32")[:, 1:V + 1]          # row stride V + 3, rows not 16-byte aligned
+    print_case("greedy_strided", V=V)
+    got = sampler.greedy_argmax(x).cpu().numpy()
+    assert got.tolist() == [int(np.argmax(r[1:V + 1])) for r in base]
+
+
+# ---------------------------------------------------------------- sampler, workloads
+
+def check_workload(sampler_seed, w, params, step, rows=None, probs_rows=8):
+    values = vals(w.data, w.dtype)
+    rows = list(range(w.rows)) if rows is None else rows
+    refs = [oracle.sample_row(values[b], params, sampler_seed, b, step) for b in rows]
+    with make_sampler(sampler_seed) as s:
+        x = to_dev(w.data, w.dtype)
+        plain = run_sample(s, x, params, step)                       # as the bench runs it
+        full = run_sample(s, x, params, step, diag=True, probs=True)
+    assert np.array_equal(plain["token"], full["token"])
+    t = compare(full, refs, rows, values, check_probs_rows=set(rows[:probs_rows]))
+    print(f"parity {w.name} {params}: rows={t.rows} in_band={t.in_band} "
+          f"token_excused={t.token_excused} support_excused={t.support_excused}", flush=True)
+    return t
+
+
+def test_config1(sampler):
+    w = wl.config(1)
+    print_case("config1")
+    check_workload(wl.philox_seed(1), w, w.runs[0], 0, probs_rows=64)
+
+
+@pytest.mark.parametrize("run", [1, 2])
+def test_config2_runs(run):
+    w = wl.config(2)
+    print_case("config2", run=run)
+    check_workload(wl.philox_seed(2), w, w.runs[run], run)
+
+
+def test_config3_full_chain():
+    w = wl.config(3)
+    print_case("config3")
+    t = check_workload(wl.philox_seed(3), w, w.runs[0], 0, probs_rows=16)
+    assert t.rows == 256
+
+
+@pytest.mark.parametrize("run", [0, 1])
+def test_config5_sampled_rows(run):
+    w = wl.config(5)
+    print_case("config5", run=run)
+    rows = list(range(0, 1024, 16))
+    check_workload(wl.philox_seed(5), w, w.runs[run], run, rows=rows, probs_rows=4)
+
+
+# ---------------------------------------------------------------- sampler, edges
+
+PARAM_GRID = [
+    dict(temperature=1.0),
+    dict(temperature=0.8, top_k=40, top_p=0.9, min_p=0.05),
+    dict(temperature=0.8, top_k=40, top_p=0.9, min_p=0.05, mode=1),
+    dict(temperature=1.3, top_k=5, top_p=0.5, mode=1),
+    dict(temperature=1.0, top_k=1),
+    dict(temperature=1.0, top_p=0.0),
+    dict(temperature=2.0, top_p=0.95),
+    dict(temperature=0.5, min_p=0.999),
+    dict(temperature=1e-3),
+    dict(temperature=50.0, top_k=3000),
+    dict(temperature=0.9, top_k=2500, top_p=0.99),
+    dict(temperature=1.0, min_p=1e-6),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 2, 3, 7, 100, 1000, 4099, 20000, 70001])
+def test_small_grid(dtype, V):
+    rng = np.random.default_rng(V + (7 if dtype == "bf16" else 0))
+    rows = []
+    for q in (0.0, 0.5):                            # q > 0 quantises logits: many ties
+        for a in (1.0, 0.2):
+            r = -a * np.log(rng.permutation(V) + 1.0) + rng.normal(0, 0.5, V)
+            if q:
+                r = np.round(r / q) * q
+            rows.append(r)
+    r = rng.normal(0, 1, V); r[rng.random(V) < 0.3] = -np.inf; r[0] = 0.0
+    rows.append(r)                                  # -inf holes
+    rows.append(np.zeros(V))                        # one tie group
+    data = np.stack(rows).astype(np.float32)
+    if dtype == "bf16":
+        data = wl.f32_to_bf16_bits(data)
+    values = vals(data, dtype)
+    seed = 1234 + V
+    tally = Tally()
+    with make_sampler(seed) as s:
+        x = to_dev(data, dtype)
+        for i, prm in enumerate(PARAM_GRID):
+            print_case("grid", dtype=dtype, V=V, params=prm)
+            refs = [oracle.sample_row(values[b], prm, seed, b, i) for b in range(len(rows))]
+            got = run_sample(s, x, prm, i, diag=True, probs=True)
+            compare(got, refs, list(range(len(rows))), values, tally=tally)
+    print(f"grid V={V} {dtype}: rows={tally.rows} excused token={tally.token_excused} "
+          f"support={tally.support_excused}")
+
+
+def test_general_path_wide_supports():
+    """Kept sets far larger than the LDS candidate buffer: the histogram path."""
+    rng = np.random.default_rng(5)
+    V = 100000
+    rows = [rng.normal(0, 0.3, V),                          # flat: huge nucleus
+            np.round(rng.normal(0, 0.3, V), 2),             # flat with heavy ties
+            np.concatenate([np.zeros(V // 2), np.full(V - V // 2, -0.001)]),  # 2 big groups
+            -0.05 * np.log(rng.permutation(V) + 1.0)]
+    data = np.stack(rows).astype(np.float32)
+    values = vals(data, "f32")
+    seed = 77
+    grid = [dict(temperature=1.0, top_p=0.9), dict(temperature=1.0, top_p=0.5, mode=1),
+            dict(temperature=1.0, min_p=0.5), dict(temperature=1.0, top_k=30000),
+            dict(temperature=1.0, top_k=60000, top_p=0.7),
+            dict(temperature=1.0, top_k=60000, top_p=0.7, mode=1),
+            dict(temperature=0.7, top_p=0.999, min_p=0.2), dict(temperature=1.0)]
+    with make_sampler(seed) as s:
+        x = to_dev(data, "f32")
+        for i, prm in enumerate(grid):
+            print_case("general", params=prm)
+            refs = [oracle.sample_row(values[b], prm, seed, b, i) for b in range(len(rows))]
+            got = run_sample(s, x, prm, i, diag=True, probs=True)
+            compare(got, refs, list(range(len(rows))), values)
+
+
+def test_bad_rows_and_status(sampler):
+    V = 5000
+    rng = np.random.default_rng(2)
+    rows = edge_rows(V, rng)
+    values = vals(rows, "f32")
+    prm = dict(temperature=0.9, top_k=50, top_p=0.95, min_p=0.1)
+    print_case("bad_rows")
+    refs = [oracle.sample_row(values[b], prm, 0x5EED0001, b, 0) for b in range(len(rows))]
+    got = run_sample(sampler, to_dev(rows, "f32"), prm, 0, diag=True)
+    compare(got, refs, list(range(len(rows))), values)
+
+
+def test_determinism_and_step(sampler):
+    w = wl.config(3, rows=64)
+    x = to_dev(w.data, w.dtype)
+    print_case("determinism")
+    a = sampler.sample_rows(x, {"temperature": 1.5}, 5).cpu().numpy()
+    b = sampler.sample_rows(x, {"temperature": 1.5}, 5).cpu().numpy()
+    c = sampler.sample_rows(x, {"temperature": 1.5}, 6).cpu().numpy()
+    assert np.array_equal(a, b)
+    assert (a != c).mean() > 0.5
+
+
+def test_token_histogram_chi_square(sampler):
+    """Many copies of one row: tokens follow p~ (eq. 39.2)."""
+    from scipy import stats
+    l = np.array([1.0, 0.2, 0.7, -0.4, 0.7, -2.0, 0.3, -1.0, 1.0, 0.0] * 4, dtype=np.float32)
+    prm = dict(temperature=0.9, top_k=12, top_p=0.9, min_p=0.05)
+    s = oracle.support(l.astype(np.float64), oracle.Params.of(prm))
+    n = 1 << 17
+    print_case("chi_square", n=n)
+    x = to_dev(np.tile(l, (n, 1)), "f32")
+    toks = sampler.sample_rows(x, prm, 11).cpu().numpy()
+    obs = np.bincount(toks, minlength=len(l))
+    assert (obs[~s.keep] == 0).all()
+    assert stats.chisquare(obs[s.keep], s.p_tilde[s.keep] * n).pvalue > 1e-4

@@ -1,0 +1,241 @@
+// C-ABI host layer: argument validation, workspace, dispatch and error mapping.
+// Nothing here computes on logits; every step of the path runs in kernels.hip.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/tsr.h"
+#include "kernels.hpp"
+
+struct tsr_ctx {
+  int device;
+  int max_rows;
+  int max_vocab;
+  int max_k;
+  uint64_t seed;
+  tsr::VerifyWs ws;
+  void* ws_block;
+};
+
+namespace {
+
+constexpr double kTemperatureMin = 1e-30;
+constexpr int kMaxDraft = 32;
+
+// Runs f with the handle's device current and restores the caller's device.
+template <class F>
+int on_device(int device, F&& f) {
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return TSR_EDEVICE;
+  if (prev != device && hipSetDevice(device) != hipSuccess) return TSR_EDEVICE;
+  const int rc = f();
+  if (prev != device) (void)hipSetDevice(prev);
+  return rc;
+}
+
+int check_params(const tsr_params* p) {
+  if (!p) return TSR_EINVAL;
+  if (!isfinite(p->temperature) || !isfinite(p->top_p) || !isfinite(p->min_p))
+    return TSR_EINVAL;
+  if (p->temperature < 0.0) return TSR_EINVAL;
+  if (p->temperature > 0.0 && p->temperature < kTemperatureMin) return TSR_EINVAL;
+  if (p->top_p < 0.0) return TSR_EINVAL;
+  if (p->filter_mode != TSR_JOINT && p->filter_mode != TSR_SEQUENTIAL) return TSR_EINVAL;
+  return TSR_OK;
+}
+
+tsr::KParams make_kparams(const tsr_ctx* h, const tsr_params* p, int vocab, uint64_t step,
+                          bool want_z) {
+  tsr::KParams kp{};
+  const double T = p->temperature;
+  if (T == 0.0) {
+    kp.flags = tsr::F_GREEDY;
+    kp.c = 1.0f;
+  } else {
+    kp.c = (float)(1.4426950408889634 / T);
+    kp.cR = kp.c * 16.0f;
+    if (p->top_k > 0 && p->top_k < vocab) {
+      kp.top_k = p->top_k;
+      kp.flags |= tsr::F_K;
+    }
+    if (p->top_p < 1.0) {
+      kp.top_p = p->top_p;
+      kp.flags |= tsr::F_P;
+    }
+    if (p->min_p > 0.0 && p->min_p < 1.0) {
+      kp.minp_off = T * log(p->min_p);
+      kp.flags |= tsr::F_M;
+    }
+    if (p->filter_mode == TSR_SEQUENTIAL) kp.flags |= tsr::F_SEQ;
+    if (want_z) kp.flags |= tsr::F_Z;
+  }
+  kp.key0 = (uint32_t)(h->seed & 0xFFFFFFFFu);
+  kp.key1 = (uint32_t)(h->seed >> 32);
+  kp.step_lo = (uint32_t)(step & 0xFFFFFFFFu);
+  kp.step_hi = (uint32_t)(step >> 32);
+  return kp;
+}
+
+int esize(int dtype) { return dtype == TSR_F32 ? 4 : 2; }
+
+bool elem_aligned(const void* p, int dtype) {
+  return ((uintptr_t)p % (uintptr_t)esize(dtype)) == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sampler_strerror(int code) {
+  switch (code) {
+    case TSR_OK: return "ok";
+    case TSR_EINVAL: return "invalid argument";
+    case TSR_ENOMEM: return "out of device memory";
+    case TSR_EDEVICE: return "HIP runtime error";
+    case TSR_EUNSUPPORTED: return "size not supported by this build";
+    default: return "unknown error code";
+  }
+}
+
+int sampler_init(tsr_handle* out, int device, int max_rows, int max_vocab, int max_k,
+                 uint64_t seed) {
+  if (!out) return TSR_EINVAL;
+  *out = nullptr;
+  if (max_rows < 1 || max_vocab < 1 || max_k < 0 || max_k > kMaxDraft) return TSR_EINVAL;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess) return TSR_EDEVICE;
+  if (device < 0 || device >= ndev) return TSR_EINVAL;
+  tsr_ctx* h = (tsr_ctx*)calloc(1, sizeof(tsr_ctx));
+  if (!h) return TSR_ENOMEM;
+  h->device = device;
+  h->max_rows = max_rows;
+  h->max_vocab = max_vocab;
+  h->max_k = max_k;
+  h->seed = seed;
+  const int rc = on_device(device, [&]() -> int {
+    const size_t slots = (size_t)max_rows * (size_t)(max_k + 1);
+    const size_t bytes = 4 * slots * sizeof(int32_t) + (size_t)max_rows * sizeof(uint32_t);
+    if (hipMalloc(&h->ws_block, bytes) != hipSuccess) return TSR_ENOMEM;
+    if (hipMemset(h->ws_block, 0, bytes) != hipSuccess) return TSR_EDEVICE;
+    if (hipDeviceSynchronize() != hipSuccess) return TSR_EDEVICE;
+    int32_t* base = (int32_t*)h->ws_block;
+    h->ws.acc = base;
+    h->ws.tok = base + slots;
+    h->ws.st_t = base + 2 * slots;
+    h->ws.st_d = base + 3 * slots;
+    h->ws.counter = (uint32_t*)(base + 4 * slots);
+    h->ws.kmax1 = max_k + 1;
+    return TSR_OK;
+  });
+  if (rc != TSR_OK) {
+    if (h->ws_block) (void)hipFree(h->ws_block);
+    free(h);
+    return rc;
+  }
+  *out = h;
+  return TSR_OK;
+}
+
+int sampler_destroy(tsr_handle h) {
+  if (!h) return TSR_OK;
+  const int rc = on_device(h->device, [&]() -> int {
+    if (hipDeviceSynchronize() != hipSuccess) return TSR_EDEVICE;
+    if (h->ws_block && hipFree(h->ws_block) != hipSuccess) return TSR_EDEVICE;
+    return TSR_OK;
+  });
+  free(h);
+  return rc;
+}
+
+int greedy_argmax(tsr_handle h, const void* logits, int dtype, int rows, int vocab,
+                  int64_t row_stride, int32_t* out_tokens, int32_t* out_status,
+                  void* hip_stream) {
+  if (!h || !logits || !out_tokens) return TSR_EINVAL;
+  if (dtype != TSR_F32 && dtype != TSR_BF16) return TSR_EINVAL;
+  if (rows < 0 || rows > h->max_rows || vocab < 1 || vocab > h->max_vocab) return TSR_EINVAL;
+  if (row_stride < vocab || !elem_aligned(logits, dtype)) return TSR_EINVAL;
+  if (vocab > tsr::max_vocab_sample(dtype)) return TSR_EUNSUPPORTED;
+  if (rows == 0) return TSR_OK;
+  const long long sb = (long long)row_stride * esize(dtype);
+  const int aligned = ((uintptr_t)logits % 16 == 0) && (sb % 16 == 0);
+  const int ragged = !aligned || (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;
+  return on_device(h->device, [&]() -> int {
+    const hipError_t e = tsr::launch_greedy(logits, dtype, rows, vocab, sb, aligned, ragged,
+                                            out_tokens, out_status, (hipStream_t)hip_stream);
+    return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
+  });
+}
+
+int sample_rows(tsr_handle h, const void* logits, int dtype, int rows, int vocab,
+                int64_t row_stride, const tsr_params* params, uint64_t step,
+                int32_t* out_tokens, const tsr_diag* diag, void* hip_stream) {
+  if (!h || !logits || !out_tokens) return TSR_EINVAL;
+  if (dtype != TSR_F32 && dtype != TSR_BF16) return TSR_EINVAL;
+  if (rows < 0 || rows > h->max_rows || vocab < 1 || vocab > h->max_vocab) return TSR_EINVAL;
+  if (row_stride < vocab || !elem_aligned(logits, dtype)) return TSR_EINVAL;
+  const int prc = check_params(params);
+  if (prc != TSR_OK) return prc;
+  if (vocab > tsr::max_vocab_sample(dtype)) return TSR_EUNSUPPORTED;
+  if (rows == 0) return TSR_OK;
+  tsr::DiagPtrs dg{};
+  if (diag) {
+    dg.status = diag->status;
+    dg.kept_count = diag->kept_count;
+    dg.threshold = diag->threshold;
+    dg.kept_mass = diag->kept_mass;
+    dg.probs = diag->probs;
+  }
+  const tsr::KParams kp = make_kparams(h, params, vocab, step, dg.kept_mass != nullptr);
+  const long long sb = (long long)row_stride * esize(dtype);
+  const int aligned = ((uintptr_t)logits % 16 == 0) && (sb % 16 == 0);
+  const int ragged = !aligned || (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;
+  return on_device(h->device, [&]() -> int {
+    const hipError_t e = tsr::launch_sample(logits, dtype, rows, vocab, sb, aligned, ragged, kp,
+                                            out_tokens, dg, (hipStream_t)hip_stream);
+    return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
+  });
+}
+
+int spec_verify(tsr_handle h, const void* target_logits, const void* draft_logits, int dtype,
+                const int32_t* draft_tokens, int rows, int K, int vocab,
+                const tsr_params* params, uint64_t step, int32_t* out_tokens,
+                int32_t* out_accepted, int32_t* out_status, void* hip_stream) {
+  if (!h || !target_logits || !draft_tokens || !out_tokens || !out_accepted) return TSR_EINVAL;
+  if (dtype != TSR_F32 && dtype != TSR_BF16) return TSR_EINVAL;
+  if (rows < 0 || rows > h->max_rows || vocab < 1 || vocab > h->max_vocab) return TSR_EINVAL;
+  if (K < 1 || K > h->max_k) return TSR_EINVAL;
+  const int prc = check_params(params);
+  if (prc != TSR_OK) return prc;
+  if (params->temperature > 0.0 && !draft_logits) return TSR_EINVAL;
+  if (!elem_aligned(target_logits, dtype) || (draft_logits && !elem_aligned(draft_logits, dtype)))
+    return TSR_EINVAL;
+  if (vocab > tsr::max_vocab_verify(dtype)) return TSR_EUNSUPPORTED;
+  if (rows == 0) return TSR_OK;
+  const tsr::KParams kp = make_kparams(h, params, vocab, step, false);
+  const long long rb = (long long)vocab * esize(dtype);
+  const int aligned = ((uintptr_t)target_logits % 16 == 0) &&
+                      (!draft_logits || (uintptr_t)draft_logits % 16 == 0) && (rb % 16 == 0);
+  const int ragged = !aligned || (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;
+  return on_device(h->device, [&]() -> int {
+    const hipError_t e = tsr::launch_verify(target_logits, draft_logits, dtype, draft_tokens,
+                                            rows, K, vocab, aligned, ragged, kp, h->ws, out_tokens,
+                                            out_accepted, out_status, (hipStream_t)hip_stream);
+    return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
+  });
+}
+
+int sampler_philox(tsr_handle h, const uint32_t* counters, int n, uint32_t* out_words,
+                   void* hip_stream) {
+  if (!h || !counters || !out_words || n < 0) return TSR_EINVAL;
+  if (n == 0) return TSR_OK;
+  return on_device(h->device, [&]() -> int {
+    const hipError_t e = tsr::launch_philox(counters, n, (uint32_t)(h->seed & 0xFFFFFFFFu),
+                                            (uint32_t)(h->seed >> 32), out_words,
+                                            (hipStream_t)hip_stream);
+    return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,335 @@
+// Device primitives for the gfx950 sampler: element formats, order keys,
+// Philox4x32-10, and wavefront/workgroup reductions and scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsr {
+
+constexpr int kWave = 64;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kPosInf = __builtin_huge_valf();
+constexpr float kFltMax = 3.402823466e+38f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ------------------------------------------------------------------ formats
+// One 16-byte chunk holds 4 float32 or 8 bfloat16 logits.
+template <int DT> struct Fmt;
+template <> struct Fmt<0> { static constexpr int EPC = 4; static constexpr int ESZ = 4; };
+template <> struct Fmt<1> { static constexpr int EPC = 8; static constexpr int ESZ = 2; };
+
+template <int DT>
+__device__ __forceinline__ void unpack(const uint4 r, float* v) {
+  if constexpr (DT == 0) {
+    v[0] = __uint_as_float(r.x); v[1] = __uint_as_float(r.y);
+    v[2] = __uint_as_float(r.z); v[3] = __uint_as_float(r.w);
+  } else {
+    // bf16 -> f32 is exact: the bf16 bits are the top half of the f32 bits.
+    v[0] = __uint_as_float(r.x << 16); v[1] = __uint_as_float(r.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(r.y << 16); v[3] = __uint_as_float(r.y & 0xFFFF0000u);
+    v[4] = __uint_as_float(r.z << 16); v[5] = __uint_as_float(r.z & 0xFFFF0000u);
+    v[6] = __uint_as_float(r.w << 16); v[7] = __uint_as_float(r.w & 0xFFFF0000u);
+  }
+}
+
+// Element-wise load of chunk c of a row (elements [c*EPC, c*EPC+EPC));
+// elements at or past V read as -inf. Used for the ragged tail of a row and
+// for rows that are not 16-byte aligned.
+template <int DT>
+__device__ __forceinline__ uint4 load_chunk_slow(const unsigned char* row, long long c, int V) {
+  constexpr int EPC = Fmt<DT>::EPC;
+  const long long e0 = c * EPC;
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if constexpr (DT == 0) {
+      const long long i = e0 + q;
+      w[q] = i < V ? *reinterpret_cast<const uint32_t*>(row + i * 4) : 0xFF800000u;
+    } else {
+      const long long i0 = e0 + 2 * q, i1 = i0 + 1;
+      const uint32_t lo = i0 < V ? *reinterpret_cast<const uint16_t*>(row + i0 * 2) : 0xFF80u;
+      const uint32_t hi = i1 < V ? *reinterpret_cast<const uint16_t*>(row + i1 * 2) : 0xFF80u;
+      w[q] = lo | (hi << 16);
+    }
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int DT>
+__device__ __forceinline__ uint4 neg_inf_chunk() {
+  return DT == 0 ? make_uint4(0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u)
+                 : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+}
+
+// A chunk of -inf in global memory: chunks past the end of a row load from
+// here, so every chunk of a row is one unconditional 128-bit load.
+static __device__ uint4 g_neg_inf_chunk[2] = {
+    {0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u},
+    {0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u}};
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const unsigned char* row, long long i) {
+  if constexpr (DT == 0) return *reinterpret_cast<const float*>(row + i * 4);
+  return __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(row + i * 2)) << 16);
+}
+
+// ------------------------------------------------------------ order keys
+// Monotone map float -> uint32 (-0 and +0 share a key; larger float, larger key).
+__device__ __forceinline__ uint32_t fkey(float v) {
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key2f(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Relative weight of a logit against the row max M: e = 2^((v - M) * c) with
+// c = log2(e) / T, i.e. exp((v - M) / T) = p_v / p_max. Every mass in the
+// library is a sum of this one expression, so sums formed in different places
+// see identical terms.
+__device__ __forceinline__ float weight(float v, float M, float c) {
+  return __builtin_amdgcn_exp2f((v - M) * c);
+}
+
+// ------------------------------------------------------------ Philox4x32-10
+// Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11): ten
+// rounds of two 32x32->64 products, each high word xored with the other
+// counter words and the key, the key advanced by Weyl constants between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 x, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo_a = 0xD2511F53u * x.x, hi_a = __umulhi(0xD2511F53u, x.x);
+    const uint32_t lo_b = 0xCD9E8D57u * x.z, hi_b = __umulhi(0xCD9E8D57u, x.z);
+    x = make_uint4(hi_b ^ x.y ^ k0, lo_b, hi_a ^ x.w ^ k1, lo_a);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return x;
+}
+
+// ------------------------------------------------------------ wave ops
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+// Butterfly sums: every lane ends with the same value, in the same order.
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ unsigned long long wave_sum(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += (unsigned long long)__shfl_xor((long long)v, o);
+  return v;
+}
+// Inclusive scans (Hillis-Steele) over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+__device__ __forceinline__ unsigned long long wave_incl_scan(unsigned long long v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long t = (unsigned long long)__shfl_up((long long)v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// ------------------------------------------------------------ block ops
+// Scratch for block reductions: one slot per wave (at most 16 waves).
+struct BlockScratch {
+  float f[16];
+  int i[16];
+  uint32_t u[16];
+  double d[16];
+  unsigned long long q[16];
+};
+
+template <int BLOCK>
+__device__ __forceinline__ float block_max(float v, BlockScratch& s) {
+  constexpr int W = BLOCK / kWave;
+  v = wave_max(v);
+  __syncthreads();
+  if (__lane_id() == 0) s.f[threadIdx.x / kWave] = v;
+  __syncthreads();
+  float r = s.f[0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) r = fmaxf(r, s.f[w]);
+  return r;
+}
+template <int BLOCK>
+__device__ __forceinline__ float block_min(float v, BlockScratch& s) {
+  constexpr int W = BLOCK / kWave;
+  v = wave_min(v);
+  __syncthreads();
+  if (__lane_id() == 0) s.f[threadIdx.x / kWave] = v;
+  __syncthreads();
+  float r = s.f[0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) r = fminf(r, s.f[w]);
+  return r;
+}
+template <int BLOCK>
+__device__ __forceinline__ int block_sum(int v, BlockScratch& s) {
+  constexpr int W = BLOCK / kWave;
+  v = wave_sum(v);
+  __syncthreads();
+  if (__lane_id() == 0) s.i[threadIdx.x / kWave] = v;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) r += s.i[w];
+  return r;
+}
+template <int BLOCK>
+__device__ __forceinline__ int block_min(int v, BlockScratch& s) {
+  constexpr int W = BLOCK / kWave;
+  v = wave_min(v);
+  __syncthreads();
+  if (__lane_id() == 0) s.i[threadIdx.x / kWave] = v;
+  __syncthreads();
+  int r = s.i[0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) r = min(r, s.i[w]);
+  return r;
+}
+template <int BLOCK>
+__device__ __forceinline__ int block_max(int v, BlockScratch& s) {
+  constexpr int W = BLOCK / kWave;
+  v = wave_max(v);
+  __syncthreads();
+  if (__lane_id() == 0) s.i[threadIdx.x / kWave] = v;
+  __syncthreads();
+  int r = s.i[0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) r = max(r, s.i[w]);
+  return r;
+}
+template <int BLOCK>
+__device__ __forceinline__ uint32_t block_min_u32(uint32_t v, BlockScratch& s) {
+  constexpr int W = BLOCK / kWave;
+  v = wave_min_u32(v);
+  __syncthreads();
+  if (__lane_id() == 0) s.u[threadIdx.x / kWave] = v;
+  __syncthreads();
+  uint32_t r = s.u[0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) r = min(r, s.u[w]);
+  return r;
+}
+template <int BLOCK>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, BlockScratch& s) {
+  constexpr int W = BLOCK / kWave;
+  v = wave_max_u32(v);
+  __syncthreads();
+  if (__lane_id() == 0) s.u[threadIdx.x / kWave] = v;
+  __syncthreads();
+  uint32_t r = s.u[0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) r = max(r, s.u[w]);
+  return r;
+}
+// Sum in a fixed order (lanes by butterfly, then waves 0..W-1): deterministic.
+template <int BLOCK>
+__device__ __forceinline__ double block_sum(double v, BlockScratch& s) {
+  constexpr int W = BLOCK / kWave;
+  v = wave_sum(v);
+  __syncthreads();
+  if (__lane_id() == 0) s.d[threadIdx.x / kWave] = v;
+  __syncthreads();
+  double r = 0.0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) r += s.d[w];
+  return r;
+}
+// Exclusive scan across the block in thread order; *total gets the sum.
+template <int BLOCK>
+__device__ __forceinline__ int block_excl_scan(int v, int* total, BlockScratch& s) {
+  constexpr int W = BLOCK / kWave;
+  const int inc = wave_incl_scan(v);
+  __syncthreads();
+  if (__lane_id() == kWave - 1) s.i[threadIdx.x / kWave] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+  const int wid = threadIdx.x / kWave;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const int t = s.i[w];
+    if (w < wid) before += t;
+    all += t;
+  }
+  *total = all;
+  return before + inc - v;
+}
+template <int BLOCK>
+__device__ __forceinline__ double block_excl_scan(double v, double* total, BlockScratch& s) {
+  constexpr int W = BLOCK / kWave;
+  const double inc = wave_incl_scan(v);
+  __syncthreads();
+  if (__lane_id() == kWave - 1) s.d[threadIdx.x / kWave] = inc;
+  __syncthreads();
+  double before = 0.0, all = 0.0;
+  const int wid = threadIdx.x / kWave;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const double t = s.d[w];
+    if (w < wid) before += t;
+    all += t;
+  }
+  *total = all;
+  // exclusive prefix = (earlier waves) + (earlier lanes of this wave)
+  const double lane_before = __shfl_up(inc, 1);
+  return before + (__lane_id() == 0 ? 0.0 : lane_before);
+}
+
+}  // namespace tsr

@@ -1,0 +1,23 @@
+// sample_rows kernels for one element type (bf16).
+#include "dispatch.hpp"
+
+namespace tsr {
+
+hipError_t launch_sample_dt1(const unsigned char* p, int rows, int V, long long stride_bytes,
+                              int aligned, int ragged, const KParams& kp, int32_t* out,
+                              const DiagPtrs& dg, hipStream_t s) {
+  const int nc = pick_nc(chunks_per_thread(1, V), kRowNcs, 7);
+#define TSR_CASE(N)                                                                      \
+  case N:                                                                                \
+    hipLaunchKernelGGL((sample_kernel<1, N>), dim3(rows), dim3(kBlock), 0, s, p,        \
+                       stride_bytes, V, aligned, ragged, kp, out, dg);                   \
+    break;
+  switch (nc) {
+    TSR_ROW_NCS(TSR_CASE)
+    default: return hipErrorInvalidValue;
+  }
+#undef TSR_CASE
+  return hipGetLastError();
+}
+
+}  // namespace tsr

@@ -1,0 +1,66 @@
+// Plain structures shared by the C-ABI host layer and the gfx950 kernels, and
+// the launch entry points the host layer calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsr {
+
+// Sampling parameters after host-side validation.
+struct KParams {
+  float c;             // log2(e) / T
+  float cR;            // c * (log-probability bins per unit of log2)
+  double minp_off;     // T * ln(min_p): min-p keeps v >= M + minp_off
+  double top_p;
+  int top_k;           // 0 = off (the host maps k <= 0 and k >= V to 0)
+  int flags;
+  uint32_t key0, key1; // Philox key = seed (low word, high word)
+  uint32_t step_lo, step_hi;
+};
+enum : int {
+  F_GREEDY = 1,   // temperature 0
+  F_K = 2,        // top-k active
+  F_P = 4,        // top-p active
+  F_M = 8,        // min-p active
+  F_SEQ = 16,     // SEQUENTIAL filter mode
+  F_Z = 32,       // the full weight sum is wanted (kept-mass diagnostic)
+};
+
+struct DiagPtrs {
+  int32_t* status;
+  int32_t* kept_count;
+  float* threshold;
+  double* kept_mass;
+  float* probs;
+};
+
+// Per-handle workspace of the verify step: per (sequence, position) results
+// and one arrival counter per sequence (zero between calls).
+struct VerifyWs {
+  int32_t* acc;
+  int32_t* tok;
+  int32_t* st_t;
+  int32_t* st_d;
+  uint32_t* counter;
+  int kmax1;      // max_k + 1: stride of the per-position arrays
+};
+
+int max_vocab_sample(int dtype);
+int max_vocab_verify(int dtype);
+
+// aligned: every row starts on a 16-byte boundary. ragged: a row does not
+// split into whole 16-byte chunks (vocab not a multiple of 4 / 8, or unaligned).
+hipError_t launch_greedy(const void* logits, int dtype, int rows, int V, long long stride_bytes,
+                         int aligned, int ragged, int32_t* out, int32_t* status, hipStream_t s);
+hipError_t launch_sample(const void* logits, int dtype, int rows, int V, long long stride_bytes,
+                         int aligned, int ragged, const KParams& kp, int32_t* out,
+                         const DiagPtrs& dg, hipStream_t s);
+hipError_t launch_verify(const void* tgt, const void* dft, int dtype, const int32_t* xs,
+                         int rows, int K, int V, int aligned, int ragged, const KParams& kp,
+                         const VerifyWs& ws, int32_t* out_tokens, int32_t* out_acc,
+                         int32_t* out_status, hipStream_t s);
+hipError_t launch_philox(const uint32_t* ctr, int n, uint32_t k0, uint32_t k1, uint32_t* out,
+                         hipStream_t s);
+
+}  // namespace tsr
