@@ -264,7 +264,7 @@ struct Resolved {
 template <int BLOCK>
 __device__ __forceinline__ Resolved resolve_sorted(Lds& L, int n, int cnt_above, double mass_above, float M,
                                    float c, bool k_on, int k, bool p_on, double thr,
-                                   bool seq_k, double top_p) {
+                                   bool seq_k, double top_p, float tau_m) {
   static_assert(2 * BLOCK >= kCap, "two candidates per thread must cover the LDS");
   // weights and their exclusive prefix in sorted order (two positions per thread)
   const int p0 = 2 * (int)threadIdx.x, p1 = p0 + 1;
@@ -287,8 +287,10 @@ __device__ __forceinline__ Resolved resolve_sorted(Lds& L, int n, int cnt_above,
                                     (p1 < n && cnt_above + f1 < k ? 1 : 0), L.bs);
     thr_eff = top_p * (mass_above + L.pref[nk]);
   }
+  const uint32_t kmin = fkey(tau_m);
   auto kept = [&](int m, int f) -> int {
     if (m >= n) return 0;
+    if (key_hi(L.key[m]) < kmin) return 0;
     if (k_on && !(cnt_above + f < k)) return 0;
     if (p_on && !(mass_above + L.pref[f] < thr_eff) && key_hi(L.key[m]) != kM) return 0;
     return 1;
@@ -534,7 +536,7 @@ __device__ __forceinline__ void general_cut(const Row<DT, NC, BLOCK>& r, float M
   total = min(total, kCap);
   sort_keys_desc<BLOCK>(L, total);
   const Resolved res = resolve_sorted<BLOCK>(L, total, cnt_above, mass_above, M, c, k_on, k,
-                                             p_on, thr, false, 0.0);
+                                             p_on, thr, false, 0.0, tau_m);
   if (res.n_in > 0) {
     *tau_out = res.tau;
     *kept_out = cnt_above + res.n_in;
@@ -571,10 +573,13 @@ __device__ __forceinline__ Cut row_cut(Row<DT, NC, BLOCK>& r, const KParams& kp,
   const int tid = threadIdx.x;
   const float tau_m = m_on ? ceil_to_float((double)M + kp.minp_off) : kNegInf;
 
-  // ---- fast path: a lower bound Lb <= tau with few logits above it
-  float Lb = tau_m;
+  // ---- fast path: a lower bound Lb <= tau with few logits above it. In
+  // SEQUENTIAL mode top-p measures against the whole top-k set, so min-p may
+  // not narrow the candidates there.
+  const bool seq_kp = seq && k_on && p_on;
+  float Lb = seq_kp ? kNegInf : tau_m;
   if (k_on) {
-    const float lo = fmaxf(tau_m, st.smin);
+    const float lo = fmaxf(Lb, st.smin);
     int ns = 0;
 #pragma unroll
     for (int j = 0; j < NC; ++j) ns += (r.cm[j] >= lo) ? 1 : 0;
@@ -663,7 +668,7 @@ __device__ __forceinline__ Cut row_cut(Row<DT, NC, BLOCK>& r, const KParams& kp,
     sort_keys_desc<BLOCK>(L, total);
     const double thr = p_on ? kp.top_p * st.z : 0.0;
     const Resolved res = resolve_sorted<BLOCK>(L, total, 0, 0.0, M, c, k_on, k, p_on, thr,
-                                               seq, kp.top_p);
+                                               seq, kp.top_p, tau_m);
     cut.tau = res.tau;
     cut.kept = res.n_in;
     cut.zs = res.zs;
