@@ -1,0 +1,257 @@
+"""Throughput of the batched logits-to-token sampler on one MI355X.
+
+A step is one sample_rows call over one batch: temperature, softmax, top-k,
+top-p, min-p, renormalisation (eq. 39.2) and one Philox draw per row. The
+headline workload is 256 rows x 128256 bf16 logits with the full chain
+(T=0.9, top_k=50, top_p=0.95, min_p=0.1). Inputs are synthetic, seeded,
+Zipf-like logits already resident in HBM; eight copies of the batch in eight
+separate allocations are used in turn, so each call reads HBM rather than the
+256 MB last-level cache.
+
+Prints one JSON line. Also times the other workloads (greedy, pure sampling,
+min-p, the verify step, the wide-nucleus batch) and, on the host, the float64
+oracle on a bounded sample of the headline batch.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extra] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
+ROTATE = 8                     # distinct input buffers used in turn
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "token_sampling_row_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if they were taken
+    on the current kernel sources (profiles/traffic_<workload>.json)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def device_batch(torch, w, copies):
+    import numpy as np
+    dev = torch.device("cuda:0")
+    if w.dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(w.data).view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(w.data)).to(dev)
+    return [t.clone() for _ in range(copies)]
+
+
+def time_calls(torch, fn, steps, warmup):
+    """Average GPU time per call with HIP events on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(w, params, seed, budget_s=12.0):
+    """The float64 oracle on the host cores over a bounded sample of the batch."""
+    import multiprocessing as mp
+    cores = min(16, os.cpu_count() or 1)
+    values_rows = list(range(w.rows))
+    ctx = mp.get_context("fork")
+    done, t0 = 0, time.perf_counter()
+    with ctx.Pool(cores, initializer=_pool_init, initargs=(w.data, w.dtype, params, seed)) as pool:
+        while time.perf_counter() - t0 < budget_s:
+            n = sum(pool.map(_oracle_rows, [values_rows[i::cores] for i in range(cores)]))
+            done += n
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} rows of the {w.rows}x{w.vocab} {w.dtype} batch "
+                      f"({done // w.rows} passes, {dt:.1f} s wall on {cores} processes)"}
+
+
+_POOL = {}
+
+
+def _pool_init(data, dtype, params, seed):
+    import oracle
+    _POOL["values"] = oracle.values_from_stored(data, dtype)
+    _POOL["params"] = params
+    _POOL["seed"] = seed
+
+
+def _oracle_rows(rows):
+    import oracle
+    for b in rows:
+        oracle.sample_row(_POOL["values"][b], _POOL["params"], _POOL["seed"], b, 0)
+    return len(rows)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run plain 256 MiB device copies (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the sampler shards by batch row with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import token_sampling_row_amd as tsr
+    from token_sampling_row_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    w3 = wl.config(3)
+    params = w3.runs[0]
+    seed = wl.philox_seed(3)
+    bufs = device_batch(torch, w3, ROTATE)
+    out = torch.empty(w3.rows, dtype=torch.int32, device="cuda:0")
+    sampler = tsr.Sampler(0, max_rows=4096, max_vocab=1 << 18, max_k=8, seed=seed)
+
+    ms = time_calls(torch, lambda i: sampler.sample_rows(bufs[i % ROTATE], params, i, out=out),
+                    args.steps, args.warmup)
+    rows_per_s = w3.rows / (ms * 1e-3)
+    alg_bytes = w3.rows * w3.vocab * 2
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(w3.name)
+
+    extra = {}
+    if not args.no_extra:
+        extra = run_extra(torch, tsr, wl, max(50, args.steps // 4), max(5, args.warmup // 4))
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w3, params, seed)
+
+    line = {
+        "metric": "sampled rows/s + achieved HBM GB/s (% peak), B=256 V=128256 full filter chain",
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "batch256_vocab128256_bf16_full_chain", "rows": w3.rows,
+                   "vocab": w3.vocab, "logits": "bf16", "temperature": 0.9, "top_k": 50,
+                   "top_p": 0.95, "min_p": 0.1, "tokens_per_s": rows_per_s,
+                   "input_buffers": ROTATE},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "kernel": "sample_kernel<bf16, 16>",
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    sampler.close()
+    print(json.dumps(line))
+
+
+def run_extra(torch, tsr, wl, steps, warmup):
+    """Rows/s and GB/s of the other workloads (same timing method)."""
+    res = {}
+    with tsr.Sampler(0, max_rows=4096, max_vocab=1 << 18, max_k=8, seed=wl.philox_seed(2)) as s:
+        w = wl.config(1)
+        bufs = device_batch(torch, w, ROTATE)
+        out = torch.empty(w.rows, dtype=torch.int32, device="cuda:0")
+        ms = time_calls(torch, lambda i: s.sample_rows(bufs[i % ROTATE], w.runs[0], i, out=out),
+                        steps, warmup)
+        res["tiny64_8192_f32_chain"] = _rates(w.rows, w.rows * w.vocab * 4, ms)
+
+        w = wl.config(2)
+        bufs = device_batch(torch, w, ROTATE)
+        out = torch.empty(w.rows, dtype=torch.int32, device="cuda:0")
+        ms = time_calls(torch, lambda i: s.greedy_argmax(bufs[i % ROTATE], out=out), steps, warmup)
+        res["batch256_32000_f32_greedy"] = _rates(w.rows, w.rows * w.vocab * 4, ms)
+        for name, prm in (("pure_T1", w.runs[1]), ("minp_T0.7", w.runs[2])):
+            ms = time_calls(torch, lambda i: s.sample_rows(bufs[i % ROTATE], prm, i, out=out),
+                            steps, warmup)
+            res[f"batch256_32000_f32_{name}"] = _rates(w.rows, w.rows * w.vocab * 4, ms)
+        del bufs
+
+        w = wl.config(4)
+        K = w.extra["K"]
+        dev = torch.device("cuda:0")
+        tg = torch.from_numpy(w.data).to(dev)
+        df = torch.from_numpy(w.extra["draft"]).to(dev)
+        tgs = [tg.clone() for _ in range(ROTATE)]
+        dfs = [df.clone() for _ in range(ROTATE)]
+        # draft tokens drawn from q by the sampler itself, as a draft model would
+        xs = s.sample_rows(df.view(w.rows * K, w.vocab), {"temperature": 1.0}, 777)
+        xs = xs.view(w.rows, K).contiguous()
+        toks = torch.empty(w.rows, K + 1, dtype=torch.int32, device=dev)
+        acc = torch.empty(w.rows, dtype=torch.int32, device=dev)
+        nbytes = w.rows * (2 * K + 1) * w.vocab * 4
+        for name, prm in (("T1", w.runs[0]), ("greedy", w.runs[1])):
+            ms = time_calls(torch, lambda i: s.spec_verify(tgs[i % ROTATE], dfs[i % ROTATE], xs, prm,
+                                                           i, out_tokens=toks, out_accepted=acc),
+                            steps, warmup)
+            a = acc.float().mean().item()
+            r = _rates(w.rows, nbytes if prm["temperature"] else w.rows * (K + 1) * w.vocab * 4, ms)
+            r.update(acceptance_rate=a / K, tokens_per_verify=a + 1,
+                     tokens_per_s=w.rows * (a + 1) / (ms * 1e-3))
+            res[f"verify64_k4_32000_f32_{name}"] = r
+        del tgs, dfs
+
+        w = wl.config(5)
+        bufs = device_batch(torch, w, 2)          # 2 x 311 MB already exceeds the 256 MB cache
+        out = torch.empty(w.rows, dtype=torch.int32, device="cuda:0")
+        for name, prm in (("top_p0.9", w.runs[0]), ("top_k1024", w.runs[1])):
+            ms = time_calls(torch, lambda i: s.sample_rows(bufs[i % 2], prm, i, out=out),
+                            max(20, steps // 4), warmup)
+            res[f"batch1024_151936_bf16_{name}"] = _rates(w.rows, w.rows * w.vocab * 2, ms)
+    return res
+
+
+def _rates(rows, nbytes, ms):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms_per_call": ms, "rows_per_s": rows / (ms * 1e-3), "algorithmic_GB_s": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS}
+
+
+if __name__ == "__main__":
+    main()

@@ -24,10 +24,6 @@ def make_sampler(seed):
     return tsr.Sampler(0, max_rows=1 << 17, max_vocab=1 << 18, max_k=8, seed=seed)
 
 
-# Largest row the register-resident kernels hold: 19 chunks of 16 bytes per thread.
-MAX_VOCAB = {"f32": 19 * 1024 * 4, "bf16": 19 * 1024 * 8}
-
-
 def vals(data, dtype):
     return oracle.values_from_stored(data, dtype)
 
@@ -85,7 +81,8 @@ def edge_rows(V, rng):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("V", [1, 2, 3, 5, 8, 63, 64, 1000, 4097, 8192, 32000, 65537, 128256])
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 8, 63, 64, 1000, 4097, 8192, 32000, 65537, 128256,
+                               200003])
 def test_greedy_edges(sampler, dtype, V):
     rng = np.random.default_rng(V)
     rows = edge_rows(V, rng)
@@ -94,14 +91,25 @@ def test_greedy_edges(sampler, dtype, V):
     x = to_dev(data, dtype)
     ref = oracle.greedy_batch(vals(data, dtype))
     st = torch.empty(rows.shape[0], dtype=torch.int32, device=device())
-    if V > MAX_VOCAB[dtype]:
-        with pytest.raises(tsr.TsrError) as e:
-            sampler.greedy_argmax(x, status=st)
-        assert e.value.code == 4                 # TSR_EUNSUPPORTED
-        return
     got = sampler.greedy_argmax(x, status=st).cpu().numpy()
     assert got.tolist() == [t for t, _ in ref]
     assert st.cpu().numpy().tolist() == [s for _, s in ref]
+
+
+def test_sample_strided_and_unaligned():
+    rng = np.random.default_rng(4)
+    V = 3001
+    base = rng.normal(0, 1.5, (24, V + 5)).astype(np.float32)
+    x = to_dev(base, "f32")[:, 3:V + 3]          # unaligned rows: the streaming kernel
+    values = oracle.values_from_stored(np.ascontiguousarray(base[:, 3:V + 3]), "f32")
+    seed = 5150
+    with make_sampler(seed) as s:
+        for i, prm in enumerate([dict(temperature=0.8, top_k=40, top_p=0.9, min_p=0.05),
+                                 dict(temperature=1.0), dict(temperature=0.0)]):
+            print_case("strided_sample", params=prm)
+            refs = [oracle.sample_row(values[b], prm, seed, b, i) for b in range(24)]
+            got = run_sample(s, x, prm, i, diag=True)
+            compare(got, refs, list(range(24)), values, greedy=prm["temperature"] == 0.0)
 
 
 def test_greedy_strided_and_unaligned(sampler):
@@ -178,7 +186,7 @@ PARAM_GRID = [
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("V", [1, 2, 3, 7, 100, 1000, 4099, 20000, 70001])
+@pytest.mark.parametrize("V", [1, 2, 3, 7, 100, 1000, 4099, 20000, 70001, 131072])
 def test_small_grid(dtype, V):
     rng = np.random.default_rng(V + (7 if dtype == "bf16" else 0))
     rows = []
@@ -208,10 +216,11 @@ def test_small_grid(dtype, V):
           f"support={tally.support_excused}")
 
 
-def test_general_path_wide_supports():
-    """Kept sets far larger than the LDS candidate buffer: the histogram path."""
+@pytest.mark.parametrize("V", [70000, 160001])
+def test_general_path_wide_supports(V):
+    """Kept sets far larger than the LDS candidate buffer (the histogram path),
+    in rows held in registers and in rows too wide for them (streamed)."""
     rng = np.random.default_rng(5)
-    V = 70000
     rows = [rng.normal(0, 0.3, V),                          # flat: huge nucleus
             np.round(rng.normal(0, 0.3, V), 2),             # flat with heavy ties
             np.concatenate([np.zeros(V // 2), np.full(V - V // 2, -0.001)]),  # 2 big groups
@@ -227,7 +236,7 @@ def test_general_path_wide_supports():
     with make_sampler(seed) as s:
         x = to_dev(data, "f32")
         for i, prm in enumerate(grid):
-            print_case("general", params=prm)
+            print_case("general", V=V, params=prm)
             refs = [oracle.sample_row(values[b], prm, seed, b, i) for b in range(len(rows))]
             got = run_sample(s, x, prm, i, diag=True, probs=True)
             compare(got, refs, list(range(len(rows))), values)

@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtsr.so")
 ARCH = os.environ.get("TSR_OFFLOAD_ARCH", "gfx950")
-SOURCES = ["k_greedy.hip", "k_sample_f32.hip", "k_sample_bf16.hip", "k_verify.hip", "api.hip"]
+SOURCES = ["k_sample_bf16.hip", "k_sample_f32.hip", "k_verify_f32.hip", "k_verify_bf16.hip",
+           "k_greedy.hip", "k_misc.hip", "api.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # no packed fp32 instructions (v_pk_add/mul/fma_f32) anywhere
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -34,23 +34,26 @@ __device__ __forceinline__ void unpack(const uint4 r, float* v) {
 }
 
 // Element-wise load of chunk c of a row (elements [c*EPC, c*EPC+EPC));
-// elements at or past V read as -inf. Used for the ragged tail of a row and
-// for rows that are not 16-byte aligned.
+// elements at or past V read as -inf. Branch-free: an element past the end
+// re-reads element V-1 and is replaced by -inf. Used for the ragged tail of a
+// row and for rows that are not 16-byte aligned.
 template <int DT>
 __device__ __forceinline__ uint4 load_chunk_slow(const unsigned char* row, long long c, int V) {
   constexpr int EPC = Fmt<DT>::EPC;
   const long long e0 = c * EPC;
+  const long long last = (long long)V - 1;
   uint32_t w[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if constexpr (DT == 0) {
       const long long i = e0 + q;
-      w[q] = i < V ? *reinterpret_cast<const uint32_t*>(row + i * 4) : 0xFF800000u;
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(row + (i < V ? i : last) * 4);
+      w[q] = i < V ? x : 0xFF800000u;
     } else {
       const long long i0 = e0 + 2 * q, i1 = i0 + 1;
-      const uint32_t lo = i0 < V ? *reinterpret_cast<const uint16_t*>(row + i0 * 2) : 0xFF80u;
-      const uint32_t hi = i1 < V ? *reinterpret_cast<const uint16_t*>(row + i1 * 2) : 0xFF80u;
-      w[q] = lo | (hi << 16);
+      const uint32_t lo = *reinterpret_cast<const uint16_t*>(row + (i0 < V ? i0 : last) * 2);
+      const uint32_t hi = *reinterpret_cast<const uint16_t*>(row + (i1 < V ? i1 : last) * 2);
+      w[q] = (i0 < V ? lo : 0xFF80u) | ((i1 < V ? hi : 0xFF80u) << 16);
     }
   }
   return make_uint4(w[0], w[1], w[2], w[3]);

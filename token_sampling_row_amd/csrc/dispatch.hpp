@@ -6,8 +6,8 @@
 
 namespace tsr {
 
-#define TSR_ROW_NCS(X) X(1) X(2) X(4) X(8) X(12) X(16) X(19)
-#define TSR_VERIFY_NCS(X) X(1) X(2) X(4) X(8)
+#define TSR_ROW_NCS(X) X(1) X(2) X(4) X(8) X(16) X(24) X(32) X(38)
+#define TSR_VERIFY_NCS(X) X(1) X(2) X(4) X(8) X(16)
 
 inline int chunks_per_thread(int dtype, int V) {
   const int epc = dtype == 0 ? 4 : 8;
@@ -21,7 +21,7 @@ inline int pick_nc(int needed, const int* list, int n) {
   return 0;
 }
 
-constexpr int kRowNcs[] = {1, 2, 4, 8, 12, 16, 19};
-constexpr int kVerifyNcs[] = {1, 2, 4, 8};
+constexpr int kRowNcs[] = {1, 2, 4, 8, 16, 24, 32, 38};
+constexpr int kVerifyNcs[] = {1, 2, 4, 8, 16};
 
 }  // namespace tsr

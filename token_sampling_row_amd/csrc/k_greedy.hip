@@ -5,8 +5,17 @@ namespace tsr {
 
 hipError_t launch_greedy(const void* logits, int dtype, int rows, int V, long long stride_bytes,
                          int aligned, int ragged, int32_t* out, int32_t* status, hipStream_t s) {
-  const int nc = pick_nc(chunks_per_thread(dtype, V), kRowNcs, 7);
+  const int nc = pick_nc(chunks_per_thread(dtype, V), kRowNcs, 8);
   const unsigned char* p = static_cast<const unsigned char*>(logits);
+  if (nc == 0 || !aligned) {   // wider than the register file, or unaligned: stream
+    if (dtype == 0)
+      hipLaunchKernelGGL((greedy_kernel_stream<0>), dim3(rows), dim3(kBlock), 0, s, p,
+                         stride_bytes, V, aligned, out, status);
+    else
+      hipLaunchKernelGGL((greedy_kernel_stream<1>), dim3(rows), dim3(kBlock), 0, s, p,
+                         stride_bytes, V, aligned, out, status);
+    return hipGetLastError();
+  }
 #define TSR_CASE(N)                                                                      \
   case N:                                                                                \
     if (dtype == 0)                                                                      \
@@ -24,7 +33,9 @@ hipError_t launch_greedy(const void* logits, int dtype, int rows, int V, long lo
   return hipGetLastError();
 }
 
-int max_vocab_sample(int dtype) { return 19 * kBlock * (dtype == 0 ? 4 : 8); }
-int max_vocab_verify(int dtype) { return 8 * kBlock * (dtype == 0 ? 4 : 8); }
+// Rows stream when they exceed the register file; the bound keeps histogram
+// masses (2^40 fixed point, weights <= 1) inside 64 bits.
+int max_vocab_sample(int) { return 1 << 23; }
+int max_vocab_verify(int dtype) { return 16 * kBlock * (dtype == 0 ? 4 : 8); }
 
 }  // namespace tsr

@@ -6,7 +6,12 @@ namespace tsr {
 hipError_t launch_sample_dt0(const unsigned char* p, int rows, int V, long long stride_bytes,
                               int aligned, int ragged, const KParams& kp, int32_t* out,
                               const DiagPtrs& dg, hipStream_t s) {
-  const int nc = pick_nc(chunks_per_thread(0, V), kRowNcs, 7);
+  const int nc = pick_nc(chunks_per_thread(0, V), kRowNcs, 8);
+  if (nc == 0 || !aligned) {   // wider than the register file, or unaligned: stream
+    hipLaunchKernelGGL((sample_kernel_stream<0>), dim3(rows), dim3(kBlock), 0, s, p,
+                       stride_bytes, V, aligned, kp, out, dg);
+    return hipGetLastError();
+  }
 #define TSR_CASE(N)                                                                      \
   case N:                                                                                \
     hipLaunchKernelGGL((sample_kernel<0, N>), dim3(rows), dim3(kBlock), 0, s, p,        \

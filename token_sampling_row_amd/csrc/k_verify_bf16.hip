@@ -1,0 +1,29 @@
+// Verify-step kernels for one element type (bf16).
+#include "dispatch.hpp"
+
+namespace tsr {
+
+hipError_t launch_verify_dt1(const unsigned char* tp, const unsigned char* dp, const int32_t* xs,
+                             int rows, int K, int V, int aligned, int ragged, const KParams& kp,
+                             const VerifyWs& ws, int32_t* out_tokens, int32_t* out_acc,
+                             int32_t* out_status, hipStream_t s) {
+  const int nc = pick_nc(chunks_per_thread(1, V), kVerifyNcs, 5);
+  const dim3 grid((unsigned)rows * (unsigned)(K + 1));
+#define TSR_CASE(N)                                                                          \
+  case N:                                                                                    \
+    if (aligned)                                                                             \
+      hipLaunchKernelGGL((verify_kernel<1, N, false>), grid, dim3(kBlock), 0, s, tp, dp, xs,  \
+                         K, V, aligned, ragged, kp, ws, out_tokens, out_acc, out_status);    \
+    else                                                                                     \
+      hipLaunchKernelGGL((verify_kernel<1, N, true>), grid, dim3(kBlock), 0, s, tp, dp, xs,   \
+                         K, V, aligned, ragged, kp, ws, out_tokens, out_acc, out_status);    \
+    break;
+  switch (nc) {
+    TSR_VERIFY_NCS(TSR_CASE)
+    default: return hipErrorInvalidValue;
+  }
+#undef TSR_CASE
+  return hipGetLastError();
+}
+
+}  // namespace tsr

@@ -1,75 +1,110 @@
-// gfx950 kernel templates of the sampler: greedy argmax, sample_rows, the speculative
-// verify step, and the Philox test hook. One workgroup of 1024 threads (16
-// wavefronts) per row; the row is held in VGPRs (see row_sampler.hpp).
+// gfx950 kernel templates of the sampler: greedy argmax, sample_rows, the
+// speculative verify step and the Philox test hook. One workgroup of kBlock
+// threads per row. Rows up to 19 chunks per thread stay in VGPRs (row_regs);
+// wider rows stream through the cache hierarchy (row_stream).
 #pragma once
 
-#include "kernels.hpp"
-#include "row_sampler.hpp"
+#include "row_regs.hpp"
+#include "row_stream.hpp"
 
 namespace tsr {
 
-constexpr int kBlock = 1024;
+__device__ __forceinline__ Filters make_filters(const KParams& kp, float M) {
+  Filters f;
+  f.k_on = (kp.flags & F_K) != 0;
+  f.p_on = (kp.flags & F_P) != 0;
+  f.m_on = (kp.flags & F_M) != 0;
+  f.seq = (kp.flags & F_SEQ) != 0;
+  f.k = kp.top_k;
+  f.top_p = kp.top_p;
+  f.tau_m = f.m_on ? ceil_to_float((double)M + kp.minp_off) : kNegInf;
+  return f;
+}
+
+// The row's full weight sum is needed by JOINT top-p (its mass reference) and
+// by the kept-mass diagnostic.
+__device__ __forceinline__ bool wants_z(const KParams& kp) {
+  const bool k_on = kp.flags & F_K, p_on = kp.flags & F_P, seq = kp.flags & F_SEQ;
+  return (kp.flags & F_Z) || (p_on && !(seq && k_on));
+}
+
+__device__ __forceinline__ double draw_uniform(const KParams& kp, uint32_t row, uint32_t pos,
+                                               uint32_t domain, int word) {
+  const uint4 w = philox4x32_10(make_uint4(row, pos | (domain << 16), kp.step_lo, kp.step_hi),
+                                kp.key0, kp.key1);
+  return (double)(word == 0 ? w.x : w.y) * 0x1p-32;
+}
+
+__device__ __forceinline__ void write_row(int row, int tok, int status, int kept, float tmin,
+                                          double kmass, int32_t* out, const DiagPtrs& dg) {
+  if (threadIdx.x == 0) {
+    out[row] = tok;
+    if (dg.status) dg.status[row] = status;
+    if (dg.kept_count) dg.kept_count[row] = kept;
+    if (dg.threshold) dg.threshold[row] = tmin;
+    if (dg.kept_mass) dg.kept_mass[row] = kmass;
+  }
+}
+
+__device__ __forceinline__ void zero_probs(const DiagPtrs& dg, int row, int V) {
+  if (dg.probs) {
+    float* pr = dg.probs + (long long)row * V;
+    for (int i = threadIdx.x; i < V; i += kBlock) pr[i] = 0.0f;
+  }
+}
+
+// Kept set, draw and diagnostics of one row on the streaming path.
+template <int DT>
+__device__ __noinline__ void stream_finish(const StreamRow<DT> s, int row, float M, double Z,
+                                           const KParams kp, const Filters f, double u,
+                                           int32_t* out, const DiagPtrs dg) {
+  const Cut cut = general_stream(s, M, Z, kp.c, kp.cR, f);
+  double zs;
+  const int tok = walk_stream(s, cut.tau, M, kp.c, u, &zs);
+  int kept = cut.kept;
+  float tmin = cut.tau;
+  if (dg.kept_count || dg.threshold) stream_kept_stats(s, cut.tau, &kept, &tmin);
+  write_row(row, tok, 0, kept, tmin, Z > 0.0 ? zs / Z : 0.0, out, dg);
+  if (dg.probs) stream_probs(s, cut.tau, M, kp.c, zs, dg.probs + (long long)row * s.V);
+}
+
+// ---------------------------------------------------------------- greedy
 
 template <int DT, int NC>
 __global__ __launch_bounds__(kBlock) void greedy_kernel(const unsigned char* logits,
                                                         long long stride_bytes, int V,
-                                                        int aligned, int ragged,
-                                                        int32_t* out, int32_t* status) {
-  __shared__ Lds L;
+                                                        int aligned, int ragged, int32_t* out,
+                                                        int32_t* status) {
+  Lds& L = tsr_lds;
   const int row = blockIdx.x;
-  Row<DT, NC, kBlock> r;
-  r.load(logits + (long long)row * stride_bytes, V, aligned != 0, ragged != 0);
-  const RowStats st = row_stats(r, false, 1.0f, L);
+  RegRow<DT, NC> r;
+  r.load(logits + (long long)row * stride_bytes, V, ragged != 0);
+  const RowStats st = reg_stats(r, false, 1.0f, L);
   int tok = -1;
-  if (st.status == 0) tok = row_argmax(r, st.M, L);
+  if (st.status == 0) tok = reg_argmax(r, st.M, L);
   if (threadIdx.x == 0) {
     out[row] = tok;
     if (status) status[row] = st.status;
   }
 }
 
-// Weights of the kept set S = {v >= tau} for the walk; chunks whose maximum is
-// below tau contribute zeros without any exponential.
-template <int DT, int NC>
-struct KeptWeights {
-  const Row<DT, NC, kBlock>& r;
-  float tau, M, c;
-  __device__ __forceinline__ void operator()(int j, float* w) const {
-    constexpr int EPC = Fmt<DT>::EPC;
-    if (r.cm[j] >= tau) {
-      float v[EPC];
-      r.elems(j, v);
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) w[e] = v[e] >= tau ? weight(v[e], M, c) : 0.0f;
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) w[e] = 0.0f;
-    }
+template <int DT>
+__global__ __launch_bounds__(kBlock) void greedy_kernel_stream(const unsigned char* logits,
+                                                               long long stride_bytes, int V,
+                                                               int aligned, int32_t* out,
+                                                               int32_t* status) {
+  const int row = blockIdx.x;
+  const StreamRow<DT> s(logits + (long long)row * stride_bytes, V, aligned != 0);
+  const StreamStats st = stream_stats(s, false, 1.0f);
+  int tok = -1;
+  if (st.status == 0) tok = stream_argmax(s, st.M);
+  if (threadIdx.x == 0) {
+    out[row] = tok;
+    if (status) status[row] = st.status;
   }
-};
-
-// Count and smallest value of S = {v >= tau} (used when a cut left them open).
-template <int DT, int NC>
-__device__ __forceinline__ void kept_stats(const Row<DT, NC, kBlock>& r, float tau, Lds& L, int* count,
-                           float* vmin) {
-  constexpr int EPC = Fmt<DT>::EPC;
-  int n = 0;
-  float mn = kPosInf;
-#pragma unroll
-  for (int j = 0; j < NC; ++j)
-    if (r.cm[j] >= tau) {
-      float v[EPC];
-      r.elems(j, v);
-#pragma unroll
-      for (int e = 0; e < EPC; ++e)
-        if (v[e] >= tau) {
-          ++n;
-          mn = fminf(mn, v[e]);
-        }
-    }
-  *count = block_sum<kBlock>(n, L.bs);
-  *vmin = block_min<kBlock>(mn, L.bs);
 }
+
+// ---------------------------------------------------------------- sample_rows
 
 template <int DT, int NC>
 __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* logits,
@@ -77,54 +112,49 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
                                                         int aligned, int ragged, KParams kp,
                                                         int32_t* out, DiagPtrs dg) {
   constexpr int EPC = Fmt<DT>::EPC;
-  __shared__ Lds L;
+  Lds& L = tsr_lds;
   const int row = blockIdx.x;
-  Row<DT, NC, kBlock> r;
-  r.load(logits + (long long)row * stride_bytes, V, aligned != 0, ragged != 0);
-  if (kp.flags & F_GREEDY) {
-    const RowStats st = row_stats(r, false, 1.0f, L);
-    int tok = -1;
-    if (st.status == 0) tok = row_argmax(r, st.M, L);
-    if (threadIdx.x == 0) {
-      out[row] = tok;
-      if (dg.status) dg.status[row] = st.status;
-      if (dg.kept_count) dg.kept_count[row] = 0;
-      if (dg.threshold) dg.threshold[row] = kNegInf;
-      if (dg.kept_mass) dg.kept_mass[row] = 0.0;
-    }
+  const unsigned char* p = logits + (long long)row * stride_bytes;
+  RegRow<DT, NC> r;
+  r.load(p, V, ragged != 0);
+  const bool greedy = (kp.flags & F_GREEDY) != 0;
+  const RowStats st = reg_stats(r, !greedy && wants_z(kp), kp.c, L);
+  if (st.status != 0) {
+    write_row(row, -1, st.status, 0, kNegInf, 0.0, out, dg);
+    zero_probs(dg, row, V);
     return;
   }
-  const Cut cut = row_cut(r, kp, V, L);
-  if (cut.status != 0) {
-    if (threadIdx.x == 0) {
-      out[row] = -1;
-      if (dg.status) dg.status[row] = cut.status;
-      if (dg.kept_count) dg.kept_count[row] = 0;
-      if (dg.threshold) dg.threshold[row] = kNegInf;
-      if (dg.kept_mass) dg.kept_mass[row] = 0.0;
-    }
-    if (dg.probs) {
-      float* pr = dg.probs + (long long)row * V;
-      for (int i = threadIdx.x; i < V; i += kBlock) pr[i] = 0.0f;
-    }
+  if (greedy) {
+    const int tok = reg_argmax(r, st.M, L);
+    write_row(row, tok, 0, 0, kNegInf, 0.0, out, dg);
     return;
   }
-  const uint4 w = philox4x32_10(make_uint4((uint32_t)row, 0u, kp.step_lo, kp.step_hi),
-                                kp.key0, kp.key1);
-  const double u = (double)w.x * 0x1p-32;
+  const float M = st.M, c = kp.c;
+  const Filters f = make_filters(kp, M);
+  const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);
+  int tok, kept = -1;
+  float tau;
   double zs;
-  const int tok = walk_draw<NC, EPC, kBlock>(KeptWeights<DT, NC>{r, cut.tau, cut.M, kp.c}, u,
-                                             L, &zs);
-  int kept = cut.kept;
-  float tmin = cut.tau;
-  if (dg.kept_count || dg.threshold) kept_stats(r, cut.tau, L, &kept, &tmin);
-  if (threadIdx.x == 0) {
-    out[row] = tok;
-    if (dg.status) dg.status[row] = 0;
-    if (dg.kept_count) dg.kept_count[row] = kept;
-    if (dg.threshold) dg.threshold[row] = tmin;
-    if (dg.kept_mass) dg.kept_mass[row] = cut.z > 0.0 ? zs / cut.z : 0.0;
+  if (!f.k_on && !f.p_on && !f.m_on) {
+    tau = -kFltMax;                       // every finite logit
+    tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs);
+  } else {
+    const FastOut fo = fast_cut(r, V, M, st.smin, st.z, c, f, u, L);
+    if (!fo.ok) {
+      // the candidates did not fit: the streaming path finishes this row (the
+      // registers are dead from here on, so the calls save nothing)
+      stream_finish(StreamRow<DT>(p, V, aligned != 0), row, M, st.z, kp, f, u, out, dg);
+      return;
+    }
+    tau = fo.tau;
+    kept = fo.kept;
+    zs = fo.zs;
+    if (fo.drawn) tok = fo.token;
+    else tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs);
   }
+  float tmin = tau;
+  if (dg.kept_count || dg.threshold) reg_kept_stats(r, tau, L, &kept, &tmin);
+  write_row(row, tok, 0, kept, tmin, st.z > 0.0 ? zs / st.z : 0.0, out, dg);
   if (dg.probs) {
     float* pr = dg.probs + (long long)row * V;
     const double inv = 1.0 / zs;
@@ -135,19 +165,45 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
         const int i = r.base(j) + e;
-        if (i < V)
-          pr[i] = v[e] >= cut.tau ? (float)((double)weight(v[e], cut.M, kp.c) * inv) : 0.0f;
+        if (i < V) pr[i] = v[e] >= tau ? (float)((double)weight(v[e], M, c) * inv) : 0.0f;
       }
     }
   }
 }
 
+// Rows wider than the register file: every pass streams the row.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void sample_kernel_stream(const unsigned char* logits,
+                                                               long long stride_bytes, int V,
+                                                               int aligned, KParams kp,
+                                                               int32_t* out, DiagPtrs dg) {
+  const int row = blockIdx.x;
+  const unsigned char* p = logits + (long long)row * stride_bytes;
+  const StreamRow<DT> s(p, V, aligned != 0);
+  const bool greedy = (kp.flags & F_GREEDY) != 0;
+  const StreamStats st = stream_stats(s, !greedy && wants_z(kp), kp.c);
+  if (st.status != 0) {
+    write_row(row, -1, st.status, 0, kNegInf, 0.0, out, dg);
+    zero_probs(dg, row, V);
+    return;
+  }
+  if (greedy) {
+    write_row(row, stream_argmax(s, st.M), 0, 0, kNegInf, 0.0, out, dg);
+    return;
+  }
+  const Filters f = make_filters(kp, st.M);
+  const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);
+  stream_finish(s, row, st.M, st.z, kp, f, u, out, dg);
+}
+
+// ---------------------------------------------------------------- verify
+
 // Residual weights max(0, p~ - q~) of one verify position (eq. 39.4), both
 // rows resident in this workgroup with the same element layout.
 template <int DT, int NC>
 struct ResidualWeights {
-  const Row<DT, NC, kBlock>& rp;
-  const Row<DT, NC, kBlock>& rq;
+  const RegRow<DT, NC>& rp;
+  const RegRow<DT, NC>& rq;
   float tp, Mp, tq, Mq, c;
   double inv_zp, inv_zq;
   __device__ __forceinline__ void operator()(int j, float* w) const {
@@ -170,34 +226,48 @@ struct ResidualWeights {
   }
 };
 
+struct RowCut {
+  int status;
+  float M;
+  float tau;
+  double zs;     // weight sum over S
+};
+
+// Status, row max and kept set of a resident row, with the exact kept weight.
 template <int DT, int NC>
-__device__ __forceinline__ double kept_mass(const Row<DT, NC, kBlock>& r, float tau, float M, float c, Lds& L) {
-  constexpr int EPC = Fmt<DT>::EPC;
-  double s = 0.0;
-#pragma unroll
-  for (int j = 0; j < NC; ++j)
-    if (r.cm[j] >= tau) {
-      float v[EPC];
-      r.elems(j, v);
-      float t = 0.0f;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) t += v[e] >= tau ? weight(v[e], M, c) : 0.0f;
-      s += (double)t;
-    }
-  return block_sum<kBlock>(s, L.bs);
+__device__ __forceinline__ RowCut verify_row_cut(RegRow<DT, NC>& r, const unsigned char* p,
+                                                 int V, bool aligned, const KParams& kp,
+                                                 Lds& L) {
+  const RowStats st = reg_stats(r, wants_z(kp), kp.c, L);
+  RowCut rc{st.status, st.M, kPosInf, 0.0};
+  if (st.status != 0) return rc;
+  const Filters f = make_filters(kp, st.M);
+  if (!f.k_on && !f.p_on && !f.m_on) {
+    rc.tau = -kFltMax;
+    rc.zs = reg_kept_mass(r, rc.tau, st.M, kp.c, L);
+    return rc;
+  }
+  const FastOut fo = fast_cut(r, V, st.M, st.smin, st.z, kp.c, f, 0.0, L);
+  if (fo.ok) {
+    rc.tau = fo.tau;
+    rc.zs = fo.zs;
+    return rc;
+  }
+  const Cut cut = general_stream(StreamRow<DT>(p, V, aligned), st.M, st.z, kp.c, kp.cR, f);
+  rc.tau = cut.tau;
+  rc.zs = reg_kept_mass(r, rc.tau, st.M, kp.c, L);
+  return rc;
 }
 
-template <int DT, int NC>
+template <int DT, int NC, bool UNALIGNED>
 __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt,
                                                         const unsigned char* dft,
                                                         const int32_t* xs, int K, int V,
                                                         int aligned, int ragged, KParams kp,
-                                                        VerifyWs ws,
-                                                        int32_t* out_tokens,
-                                                        int32_t* out_acc,
-                                                        int32_t* out_status) {
+                                                        VerifyWs ws, int32_t* out_tokens,
+                                                        int32_t* out_acc, int32_t* out_status) {
   constexpr int EPC = Fmt<DT>::EPC;
-  __shared__ Lds L;
+  Lds& L = tsr_lds;
   const int b = blockIdx.x / (K + 1);
   const int j = blockIdx.x - b * (K + 1);
   const long long rowbytes = (long long)V * Fmt<DT>::ESZ;
@@ -205,51 +275,46 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt
   const unsigned char* dp = dft + ((long long)b * K + (j < K ? j : 0)) * rowbytes;
   const bool greedy = (kp.flags & F_GREEDY) != 0;
   const bool with_draft = !greedy && j < K;
-  Row<DT, NC, kBlock> rp, rq;
-  rp.load(tp, V, aligned != 0, ragged != 0);
-  if (with_draft) rq.load(dp, V, aligned != 0, ragged != 0);
+  RegRow<DT, NC> rp, rq;
+  rp.template load<UNALIGNED>(tp, V, ragged != 0);
+  if (with_draft) rq.template load<UNALIGNED>(dp, V, ragged != 0);
   int st_t = 0, st_d = 0, acc = 0, tok = -1;
   const int x = j < K ? xs[(long long)b * K + j] : 0;
   const bool x_ok = x >= 0 && x < V;
   if (greedy) {
-    const RowStats s = row_stats(rp, false, 1.0f, L);
+    const RowStats s = reg_stats(rp, false, 1.0f, L);
     st_t = s.status;
     if (st_t == 0) {
-      tok = row_argmax(rp, s.M, L);
+      tok = reg_argmax(rp, s.M, L);
       acc = (j < K && x == tok) ? 1 : 0;
     }
   } else {
-    const Cut cp = row_cut(rp, kp, V, L);
+    const RowCut cp = verify_row_cut(rp, tp, V, aligned != 0, kp, L);
     st_t = cp.status;
-    const uint4 w = philox4x32_10(make_uint4((uint32_t)b, (uint32_t)j | (1u << 16), kp.step_lo,
-                                             kp.step_hi), kp.key0, kp.key1);
-    const double u0 = (double)w.x * 0x1p-32;
-    const double u1 = (double)w.y * 0x1p-32;
+    const double u0 = draw_uniform(kp, (uint32_t)b, (uint32_t)j, 1u, 0);
+    const double u1 = draw_uniform(kp, (uint32_t)b, (uint32_t)j, 1u, 1);
     if (j == K) {
       if (st_t == 0) {
         double zs;
-        tok = walk_draw<NC, EPC, kBlock>(KeptWeights<DT, NC>{rp, cp.tau, cp.M, kp.c}, u0, L, &zs);
+        tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{rp, cp.tau, cp.M, kp.c}, u0, L, &zs);
       }
     } else {
-      const Cut cq = row_cut(rq, kp, V, L);
+      const RowCut cq = verify_row_cut(rq, dp, V, aligned != 0, kp, L);
       st_d = cq.status;
       if (st_t == 0 && st_d == 0 && x_ok) {
-        const double zp = cp.zs > 0.0 ? cp.zs : kept_mass(rp, cp.tau, cp.M, kp.c, L);
-        const double zq = cq.zs > 0.0 ? cq.zs : kept_mass(rq, cq.tau, cq.M, kp.c, L);
         const float lp = load_elem<DT>(tp, x), lq = load_elem<DT>(dp, x);
-        const double pt = lp >= cp.tau ? (double)weight(lp, cp.M, kp.c) / zp : 0.0;
-        const double qt = lq >= cq.tau ? (double)weight(lq, cq.M, kp.c) / zq : 0.0;
+        const double pt = lp >= cp.tau ? (double)weight(lp, cp.M, kp.c) / cp.zs : 0.0;
+        const double qt = lq >= cq.tau ? (double)weight(lq, cq.M, kp.c) / cq.zs : 0.0;
         const double a = fmin(1.0, pt / fmax(qt, 1e-300));
         acc = u0 < a ? 1 : 0;
         if (!acc) {
           double zr;
-          tok = walk_draw<NC, EPC, kBlock>(
-              ResidualWeights<DT, NC>{rp, rq, cp.tau, cp.M, cq.tau, cq.M, kp.c, 1.0 / zp, 1.0 / zq},
-              u1, L, &zr);
+          tok = walk_regs<NC, EPC>(ResidualWeights<DT, NC>{rp, rq, cp.tau, cp.M, cq.tau, cq.M,
+                                                           kp.c, 1.0 / cp.zs, 1.0 / cq.zs},
+                                   u1, L, &zr);
           if (!(zr > 0.0)) {
             double zs;
-            tok = walk_draw<NC, EPC, kBlock>(KeptWeights<DT, NC>{rp, cp.tau, cp.M, kp.c}, u1, L,
-                                             &zs);
+            tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{rp, cp.tau, cp.M, kp.c}, u1, L, &zs);
           }
         }
       }
@@ -296,7 +361,7 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt
 }
 
 static __global__ void philox_kernel(const uint32_t* ctr, int n, uint32_t k0, uint32_t k1,
-                              uint32_t* out) {
+                                     uint32_t* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
     const uint4 c = make_uint4(ctr[4 * i], ctr[4 * i + 1], ctr[4 * i + 2], ctr[4 * i + 3]);
