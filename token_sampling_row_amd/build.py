@@ -1,7 +1,9 @@
 """Build libtsr.so (the C-ABI sampler library) for gfx950 with hipcc.
 
-Each kernel family is its own translation unit, compiled in parallel; the
-objects are linked into token_sampling_row_amd/libtsr.so in-tree.
+Every kernel instance (element type x chunks per thread) is compiled in a
+generated translation unit of its own, in parallel; the dispatch units and the
+C-ABI host layer only declare them. Everything links into
+token_sampling_row_amd/libtsr.so, in-tree.
 """
 from __future__ import annotations
 
@@ -12,13 +14,17 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
+GEN = os.path.join(BUILD, "gen")
 LIB = os.path.join(HERE, "libtsr.so")
 ARCH = os.environ.get("TSR_OFFLOAD_ARCH", "gfx950")
-SOURCES = ["k_sample_bf16.hip", "k_sample_f32.hip", "k_verify_f32.hip", "k_verify_bf16.hip",
-           "k_greedy.hip", "k_misc.hip", "api.hip"]
-FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+ROW_NCS = (1, 2, 4, 8, 16, 24, 32, 38)      # must match kRowNcs in dispatch.hpp
+VERIFY_NCS = (1, 2, 4, 8, 16)               # must match kVerifyNcs
+DISPATCH = ["k_greedy.hip", "k_sample_f32.hip", "k_sample_bf16.hip", "k_verify_f32.hip",
+            "k_verify_bf16.hip", "k_misc.hip", "api.hip"]
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
          # no packed fp32 instructions (v_pk_add/mul/fma_f32) anywhere
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
@@ -30,13 +36,39 @@ def _hipcc() -> str:
     return exe
 
 
-def _compile(src: str) -> tuple[str, str]:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
-           os.path.join(CSRC, src), "-o", obj]
+def instance_units() -> dict[str, str]:
+    """name -> source of one translation unit per kernel instance."""
+    head = '#define TSR_INSTANCE_UNIT 1\n#include "dispatch.hpp"\nnamespace tsr {\n'
+    units = {}
+    for dt in (0, 1):
+        for nc in ROW_NCS:
+            units[f"i_sample_{dt}_{nc}.hip"] = head + (
+                f"template __global__ void sample_kernel<{dt}, {nc}>(const unsigned char*, "
+                "long long, int, int, int, KParams, int32_t*, DiagPtrs);\n}\n")
+            units[f"i_greedy_{dt}_{nc}.hip"] = head + (
+                f"template __global__ void greedy_kernel<{dt}, {nc}>(const unsigned char*, "
+                "long long, int, int, int, int32_t*, int32_t*);\n}\n")
+        for nc in VERIFY_NCS:
+            for un in ("false", "true"):
+                units[f"i_verify_{dt}_{nc}_{un}.hip"] = head + (
+                    f"template __global__ void verify_kernel<{dt}, {nc}, {un}>(const unsigned char*, "
+                    "const unsigned char*, const int32_t*, int, int, int, int, KParams, VerifyWs, "
+                    "int32_t*, int32_t*, int32_t*);\n}\n")
+        units[f"i_stream_{dt}.hip"] = head + (
+            f"template __global__ void sample_kernel_stream<{dt}>(const unsigned char*, long long, "
+            "int, int, KParams, int32_t*, DiagPtrs);\n"
+            f"template __global__ void greedy_kernel_stream<{dt}>(const unsigned char*, long long, "
+            "int, int, int32_t*, int32_t*);\n}\n")
+    return units
+
+
+def _compile(src_path: str) -> tuple[str, str]:
+    obj = os.path.join(BUILD, os.path.basename(src_path) + ".o")
+    cmd = [_hipcc(), *FLAGS, "-I", CSRC, "-Rpass-analysis=kernel-resource-usage", "-c", src_path,
+           "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {src}:\n{p.stderr[-4000:]}")
+        raise RuntimeError(f"hipcc failed on {src_path}:\n{p.stderr[-4000:]}")
     return obj, p.stderr
 
 
@@ -53,10 +85,20 @@ def spill_report(remarks: str) -> list[str]:
     return bad
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        results = list(ex.map(_compile, SOURCES))
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    os.makedirs(GEN, exist_ok=True)
+    srcs = [os.path.join(CSRC, s) for s in DISPATCH]
+    for name, text in instance_units().items():
+        path = os.path.join(GEN, name)
+        if not os.path.exists(path) or open(path).read() != text:
+            with open(path, "w") as f:
+                f.write(text)
+        srcs.append(path)
+    jobs = jobs or int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))
+    # biggest units first so the pool drains evenly
+    srcs.sort(key=lambda s: (not os.path.basename(s).startswith("i_sample"), s), reverse=False)
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        results = list(ex.map(_compile, srcs))
     objs = [o for o, _ in results]
     remarks = "\n".join(r for _, r in results)
     with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
@@ -69,7 +111,7 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     spills = spill_report(remarks)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} from {len(srcs)} units")
         for s in spills:
             print("  spill:", s)
     return LIB

@@ -6,7 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/tsr.h"
+#include "tsr.h"
 #include "kernels.hpp"
 
 struct tsr_ctx {

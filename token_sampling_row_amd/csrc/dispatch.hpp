@@ -24,4 +24,35 @@ inline int pick_nc(int needed, const int* list, int n) {
 constexpr int kRowNcs[] = {1, 2, 4, 8, 16, 24, 32, 38};
 constexpr int kVerifyNcs[] = {1, 2, 4, 8, 16};
 
+// Each kernel instance is compiled in a translation unit of its own (the
+// build generates them), so the units that launch them only declare them.
+#define TSR_DECLARE_ROW(N)                                                                   \
+  extern template __global__ void sample_kernel<0, N>(const unsigned char*, long long, int,  \
+                                                      int, int, KParams, int32_t*, DiagPtrs); \
+  extern template __global__ void sample_kernel<1, N>(const unsigned char*, long long, int,  \
+                                                      int, int, KParams, int32_t*, DiagPtrs); \
+  extern template __global__ void greedy_kernel<0, N>(const unsigned char*, long long, int,  \
+                                                      int, int, int32_t*, int32_t*);          \
+  extern template __global__ void greedy_kernel<1, N>(const unsigned char*, long long, int,  \
+                                                      int, int, int32_t*, int32_t*);
+#define TSR_DECLARE_VERIFY_DT(D, N, U)                                                        \
+  extern template __global__ void verify_kernel<D, N, U>(                                     \
+      const unsigned char*, const unsigned char*, const int32_t*, int, int, int, int, KParams,  \
+      VerifyWs, int32_t*, int32_t*, int32_t*);
+#define TSR_DECLARE_VERIFY(N)                                                                \
+  TSR_DECLARE_VERIFY_DT(0, N, false) TSR_DECLARE_VERIFY_DT(0, N, true)                       \
+  TSR_DECLARE_VERIFY_DT(1, N, false) TSR_DECLARE_VERIFY_DT(1, N, true)
+#ifndef TSR_INSTANCE_UNIT
+TSR_ROW_NCS(TSR_DECLARE_ROW)
+TSR_VERIFY_NCS(TSR_DECLARE_VERIFY)
+extern template __global__ void sample_kernel_stream<0>(const unsigned char*, long long, int, int,
+                                                        KParams, int32_t*, DiagPtrs);
+extern template __global__ void sample_kernel_stream<1>(const unsigned char*, long long, int, int,
+                                                        KParams, int32_t*, DiagPtrs);
+extern template __global__ void greedy_kernel_stream<0>(const unsigned char*, long long, int, int,
+                                                        int32_t*, int32_t*);
+extern template __global__ void greedy_kernel_stream<1>(const unsigned char*, long long, int, int,
+                                                        int32_t*, int32_t*);
+#endif
+
 }  // namespace tsr
