@@ -77,6 +77,11 @@ __device__ __forceinline__ float load_elem(const unsigned char* row, long long i
   return __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(row + i * 2)) << 16);
 }
 
+// Keeps the scheduler from interleaving consecutive chunk iterations of an
+// unrolled loop over register-resident data; bounded register pressure
+// matters more here than instruction-level overlap across chunks.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // ------------------------------------------------------------ order keys
 // Monotone map float -> uint32 (-0 and +0 share a key; larger float, larger key).
 __device__ __forceinline__ uint32_t fkey(float v) {
@@ -113,79 +118,136 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 x, uint32_t k0, uint32_t k1
 }
 
 // ------------------------------------------------------------ wave ops
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+// Reductions and scans over the 64 lanes of a wavefront with DPP lane moves
+// (a modifier on an ordinary VALU instruction) inside each 16-lane row, and
+// v_readlane across rows: no LDS round trips. Every lane gets the same result,
+// combined in the same order, so float sums are deterministic.
+enum : int {
+  kDppXor1 = 0xB1,      // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,      // quad_perm [2,3,0,1]
+  kDppHalfMirror = 0x141,
+  kDppMirror = 0x140,
+  kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118,
+  kDppBcast15 = 0x142, kDppBcast31 = 0x143,
+  kDppWaveShr1 = 0x138,  // whole-wave shift by one lane (lane 0 reads zero)
+};
+
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWMASK, 0xF, false);
 }
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
-  return v;
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __uint_as_float(dpp_u32<CTRL, ROWMASK>(__float_as_uint(x)));
 }
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long x) {
+  const uint32_t lo = dpp_u32<CTRL, ROWMASK>((uint32_t)x);
+  const uint32_t hi = dpp_u32<CTRL, ROWMASK>((uint32_t)(x >> 32));
+  return ((unsigned long long)hi << 32) | lo;
 }
-__device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double x) {
+  return __longlong_as_double((long long)dpp_u64<CTRL, ROWMASK>((unsigned long long)__double_as_longlong(x)));
 }
-__device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-  return v;
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t x, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, l);
 }
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
+__device__ __forceinline__ float readlane_f32(float x, int l) {
+  return __uint_as_float(readlane_u32(__float_as_uint(x), l));
 }
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long x, int l) {
+  return ((unsigned long long)readlane_u32((uint32_t)(x >> 32), l) << 32) |
+         readlane_u32((uint32_t)x, l);
 }
-// Butterfly sums: every lane ends with the same value, in the same order.
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  return __longlong_as_double((long long)readlane_u64((unsigned long long)__double_as_longlong(x), l));
 }
-__device__ __forceinline__ unsigned long long wave_sum(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += (unsigned long long)__shfl_xor((long long)v, o);
-  return v;
-}
-// Inclusive scans (Hillis-Steele) over the 64 lanes.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
+
+// Lane moves for 32- and 64-bit values.
+template <int CTRL, int ROWMASK = 0xF, class T>
+__device__ __forceinline__ T dpp_t(T x) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, dpp_u32<CTRL, ROWMASK>(__builtin_bit_cast(uint32_t, x)));
+  } else {
+    return __builtin_bit_cast(T, dpp_u64<CTRL, ROWMASK>(__builtin_bit_cast(unsigned long long, x)));
   }
-  return v;
 }
-__device__ __forceinline__ double wave_incl_scan(double v) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double t = __shfl_up(v, o);
-    if (lane >= o) v += t;
+template <class T>
+__device__ __forceinline__ T readlane_t(T x, int l) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, readlane_u32(__builtin_bit_cast(uint32_t, x), l));
+  } else {
+    return __builtin_bit_cast(T, readlane_u64(__builtin_bit_cast(unsigned long long, x), l));
   }
-  return v;
 }
-__device__ __forceinline__ unsigned long long wave_incl_scan(unsigned long long v) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned long long t = (unsigned long long)__shfl_up((long long)v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
+
+// Butterfly inside each 16-lane row, then the four row results in fixed order.
+template <class T, class Op>
+__device__ __forceinline__ T wave_reduce(T x, Op op) {
+  x = op(x, dpp_t<kDppXor1>(x));
+  x = op(x, dpp_t<kDppXor2>(x));
+  x = op(x, dpp_t<kDppHalfMirror>(x));
+  x = op(x, dpp_t<kDppMirror>(x));
+  return op(op(readlane_t(x, 0), readlane_t(x, 16)), op(readlane_t(x, 32), readlane_t(x, 48)));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  return wave_reduce(x, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ float wave_min(float x) {
+  return wave_reduce(x, [](float a, float b) { return fminf(a, b); });
+}
+__device__ __forceinline__ int wave_sum(int x) {
+  return wave_reduce(x, [](int a, int b) { return a + b; });
+}
+__device__ __forceinline__ int wave_min(int x) {
+  return wave_reduce(x, [](int a, int b) { return min(a, b); });
+}
+__device__ __forceinline__ int wave_max(int x) {
+  return wave_reduce(x, [](int a, int b) { return max(a, b); });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  return wave_reduce(x, [](uint32_t a, uint32_t b) { return min(a, b); });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  return wave_reduce(x, [](uint32_t a, uint32_t b) { return max(a, b); });
+}
+__device__ __forceinline__ double wave_sum(double x) {
+  return wave_reduce(x, [](double a, double b) { return a + b; });
+}
+__device__ __forceinline__ unsigned long long wave_sum(unsigned long long x) {
+  return wave_reduce(x, [](unsigned long long a, unsigned long long b) { return a + b; });
+}
+
+// Inclusive scans: shifts by 1, 2, 4, 8 inside rows, then the totals of
+// earlier rows broadcast in (row_bcast:15 into rows 1 and 3, row_bcast:31
+// into rows 2 and 3).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += (int)dpp_u32<kDppShr1>((uint32_t)x);
+  x += (int)dpp_u32<kDppShr2>((uint32_t)x);
+  x += (int)dpp_u32<kDppShr4>((uint32_t)x);
+  x += (int)dpp_u32<kDppShr8>((uint32_t)x);
+  x += (int)dpp_u32<kDppBcast15, 0xA>((uint32_t)x);
+  x += (int)dpp_u32<kDppBcast31, 0xC>((uint32_t)x);
+  return x;
+}
+__device__ __forceinline__ double wave_incl_scan(double x) {
+  x += dpp_f64<kDppShr1>(x);
+  x += dpp_f64<kDppShr2>(x);
+  x += dpp_f64<kDppShr4>(x);
+  x += dpp_f64<kDppShr8>(x);
+  x += dpp_f64<kDppBcast15, 0xA>(x);
+  x += dpp_f64<kDppBcast31, 0xC>(x);
+  return x;
+}
+__device__ __forceinline__ unsigned long long wave_incl_scan(unsigned long long x) {
+  x += dpp_u64<kDppShr1>(x);
+  x += dpp_u64<kDppShr2>(x);
+  x += dpp_u64<kDppShr4>(x);
+  x += dpp_u64<kDppShr8>(x);
+  x += dpp_u64<kDppBcast15, 0xA>(x);
+  x += dpp_u64<kDppBcast31, 0xC>(x);
+  return x;
 }
 
 // ------------------------------------------------------------ block ops
@@ -331,8 +393,7 @@ __device__ __forceinline__ double block_excl_scan(double v, double* total, Block
   }
   *total = all;
   // exclusive prefix = (earlier waves) + (earlier lanes of this wave)
-  const double lane_before = __shfl_up(inc, 1);
-  return before + (__lane_id() == 0 ? 0.0 : lane_before);
+  return before + dpp_t<kDppWaveShr1>(inc);
 }
 
 }  // namespace tsr

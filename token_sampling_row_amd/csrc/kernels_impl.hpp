@@ -132,43 +132,31 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   const float M = st.M, c = kp.c;
   const Filters f = make_filters(kp, M);
   const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);
-  int tok, kept = -1;
-  float tau;
-  double zs;
-  if (!f.k_on && !f.p_on && !f.m_on) {
-    tau = -kFltMax;                       // every finite logit
-    tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs);
-  } else {
+  float tau = -kFltMax;     // no filter: every finite logit
+  int kept = -1, tok = -1;
+  double zs = 0.0;
+  bool drawn = false;
+  if (f.k_on || f.p_on || f.m_on) {
     const FastOut fo = fast_cut(r, V, M, st.smin, st.z, c, f, u, L);
     if (!fo.ok) {
       // the candidates did not fit: the streaming path finishes this row (the
       // registers are dead from here on, so the calls save nothing)
-      stream_finish(StreamRow<DT>(p, V, aligned != 0), row, M, st.z, kp, f, u, out, dg);
+      stream_finish(StreamRow<DT>(p, V, true), row, M, st.z, kp, f, u, out, dg);
       return;
     }
     tau = fo.tau;
     kept = fo.kept;
     zs = fo.zs;
-    if (fo.drawn) tok = fo.token;
-    else tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs);
+    drawn = fo.drawn != 0;
+    tok = fo.token;
   }
+  if (!drawn) tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs);
+  // diagnostics re-read the row (validation outputs, off the timed path)
   float tmin = tau;
-  if (dg.kept_count || dg.threshold) reg_kept_stats(r, tau, L, &kept, &tmin);
+  const StreamRow<DT> s(p, V, true);
+  if (dg.kept_count || dg.threshold) stream_kept_stats(s, tau, &kept, &tmin);
   write_row(row, tok, 0, kept, tmin, st.z > 0.0 ? zs / st.z : 0.0, out, dg);
-  if (dg.probs) {
-    float* pr = dg.probs + (long long)row * V;
-    const double inv = 1.0 / zs;
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      float v[EPC];
-      r.elems(j, v);
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        const int i = r.base(j) + e;
-        if (i < V) pr[i] = v[e] >= tau ? (float)((double)weight(v[e], M, c) * inv) : 0.0f;
-      }
-    }
-  }
+  if (dg.probs) stream_probs(s, tau, M, c, zs, dg.probs + (long long)row * V);
 }
 
 // Rows wider than the register file: every pass streams the row.

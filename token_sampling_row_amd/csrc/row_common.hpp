@@ -93,35 +93,6 @@ __device__ __forceinline__ void mz_combine(float& m, double& z, float m2, double
   z = r;
 }
 
-// ---------------------------------------------------------------- wave sorts
-// Bitonic networks over the 64 lanes of a wavefront (one key per lane).
-__device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long x) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const unsigned long long y = (unsigned long long)__shfl_xor((long long)x, j);
-      const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
-      x = take_max ? (x > y ? x : y) : (x < y ? x : y);
-    }
-  }
-  return x;
-}
-__device__ __forceinline__ unsigned long long wave_sort_asc(unsigned long long x) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const unsigned long long y = (unsigned long long)__shfl_xor((long long)x, j);
-      const bool take_min = ((lane & j) == 0) == ((lane & k) == 0);
-      x = take_min ? (x < y ? x : y) : (x > y ? x : y);
-    }
-  }
-  return x;
-}
-
 // ---------------------------------------------------------------- LDS sort
 // Bitonic sort of key[0, n) into descending order (n <= kCap).
 __device__ __forceinline__ void sort_keys_desc(Lds& L, int n) {
@@ -293,58 +264,59 @@ __device__ __forceinline__ int find_boundary(Lds& L, int cnt_above, double mass_
 
 // Wave 0 resolves up to kWaveCap unsorted candidates key[0, n) (every logit
 // >= the candidate bound, which is <= tau) and draws from S in token-id order.
-// Results go to L.si[0] (token), L.si[1] (|S|), L.sf[0] (tau), L.sd[0] (sum of
-// weights over S). Called by wave 0 only; no barriers inside.
+// Each lane holds one candidate and learns, by reading every other lane
+// (v_readlane, no LDS), how many candidates are strictly larger and their
+// mass; the draw sums, per kept lane, the kept mass at or below its id.
+// Results: L.si[0] token, L.si[1] |S|, L.sf[0] tau, L.sd[1] sum of weights
+// over S. Called by wave 0 only; no barriers inside.
 __device__ __forceinline__ void wave_resolve_draw(Lds& L, int n, float M, float c,
                                                   const Filters& f, double thr_joint,
                                                   double u) {
   const int lane = __lane_id();
-  const bool seq_kp = f.seq && f.k_on && f.p_on;
-  unsigned long long key = lane < n ? L.key[lane] : 0ull;
-  key = wave_sort_desc(key);
   const bool valid = lane < n;
+  const unsigned long long key = valid ? L.key[lane] : 0ull;
   const uint32_t kh = key_hi(key);
   const float v = key2f(kh);
   const uint32_t idx = ~(uint32_t)key;
   const double w = valid ? (double)weight(v, M, c) : 0.0;
-  const uint32_t kh_prev = (uint32_t)__shfl_up((int)kh, 1);
-  const bool start = valid && (lane == 0 || kh_prev != kh);
-  const unsigned long long starts = __ballot(start);
-  const unsigned long long upto = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);
-  const unsigned long long mine = starts & upto;
-  const int first = mine ? 63 - __clzll((long long)mine) : 0;
-  const double incl = wave_incl_scan(w);
-  const double excl_here = __shfl_up(incl, 1);
-  const double excl = lane == 0 ? 0.0 : excl_here;
-  const double mass_gt = __shfl(excl, first);
-  const bool keep_k = !f.k_on || first < f.k;
+  int cnt_gt = 0;
+  double mass_gt = 0.0;
+  for (int j = 0; j < n; ++j) {
+    const uint32_t kj = readlane_u32(kh, j);
+    const double wj = readlane_t(w, j);
+    if (kj > kh) {
+      ++cnt_gt;
+      mass_gt += wj;
+    }
+  }
+  const bool keep_k = !f.k_on || cnt_gt < f.k;
   double thr = thr_joint;
-  if (seq_kp) thr = f.top_p * wave_sum(valid && keep_k ? w : 0.0);
+  if (f.seq && f.k_on && f.p_on) thr = f.top_p * wave_sum(valid && keep_k ? w : 0.0);
   const bool keep = valid && v >= f.tau_m && keep_k &&
                     (!f.p_on || mass_gt < thr || kh == fkey(M));
   const unsigned long long km = __ballot(keep);
   const int n_in = __popcll(km);
-  const double zs = wave_sum(keep ? w : 0.0);
-  const float tau = __shfl(v, n_in > 0 ? n_in - 1 : 0);
-  // draw: the kept entries in ascending token id, running sum against u * total
-  unsigned long long k2 = keep ? (((unsigned long long)idx << 32) | (unsigned)lane) : ~0ull;
-  k2 = wave_sort_asc(k2);
-  const bool kv = k2 != ~0ull;
-  const double w2s = __shfl(w, (int)(k2 & 63ull));
-  const double w2 = kv ? w2s : 0.0;
-  const double C = wave_incl_scan(w2);
-  const double total = __shfl(C, 63);
+  const float tau = key2f(wave_min_u32(keep ? kh : 0xFFFFFFFFu));
+  // draw: running kept mass in ascending token id
+  double C = 0.0;
+  for (int j = 0; j < n; ++j) {
+    if ((km >> j) & 1ull) {
+      const uint32_t ij = readlane_u32(idx, j);
+      const double wj = readlane_t(w, j);
+      if (ij <= idx) C += wj;
+    }
+  }
+  const double total =
+      wave_reduce(keep ? C : 0.0, [](double a, double b) { return a > b ? a : b; });
   const double target = u * total;
-  const unsigned long long hit = __ballot(kv && C > target);
-  const unsigned long long kvm = __ballot(kv);
-  const int last = kvm ? 63 - __clzll((long long)kvm) : 0;
-  const int pick = hit ? __ffsll((long long)hit) - 1 : last;
-  const int token = (int)(uint32_t)(__shfl((long long)k2, pick) >> 32);
+  const bool hit = keep && C > target;
+  const int token = __ballot(hit) ? (int)wave_min_u32(hit ? idx : 0xFFFFFFFFu)
+                                  : (int)wave_max_u32(keep ? idx : 0u);
   if (lane == 0) {
     L.si[0] = token;
     L.si[1] = n_in;
     L.sf[0] = tau;
-    L.sd[0] = zs;
+    L.sd[0] = total;
     L.sd[1] = total;
   }
 }

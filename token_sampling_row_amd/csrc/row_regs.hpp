@@ -20,36 +20,42 @@ struct RegRow {
   float cm[NC];   // chunk maxima; -inf past the end of the row
   float tmax;     // this thread's maximum
 
-  // Whole chunks of a 16-byte aligned row are plain 128-bit loads, all issued
-  // back to back; chunks past the end read a -inf chunk, and a `ragged` row
-  // (vocab not a multiple of the chunk) patches its partial chunk from element
-  // loads. UNALIGNED rows are read element-wise.
+  int nwhole;     // whole 16-byte chunks in the row (chunk ids at or past it are not)
+  uint4 tail;     // the partial chunk, read element-wise, when the row is ragged
+
+  // Whole chunks of a 16-byte aligned row are 128-bit buffer loads off one
+  // resource, all issued back to back with no per-load address registers.
+  // Chunks at or past `nwhole` come back as zeros from the range check and are
+  // replaced in pass A of reg_stats (by -inf, or by `tail` for the partial
+  // chunk of a ragged row), so no wait is forced here. UNALIGNED rows are read
+  // element-wise.
   template <bool UNALIGNED = false>
   __device__ __forceinline__ void load(const unsigned char* p, int V, bool ragged) {
-    constexpr int ESZ = Fmt<DT>::ESZ;
     if constexpr (UNALIGNED) {
+      nwhole = 0x7FFFFFFF;
+      tail = neg_inf_chunk<DT>();
 #pragma unroll
       for (int j = 0; j < NC; ++j)
         raw[j] = load_chunk_slow<DT>(p, (long long)j * kBlock + threadIdx.x, V);
     } else {
-      const uint4* neg = &g_neg_inf_chunk[DT];
+      nwhole = V / EPC;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<unsigned char*>(p), (short)0, nwhole * 16, 0x00020000);
+      const int voff = (int)threadIdx.x * 16;
 #pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const long long c = (long long)j * kBlock + threadIdx.x;
-        const bool whole = (c + 1) * EPC <= V;
-        raw[j] = *(whole ? reinterpret_cast<const uint4*>(p + c * EPC * ESZ) : neg);
-      }
-      if (ragged) {
-        const long long cl = V / EPC;  // the partial chunk, if V % EPC != 0
-        if (cl * EPC < V && (int)(cl % kBlock) == (int)threadIdx.x) {
-          const uint4 patch = load_chunk_slow<DT>(p, cl, V);
-          const int jl = (int)(cl / kBlock);
-#pragma unroll
-          for (int j = 0; j < NC; ++j)
-            if (j == jl) raw[j] = patch;
-        }
-      }
+      for (int j = 0; j < NC; ++j)
+        raw[j] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, j * kBlock * 16, 0));
+      tail = neg_inf_chunk<DT>();
+      if (ragged && nwhole * EPC < V && (nwhole % kBlock) == (int)threadIdx.x)
+        tail = load_chunk_slow<DT>(p, nwhole, V);
     }
+  }
+  // Pass-A fix-up of chunk j (see load).
+  __device__ __forceinline__ uint4 settle(int j, uint4 t) const {
+    const int cid = j * kBlock + (int)threadIdx.x;
+    if (cid >= nwhole) t = cid == nwhole ? tail : neg_inf_chunk<DT>();
+    return t;
   }
   __device__ __forceinline__ int base(int j) const {
     return (j * kBlock + (int)threadIdx.x) * EPC;
@@ -96,55 +102,58 @@ struct RowStats {
   double z;       // sum of weights over the row (when asked for)
 };
 
-// One pass over the registers (overlapping the loads still in flight): chunk
-// maxima, max, NaN/+inf, and optionally the weight sum against a running
-// per-thread maximum, rescaled when it grows. One barrier round combines.
+// Row statistics in two passes over the registers. Pass A runs as the loads
+// land: NaN/+inf detection, chunk maxima, thread max. Pass B (only when the
+// weight sum is wanted) sums 2^((v - m_t) c) against the thread's own max m_t:
+// no running rescale, so every chunk is independent work. One barrier round
+// combines the waves.
 template <int DT, int NC>
 __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_z, float c, Lds& L) {
   constexpr int EPC = Fmt<DT>::EPC;
-  float tmax = kNegInf, smin = kPosInf, mt = kNegInf;
-  double zt = 0.0;
+  float tmax = kNegInf, smin = kPosInf;
   NanAcc<DT> nan;
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
-    const uint4 t = r.packed(j);
+    const uint4 t = r.settle(j, r.packed(j));
+    r.raw[j] = t;
     nan.add(t);
     float v[EPC];
     unpack<DT>(t, v);
-    float m = v[0];
+    float m = fmaxf(v[0], v[1]);
 #pragma unroll
-    for (int e = 1; e < EPC; ++e) m = fmaxf(m, v[e]);
+    for (int e = 2; e < EPC; ++e) m = fmaxf(m, v[e]);
     r.cm[j] = m;
     tmax = fmaxf(tmax, m);
-    if (m > kNegInf) smin = fminf(smin, m);
-    if (need_z && m > kNegInf) {
-      if (m > mt) {
-        zt = (mt > kNegInf) ? zt * (double)weight(mt, m, c) : 0.0;
-        mt = m;
-      }
-      float s = 0.0f;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) s += weight(v[e], mt, c);
-      zt += (double)s;
-    }
+    smin = m > kNegInf ? fminf(smin, m) : smin;
+    sched_fence();
   }
   r.tmax = tmax;
-  // wave level
-  float wm = wave_max(tmax);
-  float ws = wave_min(smin);
-  int wb = __any(nan.nan()) ? 1 : 0;
-  double wz = 0.0;
-  if (need_z) {
-    float m = mt;
-    double z = zt;
+  double zt = 0.0;
+  if (need_z && tmax > kNegInf && tmax < kPosInf) {
+    double acc[2] = {0.0, 0.0};
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float m2 = __shfl_xor(m, o);
-      const double z2 = __shfl_xor(z, o);
-      mz_combine(m, z, m2, z2, c);
+    for (int j = 0; j < NC; ++j) {
+      float v[EPC];
+      r.elems(j, v);
+      float s[EPC / 2];
+#pragma unroll
+      for (int e = 0; e < EPC / 2; ++e)
+        s[e] = weight(v[2 * e], tmax, c) + weight(v[2 * e + 1], tmax, c);
+      float t = s[0];
+#pragma unroll
+      for (int e = 1; e < EPC / 2; ++e) t += s[e];
+      acc[j & 1] += (double)t;
+      sched_fence();
     }
-    wz = z;   // relative to wm
+    zt = acc[0] + acc[1];
   }
+  // wave level
+  const float wm = wave_max(tmax);
+  const float ws = wave_min(smin);
+  const int wb = __any(nan.nan()) ? 1 : 0;
+  double wz = 0.0;
+  if (need_z)   // relative to the wave max
+    wz = wave_sum(tmax > kNegInf && tmax < kPosInf ? zt * (double)weight(tmax, wm, c) : 0.0);
   const int wid = threadIdx.x / kWave;
   __syncthreads();
   if (__lane_id() == 0) L.ws[wid] = WaveStats{wm, ws, wz, wb};
@@ -219,14 +228,14 @@ __device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* tota
     if (lane < NC)
       for (int w = 0; w < kWaves; ++w) sj += L.jsum[w * kWalkBatch + lane];
     const double incl = wave_incl_scan(sj);
-    const double tot = __shfl(incl, 63);
+    const double tot = readlane_t(incl, 63);
     const double target = u * tot;
     const double excl = incl - sj;
     const unsigned long long hit = __ballot(sj > 0.0 && target < incl);
     const unsigned long long nz = __ballot(sj > 0.0);
     const int last = nz ? 63 - __clzll((long long)nz) : 0;
     const int jstar = hit ? __ffsll((long long)hit) - 1 : last;
-    const double r1 = hit ? target - __shfl(excl, jstar) : kPosInf;
+    const double r1 = hit ? target - readlane_t(excl, jstar) : kPosInf;
     if (lane == 0) {
       L.si[2] = jstar;
       L.sd[2] = r1;

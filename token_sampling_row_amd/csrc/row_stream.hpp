@@ -349,8 +349,8 @@ __device__ __noinline__ int walk_stream(const StreamRow<DT> s, float tau, float 
       const unsigned long long hit = __ballot(sj > 0.0 && target < incl);
       const unsigned long long nz = __ballot(sj > 0.0);
       const int hl = hit ? __ffsll((long long)hit) - 1 : 0;
-      const double e_at = __shfl(excl, hl);
-      const double batch_end = __shfl(incl, 63);
+      const double e_at = readlane_t(excl, hl);
+      const double batch_end = readlane_t(incl, 63);
       if (lane == 0) {
         L.si[2] = hit ? j0 + hl : -1;
         L.sd[2] = target - e_at;
