@@ -52,6 +52,16 @@ def traffic_from_profiles(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def row_kernel_label(dtype: str, vocab: int) -> str:
+    """Name of the sample_kernel instance a row of this size launches: 512
+    threads per row, 16-byte chunks, the smallest compiled chunk count per
+    thread that covers the row."""
+    epc = 8 if dtype == "bf16" else 4
+    need = -(-(-(-vocab // epc)) // 512)
+    nc = next((n for n in (1, 2, 4, 8, 16, 24, 32, 38) if n >= need), None)
+    return f"sample_kernel<{dtype}, {nc}>" if nc else "sample_kernel_stream"
+
+
 def device_batch(torch, w, copies):
     import numpy as np
     dev = torch.device("cuda:0")
@@ -182,7 +192,7 @@ def main():
                    "input_buffers": ROTATE},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "kernel": "sample_kernel<bf16, 16>",
+                     "traffic": traffic, "kernel": row_kernel_label(w3.dtype, w3.vocab),
                      "algorithmic_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
         "extra": extra,

@@ -125,6 +125,8 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 x, uint32_t k0, uint32_t k1
 enum : int {
   kDppXor1 = 0xB1,      // quad_perm [1,0,3,2]
   kDppXor2 = 0x4E,      // quad_perm [2,3,0,1]
+  kDppQuadMirror = 0x1B,  // quad_perm [3,2,1,0]
+  kDppRor4 = 0x124, kDppRor8 = 0x128, kDppRor12 = 0x12C,  // rotate inside a row
   kDppHalfMirror = 0x141,
   kDppMirror = 0x140,
   kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118,
@@ -248,6 +250,123 @@ __device__ __forceinline__ unsigned long long wave_incl_scan(unsigned long long 
   x += dpp_u64<kDppBcast15, 0xA>(x);
   x += dpp_u64<kDppBcast31, 0xC>(x);
   return x;
+}
+
+// Inclusive max-scans (values must be >= 0: lanes outside a DPP source row
+// read 0).
+__device__ __forceinline__ int wave_incl_max_scan(int x) {
+  x = max(x, (int)dpp_u32<kDppShr1>((uint32_t)x));
+  x = max(x, (int)dpp_u32<kDppShr2>((uint32_t)x));
+  x = max(x, (int)dpp_u32<kDppShr4>((uint32_t)x));
+  x = max(x, (int)dpp_u32<kDppShr8>((uint32_t)x));
+  x = max(x, (int)dpp_u32<kDppBcast15, 0xA>((uint32_t)x));
+  x = max(x, (int)dpp_u32<kDppBcast31, 0xC>((uint32_t)x));
+  return x;
+}
+__device__ __forceinline__ double wave_incl_max_scan(double x) {
+  x = fmax(x, dpp_f64<kDppShr1>(x));
+  x = fmax(x, dpp_f64<kDppShr2>(x));
+  x = fmax(x, dpp_f64<kDppShr4>(x));
+  x = fmax(x, dpp_f64<kDppShr8>(x));
+  x = fmax(x, dpp_f64<kDppBcast15, 0xA>(x));
+  x = fmax(x, dpp_f64<kDppBcast31, 0xC>(x));
+  return x;
+}
+
+// ------------------------------------------------------------ wave sort
+// Value of lane (i ^ D) for D in {1, 2, 4, 8, 16, 32}: DPP inside 16-lane rows,
+// ds_swizzle across the two rows of a 32-lane half, ds_bpermute across halves.
+template <int D>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+  if constexpr (D == 1) {
+    return dpp_u32<kDppXor1>(x);
+  } else if constexpr (D == 2) {
+    return dpp_u32<kDppXor2>(x);
+  } else if constexpr (D == 4) {
+    const uint32_t dn = dpp_u32<kDppRor4>(x), up = dpp_u32<kDppRor12>(x);
+    return (__lane_id() & 4) ? dn : up;
+  } else if constexpr (D == 8) {
+    return dpp_u32<kDppRor8>(x);
+  } else if constexpr (D == 16) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F);  // and 31, xor 16
+  } else {
+    static_assert(D == 32, "lane distance");
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 32u) << 2), (int)x);
+  }
+}
+// Value of lane (i ^ (S - 1)): the mirror image inside aligned blocks of S lanes.
+template <int S>
+__device__ __forceinline__ uint32_t lane_mirror(uint32_t x) {
+  if constexpr (S == 2) {
+    return dpp_u32<kDppXor1>(x);
+  } else if constexpr (S == 4) {
+    return dpp_u32<kDppQuadMirror>(x);
+  } else if constexpr (S == 8) {
+    return dpp_u32<kDppHalfMirror>(x);
+  } else if constexpr (S == 16) {
+    return dpp_u32<kDppMirror>(x);
+  } else if constexpr (S == 32) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x7C1F);  // and 31, xor 31
+  } else {
+    static_assert(S == 64, "block size");
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 63u) << 2), (int)x);
+  }
+}
+// One comparator layer: each lane meets its partner (mirror inside blocks of
+// S lanes when MIRROR, else lane ^ S) and the lower lane of the pair keeps the
+// larger key.
+template <int S, bool MIRROR>
+__device__ __forceinline__ unsigned long long cx_layer(unsigned long long x) {
+  const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+  uint32_t plo, phi;
+  bool low;
+  if constexpr (MIRROR) {
+    plo = lane_mirror<S>(lo);
+    phi = lane_mirror<S>(hi);
+    low = (__lane_id() & (S / 2)) == 0;
+  } else {
+    plo = lane_xor<S>(lo);
+    phi = lane_xor<S>(hi);
+    low = (__lane_id() & S) == 0;
+  }
+  const unsigned long long y = ((unsigned long long)phi << 32) | plo;
+  return ((x > y) != low) ? y : x;
+}
+// Sorts one 64-bit key per lane into descending lane order across the whole
+// wavefront (bitonic network in its mirror form: every comparator keeps the
+// larger key in the lower lane). All 64 lanes must be active.
+__device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long x) {
+  x = cx_layer<2, true>(x);
+  x = cx_layer<4, true>(x);
+  x = cx_layer<1, false>(x);
+  x = cx_layer<8, true>(x);
+  x = cx_layer<2, false>(x);
+  x = cx_layer<1, false>(x);
+  x = cx_layer<16, true>(x);
+  x = cx_layer<4, false>(x);
+  x = cx_layer<2, false>(x);
+  x = cx_layer<1, false>(x);
+  x = cx_layer<32, true>(x);
+  x = cx_layer<8, false>(x);
+  x = cx_layer<4, false>(x);
+  x = cx_layer<2, false>(x);
+  x = cx_layer<1, false>(x);
+  x = cx_layer<64, true>(x);
+  x = cx_layer<16, false>(x);
+  x = cx_layer<8, false>(x);
+  x = cx_layer<4, false>(x);
+  x = cx_layer<2, false>(x);
+  x = cx_layer<1, false>(x);
+  return x;
+}
+
+// v_max3_f32 without the canonicalising moves the compiler adds around fmaxf
+// (operands here are never signalling NaNs that matter: NaN rows are detected
+// on the raw bits).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // ------------------------------------------------------------ block ops

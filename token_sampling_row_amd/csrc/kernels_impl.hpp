@@ -21,11 +21,14 @@ __device__ __forceinline__ Filters make_filters(const KParams& kp, float M) {
   return f;
 }
 
-// The row's full weight sum is needed by JOINT top-p (its mass reference) and
-// by the kept-mass diagnostic.
-__device__ __forceinline__ bool wants_z(const KParams& kp) {
+// JOINT top-p measures mass against the row's full weight sum.
+__device__ __forceinline__ bool joint_top_p(const KParams& kp) {
   const bool k_on = kp.flags & F_K, p_on = kp.flags & F_P, seq = kp.flags & F_SEQ;
-  return (kp.flags & F_Z) || (p_on && !(seq && k_on));
+  return p_on && !(seq && k_on);
+}
+// The streaming path also forms the full sum for the kept-mass diagnostic.
+__device__ __forceinline__ bool wants_z(const KParams& kp) {
+  return (kp.flags & F_Z) || joint_top_p(kp);
 }
 
 __device__ __forceinline__ double draw_uniform(const KParams& kp, uint32_t row, uint32_t pos,
@@ -64,8 +67,23 @@ __device__ __noinline__ void stream_finish(const StreamRow<DT> s, int row, float
   int kept = cut.kept;
   float tmin = cut.tau;
   if (dg.kept_count || dg.threshold) stream_kept_stats(s, cut.tau, &kept, &tmin);
+  if (dg.kept_mass && !(Z > 0.0)) Z = stream_weight_sum(s, -kFltMax, M, kp.c);
   write_row(row, tok, 0, kept, tmin, Z > 0.0 ? zs / Z : 0.0, out, dg);
   if (dg.probs) stream_probs(s, cut.tau, M, kp.c, zs, dg.probs + (long long)row * s.V);
+}
+
+// Diagnostics of a row whose token the register path drew: they re-read the
+// row (validation outputs, off the timed path). Not inlined, and nothing is
+// live in the caller after it, so the hot path keeps no values for it.
+template <int DT>
+__device__ __noinline__ void diag_finish(const StreamRow<DT> s, int row, int tok, int kept,
+                                         float tau, float M, float c, double zs, int32_t* out,
+                                         const DiagPtrs dg) {
+  float tmin = tau;
+  if (dg.kept_count || dg.threshold) stream_kept_stats(s, tau, &kept, &tmin);
+  const double Z = dg.kept_mass ? stream_weight_sum(s, -kFltMax, M, c) : 0.0;
+  write_row(row, tok, 0, kept, tmin, Z > 0.0 ? zs / Z : 0.0, out, dg);
+  if (dg.probs) stream_probs(s, tau, M, c, zs, dg.probs + (long long)row * s.V);
 }
 
 // ---------------------------------------------------------------- greedy
@@ -118,7 +136,7 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   RegRow<DT, NC> r;
   r.load(p, V, ragged != 0);
   const bool greedy = (kp.flags & F_GREEDY) != 0;
-  const RowStats st = reg_stats(r, !greedy && wants_z(kp), kp.c, L);
+  const RowStats st = reg_stats(r, !greedy && joint_top_p(kp), kp.c, L);
   if (st.status != 0) {
     write_row(row, -1, st.status, 0, kNegInf, 0.0, out, dg);
     zero_probs(dg, row, V);
@@ -133,30 +151,28 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   const Filters f = make_filters(kp, M);
   const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);
   float tau = -kFltMax;     // no filter: every finite logit
-  int kept = -1, tok = -1;
-  double zs = 0.0;
-  bool drawn = false;
+  int kept = -1, tok;
+  double zs;
   if (f.k_on || f.p_on || f.m_on) {
-    const FastOut fo = fast_cut(r, V, M, st.smin, st.z, c, f, u, L);
+    // the cut and the draw; the registers are dead afterwards
+    const FastOut fo = fast_cut(r, V, M, st.tmin, st.zlo, c, f, u, L);
     if (!fo.ok) {
-      // the candidates did not fit: the streaming path finishes this row (the
-      // registers are dead from here on, so the calls save nothing)
-      stream_finish(StreamRow<DT>(p, V, true), row, M, st.z, kp, f, u, out, dg);
+      // the candidates did not fit: the streaming path finishes this row
+      stream_finish(StreamRow<DT>(p, V, true), row, M, -1.0, kp, f, u, out, dg);
       return;
     }
     tau = fo.tau;
     kept = fo.kept;
     zs = fo.zs;
-    drawn = fo.drawn != 0;
     tok = fo.token;
+  } else {
+    tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs);
   }
-  if (!drawn) tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs);
-  // diagnostics re-read the row (validation outputs, off the timed path)
-  float tmin = tau;
-  const StreamRow<DT> s(p, V, true);
-  if (dg.kept_count || dg.threshold) stream_kept_stats(s, tau, &kept, &tmin);
-  write_row(row, tok, 0, kept, tmin, st.z > 0.0 ? zs / st.z : 0.0, out, dg);
-  if (dg.probs) stream_probs(s, tau, M, c, zs, dg.probs + (long long)row * V);
+  if (dg.kept_count || dg.threshold || dg.kept_mass || dg.probs) {
+    diag_finish(StreamRow<DT>(p, V, true), row, tok, kept, tau, M, c, zs, out, dg);
+    return;
+  }
+  write_row(row, tok, 0, kept, tau, 0.0, out, dg);
 }
 
 // Rows wider than the register file: every pass streams the row.
@@ -226,7 +242,7 @@ template <int DT, int NC>
 __device__ __forceinline__ RowCut verify_row_cut(RegRow<DT, NC>& r, const unsigned char* p,
                                                  int V, bool aligned, const KParams& kp,
                                                  Lds& L) {
-  const RowStats st = reg_stats(r, wants_z(kp), kp.c, L);
+  const RowStats st = reg_stats(r, joint_top_p(kp), kp.c, L);
   RowCut rc{st.status, st.M, kPosInf, 0.0};
   if (st.status != 0) return rc;
   const Filters f = make_filters(kp, st.M);
@@ -235,13 +251,13 @@ __device__ __forceinline__ RowCut verify_row_cut(RegRow<DT, NC>& r, const unsign
     rc.zs = reg_kept_mass(r, rc.tau, st.M, kp.c, L);
     return rc;
   }
-  const FastOut fo = fast_cut(r, V, st.M, st.smin, st.z, kp.c, f, 0.0, L);
+  const FastOut fo = fast_cut(r, V, st.M, st.tmin, st.zlo, kp.c, f, 0.0, L);
   if (fo.ok) {
     rc.tau = fo.tau;
     rc.zs = fo.zs;
     return rc;
   }
-  const Cut cut = general_stream(StreamRow<DT>(p, V, aligned), st.M, st.z, kp.c, kp.cR, f);
+  const Cut cut = general_stream(StreamRow<DT>(p, V, aligned), st.M, -1.0, kp.c, kp.cR, f);
   rc.tau = cut.tau;
   rc.zs = reg_kept_mass(r, rc.tau, st.M, kp.c, L);
   return rc;

@@ -32,6 +32,8 @@ struct Lds {
   uint32_t hcnt[kBins];             // histogram counts
   unsigned long long hmass[kBins];  // histogram masses, fixed point 2^-40
   double jsum[kWaves * kWalkBatch]; // walk: per (wave, chunk row) sums
+  unsigned long long wkey[kWaves][kWaveCap];  // candidates, one region per wavefront
+  int wcnt[kWaves];                 // candidates found by each wavefront
   WaveStats ws[kWaves];
   BlockScratch bs;
   int si[8];
@@ -82,16 +84,6 @@ struct Cut {
   int kept;       // |S|, or -1 when not counted
   double zs;      // sum over S of weights, or -1 when not summed
 };
-
-// Combine two (max, weight sum relative to that max) pairs.
-__device__ __forceinline__ void mz_combine(float& m, double& z, float m2, double z2, float c) {
-  const float mx = fmaxf(m, m2);
-  double r = 0.0;
-  if (m > kNegInf) r += z * (double)weight(m, mx, c);
-  if (m2 > kNegInf) r += z2 * (double)weight(m2, mx, c);
-  m = mx;
-  z = r;
-}
 
 // ---------------------------------------------------------------- LDS sort
 // Bitonic sort of key[0, n) into descending order (n <= kCap).
@@ -197,6 +189,46 @@ __device__ __forceinline__ Resolved resolve_sorted(Lds& L, int n, int cnt_above,
   return res;
 }
 
+// Inverse-CDF draw over the kept candidates key[0, n) (the first n_in of the
+// value-sorted candidates): re-keyed by token id, sorted ascending by id, an
+// exclusive scan of their weights, and the first id whose running total
+// exceeds u * Z_S (else the last id with weight). Every thread calls.
+__device__ __forceinline__ int draw_sorted(Lds& L, int n, float M, float c, double u) {
+  constexpr int P = kCap / kBlock;
+  for (int i = threadIdx.x; i < n; i += kBlock) {
+    const unsigned long long k = L.key[i];
+    L.key[i] = ((unsigned long long)(uint32_t)k << 32) | (k >> 32);
+  }
+  __syncthreads();
+  sort_keys_desc(L, n);
+  const int m0 = (int)threadIdx.x * P;
+  float w[P];
+  double local = 0.0;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    w[i] = m0 + i < n ? weight(key2f((uint32_t)L.key[m0 + i]), M, c) : 0.0f;
+    local += (double)w[i];
+  }
+  double tot;
+  const double ex = block_excl_scan<kBlock>(local, &tot, L.bs);
+  const double target = u * tot;
+  int hit = 0x7FFFFFFF, lastw = -1;
+  double run = ex;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    run += (double)w[i];
+    if (w[i] > 0.0f) {
+      lastw = m0 + i;
+      if (hit == 0x7FFFFFFF && target < run) hit = m0 + i;
+    }
+  }
+  int pos = block_min<kBlock>(hit, L.bs);
+  if (pos == 0x7FFFFFFF) pos = block_max<kBlock>(lastw, L.bs);
+  const int token = (int)~key_hi(L.key[pos]);
+  __syncthreads();
+  return token;
+}
+
 // Boundary search over one histogram level (every thread calls; wave 0 does
 // the work). Bins are in descending value order. Returns the boundary bin
 // d* = min(top-k bin, top-p bin), or kBins if no filter cuts inside the
@@ -262,61 +294,96 @@ __device__ __forceinline__ int find_boundary(Lds& L, int cnt_above, double mass_
   return d;
 }
 
-// Wave 0 resolves up to kWaveCap unsorted candidates key[0, n) (every logit
-// >= the candidate bound, which is <= tau) and draws from S in token-id order.
-// Each lane holds one candidate and learns, by reading every other lane
-// (v_readlane, no LDS), how many candidates are strictly larger and their
-// mass; the draw sums, per kept lane, the kept mass at or below its id.
-// Results: L.si[0] token, L.si[1] |S|, L.sf[0] tau, L.sd[1] sum of weights
-// over S. Called by wave 0 only; no barriers inside.
-__device__ __forceinline__ void wave_resolve_draw(Lds& L, int n, float M, float c,
-                                                  const Filters& f, double thr_joint,
-                                                  double u) {
+// Wave 0 resolves the candidates of the per-wavefront regions (at most
+// kWaveCap in all; every logit >= the candidate bound, which is <= tau) and
+// draws from S in token-id order.
+//  - Value order (when top-k can cut or top-p is on): the candidates are
+//    sorted by (value, lowest id first); the first position of a lane's tie
+//    group is the number of logits strictly above it, and an exclusive scan
+//    of the weights at that position is their mass. Every filter keeps a
+//    prefix of this order.
+//  - JOINT top-p compares against top_p * Z. With only a lower bound of Z
+//    (z_exact false) a group that the bound would drop might be kept by the
+//    exact Z: then nothing is decided, L.si[7] is set and the caller calls
+//    again with the exact Z.
+//  - The draw: the kept candidates sorted by token id, an inclusive scan of
+//    their weights C, and the first id with u * Z_S < C.
+// Results: L.si[0] token, L.si[1] |S|, L.sf[0] tau, L.sd[1] Z_S (sum of
+// weights over S), L.si[7] 0 or 1 (see above). Wave 0 only, all lanes active.
+__device__ __forceinline__ void wave_resolve_draw(Lds& L, float M, float c, const Filters& f,
+                                                  double zref, bool z_exact, double u) {
   const int lane = __lane_id();
-  const bool valid = lane < n;
-  const unsigned long long key = valid ? L.key[lane] : 0ull;
-  const uint32_t kh = key_hi(key);
-  const float v = key2f(kh);
-  const uint32_t idx = ~(uint32_t)key;
-  const double w = valid ? (double)weight(v, M, c) : 0.0;
-  int cnt_gt = 0;
-  double mass_gt = 0.0;
-  for (int j = 0; j < n; ++j) {
-    const uint32_t kj = readlane_u32(kh, j);
-    const double wj = readlane_t(w, j);
-    if (kj > kh) {
-      ++cnt_gt;
-      mass_gt += wj;
-    }
+  unsigned long long key = 0ull;
+  int n = 0;
+#pragma unroll
+  for (int q = 0; q < kWaves; ++q) {
+    const int cq = L.wcnt[q];
+    if (lane >= n && lane < n + cq) key = L.wkey[q][lane - n];
+    n += cq;
   }
-  const bool keep_k = !f.k_on || cnt_gt < f.k;
-  double thr = thr_joint;
-  if (f.seq && f.k_on && f.p_on) thr = f.top_p * wave_sum(valid && keep_k ? w : 0.0);
-  const bool keep = valid && v >= f.tau_m && keep_k &&
-                    (!f.p_on || mass_gt < thr || kh == fkey(M));
-  const unsigned long long km = __ballot(keep);
-  const int n_in = __popcll(km);
-  const float tau = key2f(wave_min_u32(keep ? kh : 0xFFFFFFFFu));
-  // draw: running kept mass in ascending token id
-  double C = 0.0;
-  for (int j = 0; j < n; ++j) {
-    if ((km >> j) & 1ull) {
-      const uint32_t ij = readlane_u32(idx, j);
-      const double wj = readlane_t(w, j);
-      if (ij <= idx) C += wj;
+  const uint32_t kM = fkey(M);
+  const bool seq_kp = f.seq && f.k_on && f.p_on;
+  bool keep;
+  int n_in;
+  float tau;
+  if ((f.k_on && n > f.k) || f.p_on) {
+    key = wave_sort_desc(key);
+    const bool valid = lane < n;
+    const uint32_t kh = key_hi(key);
+    const float v = key2f(kh);
+    const double w = valid ? (double)weight(v, M, c) : 0.0;
+    const uint32_t prev = dpp_u32<kDppWaveShr1>(kh);
+    const bool start = valid && (lane == 0 || prev != kh);
+    const int cnt_gt = wave_incl_max_scan(start ? lane : 0);
+    const double incl = wave_incl_scan(w);
+    const double mass_gt = wave_incl_max_scan(start ? incl - w : 0.0);
+    const bool keep_k = !f.k_on || cnt_gt < f.k;
+    const bool keep_m = v >= f.tau_m;
+    bool keep_p = true;
+    if (f.p_on) {
+      double thr;
+      if (seq_kp)
+        thr = f.top_p * wave_sum(valid && keep_k ? w : 0.0);
+      else
+        thr = f.top_p * (z_exact ? zref : zref * (1.0 - 1e-4));
+      keep_p = mass_gt < thr || kh == kM;
+      if (!seq_kp && !z_exact && __any(valid && keep_k && keep_m && !keep_p)) {
+        if (lane == 0) L.si[7] = 1;
+        return;
+      }
     }
+    keep = valid && keep_k && keep_m && keep_p;
+    n_in = __popcll(__ballot(keep));
+    tau = key2f(readlane_u32(kh, n_in - 1));
+  } else {
+    const uint32_t kh = key_hi(key);
+    keep = lane < n && key2f(kh) >= f.tau_m;
+    n_in = __popcll(__ballot(keep));
+    tau = key2f(wave_min_u32(keep ? kh : 0xFFFFFFFFu));
   }
-  const double total =
-      wave_reduce(keep ? C : 0.0, [](double a, double b) { return a > b ? a : b; });
+  // token-id order: (~id) << 32 | value key, descending
+  key = keep ? (((unsigned long long)(uint32_t)key << 32) | key_hi(key)) : 0ull;
+  key = wave_sort_desc(key);
+  const bool in = lane < n_in;
+  const uint32_t idx = ~key_hi(key);
+  const double w = in ? (double)weight(key2f((uint32_t)key), M, c) : 0.0;
+  const double C = wave_incl_scan(w);
+  const double total = readlane_t(C, n_in - 1);
   const double target = u * total;
-  const bool hit = keep && C > target;
-  const int token = __ballot(hit) ? (int)wave_min_u32(hit ? idx : 0xFFFFFFFFu)
-                                  : (int)wave_max_u32(keep ? idx : 0u);
+  const unsigned long long hit = __ballot(in && C > target);
+  int pos;
+  if (hit) {
+    pos = __ffsll((long long)hit) - 1;
+  } else {  // rounding put the target past the end: the last kept id with weight
+    const unsigned long long pw = __ballot(in && w > 0.0);
+    pos = 63 - __clzll((long long)pw);
+  }
+  const int token = (int)readlane_u32(idx, pos);
   if (lane == 0) {
     L.si[0] = token;
     L.si[1] = n_in;
+    L.si[7] = 0;
     L.sf[0] = tau;
-    L.sd[0] = total;
     L.sd[1] = total;
   }
 }

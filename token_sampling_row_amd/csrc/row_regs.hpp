@@ -21,6 +21,7 @@ struct RegRow {
   float tmax;     // this thread's maximum
 
   int nwhole;     // whole 16-byte chunks in the row (chunk ids at or past it are not)
+  int jfull;      // chunk rows j < jfull are whole for every thread
   uint4 tail;     // the partial chunk, read element-wise, when the row is ragged
 
   // Whole chunks of a 16-byte aligned row are 128-bit buffer loads off one
@@ -33,28 +34,40 @@ struct RegRow {
   __device__ __forceinline__ void load(const unsigned char* p, int V, bool ragged) {
     if constexpr (UNALIGNED) {
       nwhole = 0x7FFFFFFF;
+      jfull = NC;
       tail = neg_inf_chunk<DT>();
 #pragma unroll
       for (int j = 0; j < NC; ++j)
         raw[j] = load_chunk_slow<DT>(p, (long long)j * kBlock + threadIdx.x, V);
     } else {
       nwhole = V / EPC;
+      jfull = nwhole / kBlock;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<unsigned char*>(p), (short)0, nwhole * 16, 0x00020000);
       const int voff = (int)threadIdx.x * 16;
 #pragma unroll
-      for (int j = 0; j < NC; ++j)
+      for (int j = 0; j < NC; ++j) {
         raw[j] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, j * kBlock * 16, 0));
+        sched_fence();   // issue in chunk order: pass A waits for them in that order
+      }
       tail = neg_inf_chunk<DT>();
       if (ragged && nwhole * EPC < V && (nwhole % kBlock) == (int)threadIdx.x)
         tail = load_chunk_slow<DT>(p, nwhole, V);
     }
   }
-  // Pass-A fix-up of chunk j (see load).
+  // Pass-A fix-up of chunk j (see load): only chunk rows at or past jfull
+  // (a uniform test) can hold chunks past the end; the fix is branch-free.
   __device__ __forceinline__ uint4 settle(int j, uint4 t) const {
-    const int cid = j * kBlock + (int)threadIdx.x;
-    if (cid >= nwhole) t = cid == nwhole ? tail : neg_inf_chunk<DT>();
+    if (j >= jfull) {
+      const int cid = j * kBlock + (int)threadIdx.x;
+      const uint4 ni = neg_inf_chunk<DT>();
+      const bool past = cid >= nwhole, at = cid == nwhole;
+      t.x = past ? (at ? tail.x : ni.x) : t.x;
+      t.y = past ? (at ? tail.y : ni.y) : t.y;
+      t.z = past ? (at ? tail.z : ni.z) : t.z;
+      t.w = past ? (at ? tail.w : ni.w) : t.w;
+    }
     return t;
   }
   __device__ __forceinline__ int base(int j) const {
@@ -70,115 +83,148 @@ struct RegRow {
   __device__ __forceinline__ void elems(int j, float* v) const { unpack<DT>(packed(j), v); }
 };
 
-// NaN detector on packed data: the running maximum of the magnitude bits of
-// every element. A NaN has magnitude bits above those of infinity.
-template <int DT> struct NanAcc;
-template <> struct NanAcc<0> {
-  uint32_t a = 0u;
+// NaN / +inf detector on the raw bits (-inf is a valid logit: a masked
+// token). f32: a signed maximum reaches 0x7F800000 only for +inf or a
+// positive NaN, an unsigned maximum passes 0xFF800000 only for a negative
+// NaN. bf16: the same two tests on each 16-bit half with packed maxima.
+template <int DT> struct BadAcc;
+template <> struct BadAcc<0> {
+  int32_t smax = (int32_t)0x80000000;
+  uint32_t umax = 0u;
   __device__ __forceinline__ void add(uint4 t) {
-    a = max(a, max(max(t.x & 0x7FFFFFFFu, t.y & 0x7FFFFFFFu),
-                   max(t.z & 0x7FFFFFFFu, t.w & 0x7FFFFFFFu)));
+    smax = max(max(smax, max((int32_t)t.x, (int32_t)t.y)), max((int32_t)t.z, (int32_t)t.w));
+    umax = max(max(umax, max(t.x, t.y)), max(t.z, t.w));
   }
-  __device__ __forceinline__ bool nan() const { return a > 0x7F800000u; }
+  __device__ __forceinline__ bool bad() const { return smax >= 0x7F800000 || umax > 0xFF800000u; }
 };
-template <> struct NanAcc<1> {
+template <> struct BadAcc<1> {
+  typedef short s2 __attribute__((ext_vector_type(2)));
   typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-  us2 a = {0, 0};
-  __device__ __forceinline__ static us2 mag(uint32_t w) {
-    return __builtin_bit_cast(us2, w & 0x7FFF7FFFu);
-  }
+  s2 smax = {(short)0x8000, (short)0x8000};
+  us2 umax = {0, 0};
   __device__ __forceinline__ void add(uint4 t) {
-    a = __builtin_elementwise_max(
-        a, __builtin_elementwise_max(__builtin_elementwise_max(mag(t.x), mag(t.y)),
-                                     __builtin_elementwise_max(mag(t.z), mag(t.w))));
+    smax = __builtin_elementwise_max(
+        __builtin_elementwise_max(smax, __builtin_bit_cast(s2, t.x)),
+        __builtin_elementwise_max(__builtin_elementwise_max(__builtin_bit_cast(s2, t.y),
+                                                            __builtin_bit_cast(s2, t.z)),
+                                  __builtin_bit_cast(s2, t.w)));
+    umax = __builtin_elementwise_max(
+        __builtin_elementwise_max(umax, __builtin_bit_cast(us2, t.x)),
+        __builtin_elementwise_max(__builtin_elementwise_max(__builtin_bit_cast(us2, t.y),
+                                                            __builtin_bit_cast(us2, t.z)),
+                                  __builtin_bit_cast(us2, t.w)));
   }
-  __device__ __forceinline__ bool nan() const { return a.x > 0x7F80u || a.y > 0x7F80u; }
+  __device__ __forceinline__ bool bad() const {
+    return smax.x >= (short)0x7F80 || smax.y >= (short)0x7F80 ||
+           umax.x > (unsigned short)0xFF80 || umax.y > (unsigned short)0xFF80;
+  }
 };
+
+// Largest element of a chunk, with v_max3 (both halves of a bf16 word widened
+// exactly). A NaN element may make the result NaN; such rows are flagged by
+// BadAcc and never reach the chunk tests.
+template <int DT>
+__device__ __forceinline__ float chunk_max(uint4 t) {
+  if constexpr (DT == 0) {
+    const float m = max3f(__uint_as_float(t.x), __uint_as_float(t.y), __uint_as_float(t.z));
+    return max3f(m, __uint_as_float(t.w), __uint_as_float(t.w));
+  } else {
+    float v[8];
+    unpack<1>(t, v);
+    float m = max3f(v[0], v[1], v[2]);
+    m = max3f(m, v[3], v[4]);
+    m = max3f(m, v[5], v[6]);
+    return max3f(m, v[7], v[7]);
+  }
+}
 
 struct RowStats {
   int status;     // TSR_ROW_*
   float M;        // row max
-  float smin;     // smallest finite chunk maximum
-  double z;       // sum of weights over the row (when asked for)
+  float tmin;     // smallest finite per-thread maximum
+  double zlo;     // a lower bound of the row's weight sum (when asked for)
 };
 
-// Row statistics in two passes over the registers. Pass A runs as the loads
-// land: NaN/+inf detection, chunk maxima, thread max. Pass B (only when the
-// weight sum is wanted) sums 2^((v - m_t) c) against the thread's own max m_t:
-// no running rescale, so every chunk is independent work. One barrier round
-// combines the waves.
+// Row statistics in one pass over the registers as the loads land: NaN/+inf
+// detection, chunk maxima, thread max. The empty asm at the end of each chunk
+// pins the running maximum in program order, so chunk j is reduced as soon as
+// its load has arrived instead of after the whole row.
+// need_zlo: also sum, per thread, the weights of its chunk maxima (one
+// exponential per chunk). That is a lower bound of the row's weight sum Z,
+// enough to settle JOINT top-p whenever the nucleus is not close to the cut.
 template <int DT, int NC>
-__device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_z, float c, Lds& L) {
-  constexpr int EPC = Fmt<DT>::EPC;
-  float tmax = kNegInf, smin = kPosInf;
-  NanAcc<DT> nan;
+__device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, float c, Lds& L) {
+  float tmax = kNegInf;
+  BadAcc<DT> bad;
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     const uint4 t = r.settle(j, r.packed(j));
     r.raw[j] = t;
-    nan.add(t);
-    float v[EPC];
-    unpack<DT>(t, v);
-    float m = fmaxf(v[0], v[1]);
-#pragma unroll
-    for (int e = 2; e < EPC; ++e) m = fmaxf(m, v[e]);
+    bad.add(t);
+    const float m = chunk_max<DT>(t);
     r.cm[j] = m;
-    tmax = fmaxf(tmax, m);
-    smin = m > kNegInf ? fminf(smin, m) : smin;
-    sched_fence();
+    tmax = max3f(tmax, m, m);
+    asm volatile("" : "+v"(tmax));
   }
   r.tmax = tmax;
   double zt = 0.0;
-  if (need_z && tmax > kNegInf && tmax < kPosInf) {
-    double acc[2] = {0.0, 0.0};
+  if (need_zlo && tmax > kNegInf && tmax < kPosInf) {
+    float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      float v[EPC];
-      r.elems(j, v);
-      float s[EPC / 2];
-#pragma unroll
-      for (int e = 0; e < EPC / 2; ++e)
-        s[e] = weight(v[2 * e], tmax, c) + weight(v[2 * e + 1], tmax, c);
-      float t = s[0];
-#pragma unroll
-      for (int e = 1; e < EPC / 2; ++e) t += s[e];
-      acc[j & 1] += (double)t;
-      sched_fence();
-    }
-    zt = acc[0] + acc[1];
+    for (int j = 0; j < NC; ++j) s += weight(r.cm[j], tmax, c);
+    zt = (double)s;
   }
   // wave level
   const float wm = wave_max(tmax);
-  const float ws = wave_min(smin);
-  const int wb = __any(nan.nan()) ? 1 : 0;
+  const float wt = wave_min(tmax > kNegInf ? tmax : kPosInf);
+  const int wb = __any(bad.bad()) ? 1 : 0;
   double wz = 0.0;
-  if (need_z)   // relative to the wave max
+  if (need_zlo)   // relative to the wave max
     wz = wave_sum(tmax > kNegInf && tmax < kPosInf ? zt * (double)weight(tmax, wm, c) : 0.0);
   const int wid = threadIdx.x / kWave;
   __syncthreads();
-  if (__lane_id() == 0) L.ws[wid] = WaveStats{wm, ws, wz, wb};
+  if (__lane_id() == 0) L.ws[wid] = WaveStats{wm, wt, wz, wb};
   __syncthreads();
   RowStats st;
-  float M = kNegInf, sm = kPosInf;
-  int bad = 0;
+  float M = kNegInf, tmin = kPosInf;
+  int anybad = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     M = fmaxf(M, L.ws[w].m);
-    sm = fminf(sm, L.ws[w].smin);
-    bad |= L.ws[w].bad;
+    tmin = fminf(tmin, L.ws[w].smin);
+    anybad |= L.ws[w].bad;
   }
-  double Z = -1.0;
-  if (need_z) {
-    Z = 0.0;
+  double Z = 0.0;
+  if (need_zlo) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
-      if (L.ws[w].m > kNegInf && M > kNegInf) Z += L.ws[w].z * (double)weight(L.ws[w].m, M, c);
+      if (L.ws[w].m > kNegInf && M > kNegInf && M < kPosInf)
+        Z += L.ws[w].z * (double)weight(L.ws[w].m, M, c);
   }
   st.M = M;
-  st.smin = sm;
-  st.z = Z;
-  st.status = (bad || M == kPosInf) ? 1 : (M > kNegInf ? 0 : 2);
+  st.tmin = tmin;
+  st.zlo = Z;
+  st.status = (anybad || M == kPosInf) ? 1 : (M > kNegInf ? 0 : 2);
   return st;
+}
+
+// The row's weight sum Z = sum of 2^((v - M) c) over every element.
+template <int DT, int NC>
+__device__ __forceinline__ double reg_weight_sum(const RegRow<DT, NC>& r, float M, float c,
+                                                 Lds& L) {
+  constexpr int EPC = Fmt<DT>::EPC;
+  double acc[2] = {0.0, 0.0};
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    float v[EPC];
+    r.elems(j, v);
+    float t = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) t += weight(v[e], M, c);
+    acc[j & 1] += (double)t;
+    sched_fence();
+  }
+  return block_sum<kBlock>(acc[0] + acc[1], L.bs);
 }
 
 // Lowest index among the maximal logits.
@@ -357,11 +403,115 @@ struct FastOut {
   double zs;      // sum of weights over S
 };
 
-// Candidate bound, candidate compaction and exact resolution (see the file
-// comment). Z is the row's weight sum (needed for JOINT top-p), u the uniform.
+// Single-pass compaction of the logits >= Lb into the wavefront's own LDS
+// region, in ballot order. Chunks no lane of the wavefront can contribute to
+// are skipped on their maxima; a wavefront stops once it has more than
+// kWaveCap (then the caller takes another route).
 template <int DT, int NC>
-__device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, float M, float smin,
-                                            double Z, float c, const Filters& f, double u,
+__device__ __forceinline__ void wave_compact(const RegRow<DT, NC>& r, float Lb, Lds& L) {
+  constexpr int EPC = Fmt<DT>::EPC;
+  const int wid = threadIdx.x / kWave;
+  int base = 0;
+  if (__any(r.tmax >= Lb)) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      if (base <= kWaveCap && __any(r.cm[j] >= Lb)) {
+        float v[EPC];
+        r.elems(j, v);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          const bool hit = v[e] >= Lb;
+          const unsigned long long b = __ballot(hit);
+          const int slot = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                      (uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+          if (hit && slot < kWaveCap) L.wkey[wid][slot] = cand_key(v[e], r.base(j) + e);
+          base += __popcll(b);
+        }
+      }
+    }
+  }
+  if (__lane_id() == 0) L.wcnt[wid] = base;
+}
+
+// Candidates the per-wavefront regions hold in all (after a barrier).
+__device__ __forceinline__ int wave_regions_total(const Lds& L) {
+  int t = 0;
+#pragma unroll
+  for (int q = 0; q < kWaves; ++q) t += L.wcnt[q];
+  return t;
+}
+
+// Top-k candidate bound: the k-th largest of the per-thread maxima (k <=
+// kBlock/4) or of the chunk maxima, which is at most the k-th largest logit.
+// Found on a linear histogram of [lo, M] and the smallest value in the bin
+// that reaches k. Returns -inf when fewer than k values are >= lo.
+template <int DT, int NC>
+__device__ __forceinline__ float topk_sketch(const RegRow<DT, NC>& r, float M, float lo,
+                                             int k, Lds& L) {
+  const int tid = threadIdx.x;
+  const bool by_thread = k <= kBlock / 4;
+  const float span = M - lo;
+  const float scale = (span > 0.0f && span <= kFltMax) ? fminf((float)kBins / span, 1e30f) : 0.0f;
+  auto sbin = [&](float x) -> int {
+    const float t = (M - x) * scale;
+    return t < (float)(kBins - 1) ? (int)t : kBins - 1;
+  };
+  for (int i = tid; i < kBins; i += kBlock) L.hcnt[i] = 0u;
+  if (tid == 0) {
+    L.si[6] = kBins;
+    L.su[0] = 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  if (by_thread) {
+    if (r.tmax >= lo) atomicAdd(&L.hcnt[sbin(r.tmax)], 1u);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+      if (r.cm[j] >= lo) atomicAdd(&L.hcnt[sbin(r.cm[j])], 1u);
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    constexpr int PER = kBins / kWave;
+    int lc = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) lc += (int)L.hcnt[tid * PER + i];
+    const int ic = wave_incl_scan(lc);
+    int run = ic - lc;
+    int found = kBins;
+    if (run < k && ic >= k) {
+      for (int i = 0; i < PER; ++i) {
+        run += (int)L.hcnt[tid * PER + i];
+        if (run >= k) {
+          found = tid * PER + i;
+          break;
+        }
+      }
+    }
+    found = wave_min(found);
+    if (tid == 0) L.si[6] = found;
+  }
+  __syncthreads();
+  const int bk = L.si[6];
+  if (bk < kBins) {
+    if (by_thread) {
+      if (r.tmax >= lo && sbin(r.tmax) == bk) atomicMin(&L.su[0], fkey(r.tmax));
+    } else {
+#pragma unroll
+      for (int j = 0; j < NC; ++j)
+        if (r.cm[j] >= lo && sbin(r.cm[j]) == bk) atomicMin(&L.su[0], fkey(r.cm[j]));
+    }
+  }
+  __syncthreads();
+  const uint32_t kb = L.su[0];
+  return (bk < kBins && kb != 0xFFFFFFFFu) ? key2f(kb) : kNegInf;
+}
+
+// Candidate bound, compaction and exact resolution (see the file comment).
+// zlo is a lower bound of the row's weight sum (JOINT top-p); the exact sum is
+// formed here only when the bound cannot settle the cut. u is the uniform.
+template <int DT, int NC>
+__device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, float M, float tmin,
+                                            double zlo, float c, const Filters& f, double u,
                                             Lds& L) {
   constexpr int EPC = Fmt<DT>::EPC;
   const int tid = threadIdx.x;
@@ -369,76 +519,47 @@ __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, floa
   // In SEQUENTIAL mode top-p measures against the whole top-k set, so min-p
   // may not narrow the candidates there.
   const bool seq_kp = f.seq && f.k_on && f.p_on;
+  const bool joint_p = f.p_on && !seq_kp;
   float Lb = seq_kp ? kNegInf : f.tau_m;
-  if (V <= kCap) {
-    Lb = fmaxf(Lb, -kFltMax);           // the whole (finite) row fits
-  } else if (f.k_on) {
-    const float lo = fmaxf(Lb, smin);
-    // sketch values: per-thread maxima when k is small, else chunk maxima
-    const bool by_thread = f.k <= kBlock / 4;
-    int ns = 0;
-    if (by_thread) {
-      ns = r.tmax >= lo ? 1 : 0;
-    } else {
-#pragma unroll
-      for (int j = 0; j < NC; ++j) ns += (r.cm[j] >= lo) ? 1 : 0;
-    }
-    ns = block_sum<kBlock>(ns, L.bs);
-    if (ns >= f.k) {
-      const float span = M - lo;
-      const float scale = (span > 0.0f && span <= kFltMax) ? fminf((float)kBins / span, 1e30f)
-                                                           : 0.0f;
-      auto sbin = [&](float x) -> int {
-        const float t = (M - x) * scale;
-        return t < (float)(kBins - 1) ? (int)t : kBins - 1;
-      };
-      for (int i = tid; i < kBins; i += kBlock) L.hcnt[i] = 0u;
-      if (tid == 0) {
-        L.si[6] = kBins - 1;
-        L.su[0] = 0xFFFFFFFFu;
-      }
+  if (V <= kWaveCap) Lb = -kFltMax;     // the whole (finite) row fits one wavefront
+  bool fits = false;
+  if (Lb > kNegInf) {
+    wave_compact(r, Lb, L);
+    __syncthreads();
+    fits = wave_regions_total(L) <= kWaveCap;
+  }
+  if (!fits && f.k_on && V > kWaveCap) {
+    __syncthreads();
+    const float kb = topk_sketch(r, M, fmaxf(Lb, tmin), f.k, L);
+    if (kb > Lb) {
+      Lb = kb;
+      wave_compact(r, Lb, L);
       __syncthreads();
-      if (by_thread) {
-        if (r.tmax >= lo) atomicAdd(&L.hcnt[sbin(r.tmax)], 1u);
-      } else {
-#pragma unroll
-        for (int j = 0; j < NC; ++j)
-          if (r.cm[j] >= lo) atomicAdd(&L.hcnt[sbin(r.cm[j])], 1u);
-      }
-      __syncthreads();
-      if (tid < kWave) {
-        constexpr int PER = kBins / kWave;
-        int lc = 0;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) lc += (int)L.hcnt[tid * PER + i];
-        const int ic = wave_incl_scan(lc);
-        int run = ic - lc;
-        int found = kBins;
-        if (run < f.k && ic >= f.k) {
-          for (int i = 0; i < PER; ++i) {
-            run += (int)L.hcnt[tid * PER + i];
-            if (run >= f.k) { found = tid * PER + i; break; }
-          }
-        }
-        found = wave_min(found);
-        if (tid == 0 && found < kBins) L.si[6] = found;
-      }
-      __syncthreads();
-      const int bk = L.si[6];
-      if (by_thread) {
-        if (r.tmax >= lo && sbin(r.tmax) == bk) atomicMin(&L.su[0], fkey(r.tmax));
-      } else {
-#pragma unroll
-        for (int j = 0; j < NC; ++j)
-          if (r.cm[j] >= lo && sbin(r.cm[j]) == bk) atomicMin(&L.su[0], fkey(r.cm[j]));
-      }
-      __syncthreads();
-      const uint32_t kb = L.su[0];
-      if (kb != 0xFFFFFFFFu) Lb = fmaxf(Lb, key2f(kb));
+      fits = wave_regions_total(L) <= kWaveCap;
     }
   }
   if (!(Lb > kNegInf)) return out;
-  // count and compact the candidates (logits >= Lb) into LDS
+  out.ok = 1;
+  if (fits) {
+    double zref = zlo;
+    bool zx = !joint_p;
+#pragma nounroll
+    for (;;) {
+      if (tid < kWave) wave_resolve_draw(L, M, c, f, zref, zx, u);
+      __syncthreads();
+      if (!L.si[7]) break;
+      zref = reg_weight_sum(r, M, c, L);
+      zx = true;
+    }
+    out.drawn = 1;
+    out.token = L.si[0];
+    out.kept = L.si[1];
+    out.tau = L.sf[0];
+    out.zs = L.sd[1];
+    __syncthreads();
+    return out;
+  }
+  // more than one wavefront's worth: count, compact in thread order, sort
   int cnt = 0;
   if (r.tmax >= Lb) {
 #pragma unroll
@@ -452,7 +573,10 @@ __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, floa
   }
   int total;
   int off = block_excl_scan<kBlock>(cnt, &total, L.bs);
-  if (total > kCap) return out;
+  if (total > kCap) {
+    out.ok = 0;
+    return out;
+  }
   if (cnt) {
 #pragma unroll
     for (int j = 0; j < NC; ++j)
@@ -464,25 +588,16 @@ __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, floa
           if (v[e] >= Lb && off < kCap) L.key[off++] = cand_key(v[e], r.base(j) + e);
       }
   }
+  const double Z = joint_p ? reg_weight_sum(r, M, c, L) : 0.0;
   __syncthreads();
-  const double thr = f.p_on ? f.top_p * Z : 0.0;
-  out.ok = 1;
-  if (total <= kWaveCap) {
-    if (tid < kWave) wave_resolve_draw(L, total, M, c, f, thr, u);
-    __syncthreads();
-    out.drawn = 1;
-    out.token = L.si[0];
-    out.kept = L.si[1];
-    out.tau = L.sf[0];
-    out.zs = L.sd[1];
-    __syncthreads();
-    return out;
-  }
   sort_keys_desc(L, total);
-  const Resolved res = resolve_sorted(L, total, 0, 0.0, M, c, f, thr, f.seq);
+  const Resolved res = resolve_sorted(L, total, 0, 0.0, M, c, f, f.p_on ? f.top_p * Z : 0.0,
+                                      f.seq);
   out.tau = res.tau;
   out.kept = res.n_in;
   out.zs = res.zs;
+  out.token = draw_sorted(L, res.n_in, M, c, u);
+  out.drawn = 1;
   return out;
 }
 
