@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
 ROTATE = 8                     # distinct input buffers used in turn
+CALIB_BYTES = 1 << 28          # size of each --copy-calibration device copy
 
 
 def source_hash() -> str:
@@ -60,6 +61,41 @@ def row_kernel_label(dtype: str, vocab: int) -> str:
     need = -(-(-(-vocab // epc)) // 512)
     nc = next((n for n in (1, 2, 4, 8, 16, 24, 32, 38) if n >= need), None)
     return f"sample_kernel<{dtype}, {nc}>" if nc else "sample_kernel_stream"
+
+
+def write_traffic(fetch_csv: str, write_csv: str, workload: str, kernel_prefix: str) -> dict:
+    """HBM bytes per launch of the headline kernel from two rocprofv3 --pmc runs
+    of this script with --copy-calibration (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch). Each counter is scaled by what it reads for the calibration
+    copies (256 MiB device-to-device, the copy dispatches after the last
+    sampler dispatch) against their known size. Writes
+    profiles/traffic_<workload>.json tagged with the kernel-source hash."""
+    import csv
+
+    def scaled(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        kern = [i for i, r in enumerate(rows) if r["Kernel_Name"].removeprefix("void ").startswith(kernel_prefix)]
+        if not kern:
+            raise SystemExit(f"no {kernel_prefix} dispatch in {path}")
+        calib = [float(r["Counter_Value"]) for r in rows[kern[-1] + 1:] if "copyBuffer" in r["Kernel_Name"]]
+        if not calib:
+            raise SystemExit(f"no calibration copies after the sampler dispatches in {path}")
+        factor = (CALIB_BYTES / 1024.0) / (sum(calib) / len(calib))
+        vals = [float(rows[i]["Counter_Value"]) for i in kern]
+        kib = sum(vals) / len(vals)
+        return kib, factor, len(vals), len(calib)
+
+    fk, ff, nf, cf = scaled(fetch_csv, "FETCH_SIZE")
+    wk, wf, nw, cw = scaled(write_csv, "WRITE_SIZE")
+    out = {"workload": workload, "kernel": kernel_prefix, "source_hash": source_hash(),
+           "fetch_kib_per_dispatch": fk, "fetch_scale": ff, "write_kib_per_dispatch": wk,
+           "write_scale": wf, "dispatches": [nf, nw], "calibration_copies": [cf, cw],
+           "hbm_bytes_per_launch": (fk * ff + wk * wf) * 1024.0}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    return out
 
 
 def device_batch(torch, w, copies):
@@ -130,7 +166,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 256 MiB device copies (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter files into profiles/traffic_*.json")
     args = ap.parse_args()
+    if args.write_traffic:
+        from token_sampling_row_amd import workloads as wl
+        w3 = wl.config(3, rows=1)
+        print(json.dumps(write_traffic(*args.write_traffic, "batch256_128256_bf16",
+                                       f"tsr::{row_kernel_label(w3.dtype, w3.vocab).replace('bf16', '1').replace('f32', '0')}")))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the sampler shards by batch row with no exchange; see DESIGN.md)", file=sys.stderr)
@@ -163,7 +207,7 @@ def main():
         extra = run_extra(torch, tsr, wl, max(50, args.steps // 4), max(5, args.warmup // 4))
 
     if args.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.uint8, device="cuda:0")
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
         for _ in range(10):
             dst.copy_(src)
