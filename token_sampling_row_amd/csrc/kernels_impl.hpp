@@ -212,7 +212,7 @@ struct ResidualWeights {
   double inv_zp, inv_zq;
   __device__ __forceinline__ void operator()(int j, float* w) const {
     constexpr int EPC = Fmt<DT>::EPC;
-    if (rp.cm[j] >= tp) {
+    if (rp.cmax(j) >= tp) {
       float a[EPC], b[EPC];
       rp.elems(j, a);
       rq.elems(j, b);

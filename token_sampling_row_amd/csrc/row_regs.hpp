@@ -7,22 +7,71 @@
 // which can only be at or below the k-th largest logit. The logits >= Lb are
 // the candidates; at most kWaveCap of them are resolved and drawn by one
 // wavefront with no barriers, up to kCap by the whole workgroup.
+//
+// Code size matters as much as instruction count here: a launch runs each
+// phase once per workgroup, so code the instruction cache does not hold is
+// fetched from memory at every launch. Only the pass that reduces chunks as
+// their loads land is unrolled (its waits count loads); every later pass
+// loops over chunk rows, reading chunk j of the register-resident row with a
+// wavefront-uniform j (s_set_gpr_idx indexing of a register vector).
 #pragma once
 
 #include "row_common.hpp"
 
 namespace tsr {
 
+// Cache policy of the row loads: non-temporal, so the streamed logits are the
+// first lines the caches give up and the kernel's own code stays in L2 from
+// one launch to the next (each dispatch starts with a cold instruction cache).
+constexpr int kLoadNonTemporal = 2;
+
+template <int N> struct VecU { typedef uint32_t type __attribute__((ext_vector_type(N))); };
+template <int N> struct VecF { typedef float type __attribute__((ext_vector_type(N))); };
+
+// Register vectors hold at most 32 dwords: a row of NC chunk rows per thread
+// lives in a power-of-two bank A and, when NC is not a power of two, a bank B
+// with the rest.
+constexpr int bank_a(int nc) {
+  return nc >= 32 ? 32 : nc >= 16 ? 16 : nc >= 8 ? 8 : nc >= 4 ? 4 : nc >= 2 ? 2 : 1;
+}
+
 template <int DT, int NC>
 struct RegRow {
   static constexpr int EPC = Fmt<DT>::EPC;
-  uint4 raw[NC];
-  float cm[NC];   // chunk maxima; -inf past the end of the row
+  static constexpr int NA = bank_a(NC);
+  static constexpr int NB = NC - NA;
+  static constexpr int NBS = NB > 0 ? NB : 1;
+  static_assert(NB <= 32, "chunk rows per thread");
+  typename VecU<NA>::type ax, ay, az, aw;   // the chunks, one vector per dword
+  typename VecU<NBS>::type bx, by, bz, bw;
+  typename VecF<NA>::type ca;               // chunk maxima; -inf past the end of the row
+  typename VecF<NBS>::type cb;
   float tmax;     // this thread's maximum
 
   int nwhole;     // whole 16-byte chunks in the row (chunk ids at or past it are not)
   int jfull;      // chunk rows j < jfull are whole for every thread
   uint4 tail;     // the partial chunk, read element-wise, when the row is ragged
+
+  // Chunk row j: a compile-time j in unrolled code, else wavefront-uniform.
+  __device__ __forceinline__ uint4 get(int j) const {
+    if (NB == 0 || j < NA) return make_uint4(ax[j], ay[j], az[j], aw[j]);
+    const int i = j - NA;
+    return make_uint4(bx[i], by[i], bz[i], bw[i]);
+  }
+  __device__ __forceinline__ void put(int j, uint4 t) {
+    if (NB == 0 || j < NA) {
+      ax[j] = t.x; ay[j] = t.y; az[j] = t.z; aw[j] = t.w;
+    } else {
+      const int i = j - NA;
+      bx[i] = t.x; by[i] = t.y; bz[i] = t.z; bw[i] = t.w;
+    }
+  }
+  __device__ __forceinline__ float cmax(int j) const {
+    return (NB == 0 || j < NA) ? ca[j] : cb[j - NA];
+  }
+  __device__ __forceinline__ void put_cmax(int j, float m) {
+    if (NB == 0 || j < NA) ca[j] = m; else cb[j - NA] = m;
+  }
 
   // Whole chunks of a 16-byte aligned row are 128-bit buffer loads off one
   // resource, all issued back to back with no per-load address registers.
@@ -38,7 +87,7 @@ struct RegRow {
       tail = neg_inf_chunk<DT>();
 #pragma unroll
       for (int j = 0; j < NC; ++j)
-        raw[j] = load_chunk_slow<DT>(p, (long long)j * kBlock + threadIdx.x, V);
+        put(j, load_chunk_slow<DT>(p, (long long)j * kBlock + threadIdx.x, V));
     } else {
       nwhole = V / EPC;
       jfull = nwhole / kBlock;
@@ -47,8 +96,8 @@ struct RegRow {
       const int voff = (int)threadIdx.x * 16;
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
-        raw[j] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, j * kBlock * 16, 0));
+        put(j, __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, voff, j * kBlock * 16, kLoadNonTemporal)));
         sched_fence();   // issue in chunk order: pass A waits for them in that order
       }
       tail = neg_inf_chunk<DT>();
@@ -73,15 +122,24 @@ struct RegRow {
   __device__ __forceinline__ int base(int j) const {
     return (j * kBlock + (int)threadIdx.x) * EPC;
   }
-  // Packed chunk j. The empty asm makes each pass unpack afresh from the
-  // packed registers instead of keeping unpacked copies alive between passes.
-  __device__ __forceinline__ uint4 packed(int j) const {
-    uint4 t = raw[j];
-    asm volatile("" : "+v"(t.x), "+v"(t.y), "+v"(t.z), "+v"(t.w));
-    return t;
-  }
-  __device__ __forceinline__ void elems(int j, float* v) const { unpack<DT>(packed(j), v); }
+  __device__ __forceinline__ void elems(int j, float* v) const { unpack<DT>(get(j), v); }
 };
+
+// Bit j set iff pred(j) holds in some lane (pred is evaluated by every lane;
+// call with the whole wavefront active). Unrolled: NC compares and a few
+// scalar instructions.
+template <int NC, class Pred>
+__device__ __forceinline__ unsigned long long wave_chunk_mask(Pred pred) {
+  unsigned long long m = 0ull;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) m |= (__ballot(pred(j)) != 0ull) ? (1ull << j) : 0ull;
+  return m;
+}
+__device__ __forceinline__ int pop_low(unsigned long long& m) {
+  const int j = __builtin_amdgcn_readfirstlane(__builtin_ctzll(m));
+  m &= m - 1ull;
+  return j;
+}
 
 // NaN / +inf detector on the raw bits (-inf is a valid logit: a masked
 // token). f32: a signed maximum reaches 0x7F800000 only for +inf or a
@@ -158,11 +216,13 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
   BadAcc<DT> bad;
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
-    const uint4 t = r.settle(j, r.packed(j));
-    r.raw[j] = t;
+    uint4 t = r.get(j);
+    asm volatile("" : "+v"(t.x), "+v"(t.y), "+v"(t.z), "+v"(t.w));
+    t = r.settle(j, t);
+    r.put(j, t);
     bad.add(t);
     const float m = chunk_max<DT>(t);
-    r.cm[j] = m;
+    r.put_cmax(j, m);
     tmax = max3f(tmax, m, m);
     asm volatile("" : "+v"(tmax));
   }
@@ -171,7 +231,7 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
   if (need_zlo && tmax > kNegInf && tmax < kPosInf) {
     float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NC; ++j) s += weight(r.cm[j], tmax, c);
+    for (int j = 0; j < NC; ++j) s += weight(r.cmax(j), tmax, c);
     zt = (double)s;
   }
   // wave level
@@ -213,18 +273,17 @@ template <int DT, int NC>
 __device__ __forceinline__ double reg_weight_sum(const RegRow<DT, NC>& r, float M, float c,
                                                  Lds& L) {
   constexpr int EPC = Fmt<DT>::EPC;
-  double acc[2] = {0.0, 0.0};
-#pragma unroll
+  double acc = 0.0;
+#pragma nounroll
   for (int j = 0; j < NC; ++j) {
     float v[EPC];
     r.elems(j, v);
     float t = 0.0f;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) t += weight(v[e], M, c);
-    acc[j & 1] += (double)t;
-    sched_fence();
+    acc += (double)t;
   }
-  return block_sum<kBlock>(acc[0] + acc[1], L.bs);
+  return block_sum<kBlock>(acc, L.bs);
 }
 
 // Lowest index among the maximal logits.
@@ -232,10 +291,11 @@ template <int DT, int NC>
 __device__ __forceinline__ int reg_argmax(const RegRow<DT, NC>& r, float M, Lds& L) {
   constexpr int EPC = Fmt<DT>::EPC;
   int best = 0x7FFFFFFF;
-  if (r.tmax == M) {
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      if (r.cm[j] == M) {
+  if (__any(r.tmax == M)) {
+    unsigned long long m = wave_chunk_mask<NC>([&](int j) { return r.cmax(j) == M; });
+    while (m) {
+      const int j = pop_low(m);
+      if (r.cmax(j) == M) {
         float v[EPC];
         r.elems(j, v);
 #pragma unroll
@@ -250,13 +310,13 @@ __device__ __forceinline__ int reg_argmax(const RegRow<DT, NC>& r, float M, Lds&
 // ---------------------------------------------------------------- the walk
 // Inverse-CDF draw in ascending token id over per-element weights: the first
 // element whose running total exceeds u * (total weight). cw(j, w) fills the
-// EPC weights of chunk j (j is a compile-time constant after unrolling).
+// EPC weights of chunk row j (j is wavefront-uniform).
 // Returns the element index; *total_out gets the total weight.
 template <int NC, int EPC, class CW>
 __device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* total_out) {
   static_assert(NC <= kWalkBatch, "walk scratch too small");
   const int tid = threadIdx.x, lane = __lane_id(), wid = tid / kWave;
-#pragma unroll
+#pragma nounroll
   for (int j = 0; j < NC; ++j) {
     float w[EPC];
     cw(j, w);
@@ -289,15 +349,11 @@ __device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* tota
     }
   }
   __syncthreads();
-  const int jstar = L.si[2];
+  const int jstar = __builtin_amdgcn_readfirstlane(L.si[2]);
   const double r1 = L.sd[2];
   *total_out = L.sd[3];
   float wj[EPC];
-#pragma unroll
-  for (int e = 0; e < EPC; ++e) wj[e] = 0.0f;
-#pragma unroll
-  for (int j = 0; j < NC; ++j)
-    if (j == jstar) cw(j, wj);
+  cw(jstar, wj);
   double mine = 0.0;
 #pragma unroll
   for (int e = 0; e < EPC; ++e) mine += (double)wj[e];
@@ -338,7 +394,7 @@ struct KeptWeights {
   float tau, M, c;
   __device__ __forceinline__ void operator()(int j, float* w) const {
     constexpr int EPC = Fmt<DT>::EPC;
-    if (r.cm[j] >= tau) {
+    if (r.cmax(j) >= tau) {
       float v[EPC];
       r.elems(j, v);
 #pragma unroll
@@ -357,19 +413,19 @@ __device__ __forceinline__ void reg_kept_stats(const RegRow<DT, NC>& r, float ta
   constexpr int EPC = Fmt<DT>::EPC;
   int n = 0;
   float mn = kPosInf;
-  if (r.tmax >= tau) {
+  if (__any(r.tmax >= tau)) {
+    unsigned long long m = wave_chunk_mask<NC>([&](int j) { return r.cmax(j) >= tau; });
+    while (m) {
+      const int j = pop_low(m);
+      float v[EPC];
+      r.elems(j, v);
 #pragma unroll
-    for (int j = 0; j < NC; ++j)
-      if (r.cm[j] >= tau) {
-        float v[EPC];
-        r.elems(j, v);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e)
-          if (v[e] >= tau) {
-            ++n;
-            mn = fminf(mn, v[e]);
-          }
-      }
+      for (int e = 0; e < EPC; ++e)
+        if (v[e] >= tau) {
+          ++n;
+          mn = fminf(mn, v[e]);
+        }
+    }
   }
   *count = block_sum<kBlock>(n, L.bs);
   *vmin = block_min<kBlock>(mn, L.bs);
@@ -380,16 +436,16 @@ __device__ __forceinline__ double reg_kept_mass(const RegRow<DT, NC>& r, float t
                                                 float c, Lds& L) {
   constexpr int EPC = Fmt<DT>::EPC;
   double s = 0.0;
+  unsigned long long m = wave_chunk_mask<NC>([&](int j) { return r.cmax(j) >= tau; });
+  while (m) {
+    const int j = pop_low(m);
+    float v[EPC];
+    r.elems(j, v);
+    float t = 0.0f;
 #pragma unroll
-  for (int j = 0; j < NC; ++j)
-    if (r.cm[j] >= tau) {
-      float v[EPC];
-      r.elems(j, v);
-      float t = 0.0f;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) t += v[e] >= tau ? weight(v[e], M, c) : 0.0f;
-      s += (double)t;
-    }
+    for (int e = 0; e < EPC; ++e) t += v[e] >= tau ? weight(v[e], M, c) : 0.0f;
+    s += (double)t;
+  }
   return block_sum<kBlock>(s, L.bs);
 }
 
@@ -413,20 +469,19 @@ __device__ __forceinline__ void wave_compact(const RegRow<DT, NC>& r, float Lb, 
   const int wid = threadIdx.x / kWave;
   int base = 0;
   if (__any(r.tmax >= Lb)) {
+    unsigned long long m = wave_chunk_mask<NC>([&](int j) { return r.cmax(j) >= Lb; });
+    while (m && base <= kWaveCap) {
+      const int j = pop_low(m);
+      float v[EPC];
+      r.elems(j, v);
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      if (base <= kWaveCap && __any(r.cm[j] >= Lb)) {
-        float v[EPC];
-        r.elems(j, v);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const bool hit = v[e] >= Lb;
-          const unsigned long long b = __ballot(hit);
-          const int slot = base + (int)__builtin_amdgcn_mbcnt_hi(
-                                      (uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
-          if (hit && slot < kWaveCap) L.wkey[wid][slot] = cand_key(v[e], r.base(j) + e);
-          base += __popcll(b);
-        }
+      for (int e = 0; e < EPC; ++e) {
+        const bool hit = v[e] >= Lb;
+        const unsigned long long b = __ballot(hit);
+        const int slot = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                    (uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+        if (hit && slot < kWaveCap) L.wkey[wid][slot] = cand_key(v[e], r.base(j) + e);
+        base += __popcll(b);
       }
     }
   }
@@ -465,9 +520,11 @@ __device__ __forceinline__ float topk_sketch(const RegRow<DT, NC>& r, float M, f
   if (by_thread) {
     if (r.tmax >= lo) atomicAdd(&L.hcnt[sbin(r.tmax)], 1u);
   } else {
-#pragma unroll
-    for (int j = 0; j < NC; ++j)
-      if (r.cm[j] >= lo) atomicAdd(&L.hcnt[sbin(r.cm[j])], 1u);
+#pragma nounroll
+    for (int j = 0; j < NC; ++j) {
+      const float x = r.cmax(j);
+      if (x >= lo) atomicAdd(&L.hcnt[sbin(x)], 1u);
+    }
   }
   __syncthreads();
   if (tid < kWave) {
@@ -496,9 +553,11 @@ __device__ __forceinline__ float topk_sketch(const RegRow<DT, NC>& r, float M, f
     if (by_thread) {
       if (r.tmax >= lo && sbin(r.tmax) == bk) atomicMin(&L.su[0], fkey(r.tmax));
     } else {
-#pragma unroll
-      for (int j = 0; j < NC; ++j)
-        if (r.cm[j] >= lo && sbin(r.cm[j]) == bk) atomicMin(&L.su[0], fkey(r.cm[j]));
+#pragma nounroll
+      for (int j = 0; j < NC; ++j) {
+        const float x = r.cmax(j);
+        if (x >= lo && sbin(x) == bk) atomicMin(&L.su[0], fkey(x));
+      }
     }
   }
   __syncthreads();
@@ -561,15 +620,14 @@ __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, floa
   }
   // more than one wavefront's worth: count, compact in thread order, sort
   int cnt = 0;
-  if (r.tmax >= Lb) {
+  const unsigned long long cmask = wave_chunk_mask<NC>([&](int j) { return r.cmax(j) >= Lb; });
+  unsigned long long m = cmask;
+  while (m) {
+    const int j = pop_low(m);
+    float v[EPC];
+    r.elems(j, v);
 #pragma unroll
-    for (int j = 0; j < NC; ++j)
-      if (r.cm[j] >= Lb) {
-        float v[EPC];
-        r.elems(j, v);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) cnt += (v[e] >= Lb) ? 1 : 0;
-      }
+    for (int e = 0; e < EPC; ++e) cnt += (v[e] >= Lb) ? 1 : 0;
   }
   int total;
   int off = block_excl_scan<kBlock>(cnt, &total, L.bs);
@@ -577,16 +635,14 @@ __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, floa
     out.ok = 0;
     return out;
   }
-  if (cnt) {
+  m = __any(cnt != 0) ? cmask : 0ull;
+  while (m) {
+    const int j = pop_low(m);
+    float v[EPC];
+    r.elems(j, v);
 #pragma unroll
-    for (int j = 0; j < NC; ++j)
-      if (r.cm[j] >= Lb) {
-        float v[EPC];
-        r.elems(j, v);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e)
-          if (v[e] >= Lb && off < kCap) L.key[off++] = cand_key(v[e], r.base(j) + e);
-      }
+    for (int e = 0; e < EPC; ++e)
+      if (v[e] >= Lb && off < kCap) L.key[off++] = cand_key(v[e], r.base(j) + e);
   }
   const double Z = joint_p ? reg_weight_sum(r, M, c, L) : 0.0;
   __syncthreads();
