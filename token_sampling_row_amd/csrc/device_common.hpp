@@ -332,10 +332,13 @@ __device__ __forceinline__ unsigned long long cx_layer(unsigned long long x) {
   const unsigned long long y = ((unsigned long long)phi << 32) | plo;
   return ((x > y) != low) ? y : x;
 }
-// Sorts one 64-bit key per lane into descending lane order across the whole
-// wavefront (bitonic network in its mirror form: every comparator keeps the
-// larger key in the lower lane). All 64 lanes must be active.
+// Sorts one 64-bit key per lane into descending lane order inside each aligned
+// block of W lanes (W = 16: DPP only; W = 64: the whole wavefront), with the
+// bitonic network in its mirror form: every comparator keeps the larger key
+// in the lower lane. All 64 lanes must be active.
+template <int W>
 __device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long x) {
+  static_assert(W == 16 || W == 64, "sort width");
   x = cx_layer<2, true>(x);
   x = cx_layer<4, true>(x);
   x = cx_layer<1, false>(x);
@@ -346,17 +349,19 @@ __device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long 
   x = cx_layer<4, false>(x);
   x = cx_layer<2, false>(x);
   x = cx_layer<1, false>(x);
-  x = cx_layer<32, true>(x);
-  x = cx_layer<8, false>(x);
-  x = cx_layer<4, false>(x);
-  x = cx_layer<2, false>(x);
-  x = cx_layer<1, false>(x);
-  x = cx_layer<64, true>(x);
-  x = cx_layer<16, false>(x);
-  x = cx_layer<8, false>(x);
-  x = cx_layer<4, false>(x);
-  x = cx_layer<2, false>(x);
-  x = cx_layer<1, false>(x);
+  if constexpr (W == 64) {
+    x = cx_layer<32, true>(x);
+    x = cx_layer<8, false>(x);
+    x = cx_layer<4, false>(x);
+    x = cx_layer<2, false>(x);
+    x = cx_layer<1, false>(x);
+    x = cx_layer<64, true>(x);
+    x = cx_layer<16, false>(x);
+    x = cx_layer<8, false>(x);
+    x = cx_layer<4, false>(x);
+    x = cx_layer<2, false>(x);
+    x = cx_layer<1, false>(x);
+  }
   return x;
 }
 

@@ -136,6 +136,7 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   RegRow<DT, NC> r;
   r.load(p, V, ragged != 0);
   const bool greedy = (kp.flags & F_GREEDY) != 0;
+  const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);   // while the loads fly
   const RowStats st = reg_stats(r, !greedy && joint_top_p(kp), kp.c, L);
   if (st.status != 0) {
     write_row(row, -1, st.status, 0, kNegInf, 0.0, out, dg);
@@ -149,7 +150,6 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   }
   const float M = st.M, c = kp.c;
   const Filters f = make_filters(kp, M);
-  const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);
   float tau = -kFltMax;     // no filter: every finite logit
   int kept = -1, tok;
   double zs;

@@ -297,37 +297,48 @@ __device__ __forceinline__ int find_boundary(Lds& L, int cnt_above, double mass_
 // Wave 0 resolves the candidates of the per-wavefront regions (at most
 // kWaveCap in all; every logit >= the candidate bound, which is <= tau) and
 // draws from S in token-id order.
-//  - Value order (when top-k can cut or top-p is on): the candidates are
-//    sorted by (value, lowest id first); the first position of a lane's tie
-//    group is the number of logits strictly above it, and an exclusive scan
-//    of the weights at that position is their mass. Every filter keeps a
-//    prefix of this order.
+//  - Value order, needed only when top-k can cut (more candidates than k) or
+//    top-p may drop a group: the candidates are sorted by (value, lowest id
+//    first); the first position of a lane's tie group is the number of logits
+//    strictly above it, and an exclusive scan of the weights at that position
+//    is their mass. Every filter keeps a prefix of this order. Top-p keeps
+//    every group for certain when the mass above the lowest group is already
+//    below the threshold.
 //  - JOINT top-p compares against top_p * Z. With only a lower bound of Z
 //    (z_exact false) a group that the bound would drop might be kept by the
 //    exact Z: then nothing is decided, L.si[7] is set and the caller calls
 //    again with the exact Z.
 //  - The draw: the kept candidates sorted by token id, an inclusive scan of
 //    their weights C, and the first id with u * Z_S < C.
+// At most 16 candidates are sorted inside the first 16 lanes (DPP only).
 // Results: L.si[0] token, L.si[1] |S|, L.sf[0] tau, L.sd[1] Z_S (sum of
 // weights over S), L.si[7] 0 or 1 (see above). Wave 0 only, all lanes active.
-__device__ __forceinline__ void wave_resolve_draw(Lds& L, float M, float c, const Filters& f,
-                                                  double zref, bool z_exact, double u) {
+template <int W>
+__device__ __forceinline__ void wave_resolve_draw_w(Lds& L, unsigned long long key, int n, float M,
+                                                    float c, const Filters& f, double zref,
+                                                    bool z_exact, double u) {
   const int lane = __lane_id();
-  unsigned long long key = 0ull;
-  int n = 0;
-#pragma unroll
-  for (int q = 0; q < kWaves; ++q) {
-    const int cq = L.wcnt[q];
-    if (lane >= n && lane < n + cq) key = L.wkey[q][lane - n];
-    n += cq;
-  }
   const uint32_t kM = fkey(M);
   const bool seq_kp = f.seq && f.k_on && f.p_on;
+  const bool k_cuts = f.k_on && n > f.k;
   bool keep;
   int n_in;
   float tau;
-  if ((f.k_on && n > f.k) || f.p_on) {
-    key = wave_sort_desc(key);
+  bool sorted = k_cuts;
+  if (!k_cuts && f.p_on) {
+    // top-p is certain to keep every group when the mass above the lowest
+    // group is below its threshold (top-k keeps all n candidates here)
+    const bool valid = lane < n;
+    const uint32_t kh = key_hi(key);
+    const double w = valid ? (double)weight(key2f(kh), M, c) : 0.0;
+    const double wall = wave_sum(w);
+    const uint32_t kmin = wave_min_u32(valid ? kh : 0xFFFFFFFFu);
+    const double above = wall - wave_sum(valid && kh == kmin ? w : 0.0);
+    const double thr = f.top_p * (seq_kp ? wall : (z_exact ? zref : zref * (1.0 - 1e-4)));
+    sorted = !(above < thr) && kmin != kM;
+  }
+  if (sorted) {
+    key = wave_sort_desc<W>(key);
     const bool valid = lane < n;
     const uint32_t kh = key_hi(key);
     const float v = key2f(kh);
@@ -363,7 +374,7 @@ __device__ __forceinline__ void wave_resolve_draw(Lds& L, float M, float c, cons
   }
   // token-id order: (~id) << 32 | value key, descending
   key = keep ? (((unsigned long long)(uint32_t)key << 32) | key_hi(key)) : 0ull;
-  key = wave_sort_desc(key);
+  key = wave_sort_desc<W>(key);
   const bool in = lane < n_in;
   const uint32_t idx = ~key_hi(key);
   const double w = in ? (double)weight(key2f((uint32_t)key), M, c) : 0.0;
@@ -386,6 +397,23 @@ __device__ __forceinline__ void wave_resolve_draw(Lds& L, float M, float c, cons
     L.sf[0] = tau;
     L.sd[1] = total;
   }
+}
+
+__device__ __forceinline__ void wave_resolve_draw(Lds& L, float M, float c, const Filters& f,
+                                                  double zref, bool z_exact, double u) {
+  const int lane = __lane_id();
+  unsigned long long key = 0ull;
+  int n = 0;
+#pragma unroll
+  for (int q = 0; q < kWaves; ++q) {
+    const int cq = L.wcnt[q];
+    if (lane >= n && lane < n + cq) key = L.wkey[q][lane - n];
+    n += cq;
+  }
+  if (n <= 16)
+    wave_resolve_draw_w<16>(L, key, n, M, c, f, zref, z_exact, u);
+  else
+    wave_resolve_draw_w<64>(L, key, n, M, c, f, zref, z_exact, u);
 }
 
 }  // namespace tsr

@@ -462,13 +462,19 @@ struct FastOut {
 // Single-pass compaction of the logits >= Lb into the wavefront's own LDS
 // region, in ballot order. Chunks no lane of the wavefront can contribute to
 // are skipped on their maxima; a wavefront stops once it has more than
-// kWaveCap (then the caller takes another route).
+// kWaveCap (then the caller takes another route), and does not start when more
+// than kWaveCap/4 of its threads hold a candidate: the row then has too many
+// for one wavefront unless its candidates are concentrated in this wavefront,
+// and the caller's other routes give the same result.
 template <int DT, int NC>
 __device__ __forceinline__ void wave_compact(const RegRow<DT, NC>& r, float Lb, Lds& L) {
   constexpr int EPC = Fmt<DT>::EPC;
   const int wid = threadIdx.x / kWave;
   int base = 0;
-  if (__any(r.tmax >= Lb)) {
+  const int holders = __popcll(__ballot(r.tmax >= Lb));
+  if (holders > kWaveCap / 4) {
+    base = kWaveCap + 1;
+  } else if (holders) {
     unsigned long long m = wave_chunk_mask<NC>([&](int j) { return r.cmax(j) >= Lb; });
     while (m && base <= kWaveCap) {
       const int j = pop_low(m);
