@@ -365,13 +365,13 @@ __device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long 
   return x;
 }
 
-// v_max3_f32 without the canonicalising moves the compiler adds around fmaxf
-// (operands here are never signalling NaNs that matter: NaN rows are detected
-// on the raw bits).
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+// NaN-propagating maxima (IEEE 754-2019 maximum; v_maximum3_f32 on gfx950):
+// a NaN anywhere in a row reaches the row maximum, which is how NaN rows are
+// detected, with no per-element test.
+__device__ __forceinline__ float fmaxn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float fmax3n(float a, float b, float c) { return fmaxn(fmaxn(a, b), c); }
+__device__ __forceinline__ float wave_maxn(float x) {
+  return wave_reduce(x, [](float a, float b) { return fmaxn(a, b); });
 }
 
 // ------------------------------------------------------------ block ops

@@ -32,7 +32,10 @@ struct Lds {
   uint32_t hcnt[kBins];             // histogram counts
   unsigned long long hmass[kBins];  // histogram masses, fixed point 2^-40
   double jsum[kWaves * kWalkBatch]; // walk: per (wave, chunk row) sums
-  unsigned long long wkey[kWaves][kWaveCap];  // candidates, one region per wavefront
+  struct WaveCands {                // candidates found by one wavefront
+    uint32_t val[kWaveCap];         // value bits (float32)
+    uint32_t idx[kWaveCap];         // token ids
+  } wc[kWaves];
   int wcnt[kWaves];                 // candidates found by each wavefront
   WaveStats ws[kWaves];
   BlockScratch bs;
@@ -407,7 +410,8 @@ __device__ __forceinline__ void wave_resolve_draw(Lds& L, float M, float c, cons
 #pragma unroll
   for (int q = 0; q < kWaves; ++q) {
     const int cq = L.wcnt[q];
-    if (lane >= n && lane < n + cq) key = L.wkey[q][lane - n];
+    if (lane >= n && lane < n + cq)
+      key = cand_key(__uint_as_float(L.wc[q].val[lane - n]), (int)L.wc[q].idx[lane - n]);
     n += cq;
   }
   if (n <= 16)

@@ -141,58 +141,19 @@ __device__ __forceinline__ int pop_low(unsigned long long& m) {
   return j;
 }
 
-// NaN / +inf detector on the raw bits (-inf is a valid logit: a masked
-// token). f32: a signed maximum reaches 0x7F800000 only for +inf or a
-// positive NaN, an unsigned maximum passes 0xFF800000 only for a negative
-// NaN. bf16: the same two tests on each 16-bit half with packed maxima.
-template <int DT> struct BadAcc;
-template <> struct BadAcc<0> {
-  int32_t smax = (int32_t)0x80000000;
-  uint32_t umax = 0u;
-  __device__ __forceinline__ void add(uint4 t) {
-    smax = max(max(smax, max((int32_t)t.x, (int32_t)t.y)), max((int32_t)t.z, (int32_t)t.w));
-    umax = max(max(umax, max(t.x, t.y)), max(t.z, t.w));
-  }
-  __device__ __forceinline__ bool bad() const { return smax >= 0x7F800000 || umax > 0xFF800000u; }
-};
-template <> struct BadAcc<1> {
-  typedef short s2 __attribute__((ext_vector_type(2)));
-  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-  s2 smax = {(short)0x8000, (short)0x8000};
-  us2 umax = {0, 0};
-  __device__ __forceinline__ void add(uint4 t) {
-    smax = __builtin_elementwise_max(
-        __builtin_elementwise_max(smax, __builtin_bit_cast(s2, t.x)),
-        __builtin_elementwise_max(__builtin_elementwise_max(__builtin_bit_cast(s2, t.y),
-                                                            __builtin_bit_cast(s2, t.z)),
-                                  __builtin_bit_cast(s2, t.w)));
-    umax = __builtin_elementwise_max(
-        __builtin_elementwise_max(umax, __builtin_bit_cast(us2, t.x)),
-        __builtin_elementwise_max(__builtin_elementwise_max(__builtin_bit_cast(us2, t.y),
-                                                            __builtin_bit_cast(us2, t.z)),
-                                  __builtin_bit_cast(us2, t.w)));
-  }
-  __device__ __forceinline__ bool bad() const {
-    return smax.x >= (short)0x7F80 || smax.y >= (short)0x7F80 ||
-           umax.x > (unsigned short)0xFF80 || umax.y > (unsigned short)0xFF80;
-  }
-};
-
-// Largest element of a chunk, with v_max3 (both halves of a bf16 word widened
-// exactly). A NaN element may make the result NaN; such rows are flagged by
-// BadAcc and never reach the chunk tests.
+// Largest element of a chunk (both halves of a bf16 word widened exactly);
+// NaN if the chunk holds one.
 template <int DT>
 __device__ __forceinline__ float chunk_max(uint4 t) {
+  float v[Fmt<DT>::EPC];
+  unpack<DT>(t, v);
   if constexpr (DT == 0) {
-    const float m = max3f(__uint_as_float(t.x), __uint_as_float(t.y), __uint_as_float(t.z));
-    return max3f(m, __uint_as_float(t.w), __uint_as_float(t.w));
+    return fmax3n(fmax3n(v[0], v[1], v[2]), v[3], v[3]);
   } else {
-    float v[8];
-    unpack<1>(t, v);
-    float m = max3f(v[0], v[1], v[2]);
-    m = max3f(m, v[3], v[4]);
-    m = max3f(m, v[5], v[6]);
-    return max3f(m, v[7], v[7]);
+    float m = fmax3n(v[0], v[1], v[2]);
+    m = fmax3n(m, v[3], v[4]);
+    m = fmax3n(m, v[5], v[6]);
+    return fmaxn(m, v[7]);
   }
 }
 
@@ -213,17 +174,15 @@ struct RowStats {
 template <int DT, int NC>
 __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, float c, Lds& L) {
   float tmax = kNegInf;
-  BadAcc<DT> bad;
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     uint4 t = r.get(j);
     asm volatile("" : "+v"(t.x), "+v"(t.y), "+v"(t.z), "+v"(t.w));
     t = r.settle(j, t);
     r.put(j, t);
-    bad.add(t);
     const float m = chunk_max<DT>(t);
     r.put_cmax(j, m);
-    tmax = max3f(tmax, m, m);
+    tmax = fmaxn(tmax, m);
     asm volatile("" : "+v"(tmax));
   }
   r.tmax = tmax;
@@ -235,9 +194,9 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
     zt = (double)s;
   }
   // wave level
-  const float wm = wave_max(tmax);
+  const float wm = wave_maxn(tmax);
   const float wt = wave_min(tmax > kNegInf ? tmax : kPosInf);
-  const int wb = __any(bad.bad()) ? 1 : 0;
+  const int wb = 0;
   double wz = 0.0;
   if (need_zlo)   // relative to the wave max
     wz = wave_sum(tmax > kNegInf && tmax < kPosInf ? zt * (double)weight(tmax, wm, c) : 0.0);
@@ -250,7 +209,7 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
   int anybad = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    M = fmaxf(M, L.ws[w].m);
+    M = fmaxn(M, L.ws[w].m);
     tmin = fminf(tmin, L.ws[w].smin);
     anybad |= L.ws[w].bad;
   }
@@ -264,7 +223,8 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
   st.M = M;
   st.tmin = tmin;
   st.zlo = Z;
-  st.status = (anybad || M == kPosInf) ? 1 : (M > kNegInf ? 0 : 2);
+  // NaN or +inf anywhere in the row shows in its (NaN-propagating) maximum
+  st.status = (anybad || M != M || M == kPosInf) ? 1 : (M > kNegInf ? 0 : 2);
   return st;
 }
 
@@ -480,14 +440,29 @@ __device__ __forceinline__ void wave_compact(const RegRow<DT, NC>& r, float Lb, 
       const int j = pop_low(m);
       float v[EPC];
       r.elems(j, v);
+      // all compares first (one VALU op each); the append only for the
+      // elements some lane holds (usually one per chunk)
+      bool hit[EPC];
+      unsigned long long b[EPC];
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
-        const bool hit = v[e] >= Lb;
-        const unsigned long long b = __ballot(hit);
-        const int slot = base + (int)__builtin_amdgcn_mbcnt_hi(
-                                    (uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
-        if (hit && slot < kWaveCap) L.wkey[wid][slot] = cand_key(v[e], r.base(j) + e);
-        base += __popcll(b);
+        hit[e] = v[e] >= Lb;
+        b[e] = __ballot(hit[e]);
+      }
+      const int ib = r.base(j);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        if (b[e]) {
+          const int nb = base + __popcll(b[e]);
+          if (nb <= kWaveCap && hit[e]) {
+            const int slot = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                        (uint32_t)(b[e] >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)b[e], 0u));
+            L.wc[wid].val[slot] = __float_as_uint(v[e]);
+            L.wc[wid].idx[slot] = (uint32_t)(ib + e);
+          }
+          base = nb;
+        }
       }
     }
   }
