@@ -138,6 +138,12 @@ template <int CTRL, int ROWMASK = 0xF>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWMASK, 0xF, false);
 }
+// A DPP permutation in which every lane reads a valid lane (quad_perm, row
+// mirrors, row rotations): no "old" value is needed, so none is materialised.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_perm_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+}
 template <int CTRL, int ROWMASK = 0xF>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __uint_as_float(dpp_u32<CTRL, ROWMASK>(__float_as_uint(x)));
@@ -175,6 +181,16 @@ __device__ __forceinline__ T dpp_t(T x) {
     return __builtin_bit_cast(T, dpp_u64<CTRL, ROWMASK>(__builtin_bit_cast(unsigned long long, x)));
   }
 }
+template <int CTRL, class T>
+__device__ __forceinline__ T dpp_perm_t(T x) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, dpp_perm_u32<CTRL>(__builtin_bit_cast(uint32_t, x)));
+  } else {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+    const uint32_t lo = dpp_perm_u32<CTRL>((uint32_t)u), hi = dpp_perm_u32<CTRL>((uint32_t)(u >> 32));
+    return __builtin_bit_cast(T, ((unsigned long long)hi << 32) | lo);
+  }
+}
 template <class T>
 __device__ __forceinline__ T readlane_t(T x, int l) {
   if constexpr (sizeof(T) == 4) {
@@ -187,10 +203,10 @@ __device__ __forceinline__ T readlane_t(T x, int l) {
 // Butterfly inside each 16-lane row, then the four row results in fixed order.
 template <class T, class Op>
 __device__ __forceinline__ T wave_reduce(T x, Op op) {
-  x = op(x, dpp_t<kDppXor1>(x));
-  x = op(x, dpp_t<kDppXor2>(x));
-  x = op(x, dpp_t<kDppHalfMirror>(x));
-  x = op(x, dpp_t<kDppMirror>(x));
+  x = op(x, dpp_perm_t<kDppXor1>(x));
+  x = op(x, dpp_perm_t<kDppXor2>(x));
+  x = op(x, dpp_perm_t<kDppHalfMirror>(x));
+  x = op(x, dpp_perm_t<kDppMirror>(x));
   return op(op(readlane_t(x, 0), readlane_t(x, 16)), op(readlane_t(x, 32), readlane_t(x, 48)));
 }
 __device__ __forceinline__ float wave_max(float x) {
@@ -279,14 +295,14 @@ __device__ __forceinline__ double wave_incl_max_scan(double x) {
 template <int D>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
   if constexpr (D == 1) {
-    return dpp_u32<kDppXor1>(x);
+    return dpp_perm_u32<kDppXor1>(x);
   } else if constexpr (D == 2) {
-    return dpp_u32<kDppXor2>(x);
+    return dpp_perm_u32<kDppXor2>(x);
   } else if constexpr (D == 4) {
-    const uint32_t dn = dpp_u32<kDppRor4>(x), up = dpp_u32<kDppRor12>(x);
+    const uint32_t dn = dpp_perm_u32<kDppRor4>(x), up = dpp_perm_u32<kDppRor12>(x);
     return (__lane_id() & 4) ? dn : up;
   } else if constexpr (D == 8) {
-    return dpp_u32<kDppRor8>(x);
+    return dpp_perm_u32<kDppRor8>(x);
   } else if constexpr (D == 16) {
     return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F);  // and 31, xor 16
   } else {
@@ -298,13 +314,13 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
 template <int S>
 __device__ __forceinline__ uint32_t lane_mirror(uint32_t x) {
   if constexpr (S == 2) {
-    return dpp_u32<kDppXor1>(x);
+    return dpp_perm_u32<kDppXor1>(x);
   } else if constexpr (S == 4) {
-    return dpp_u32<kDppQuadMirror>(x);
+    return dpp_perm_u32<kDppQuadMirror>(x);
   } else if constexpr (S == 8) {
-    return dpp_u32<kDppHalfMirror>(x);
+    return dpp_perm_u32<kDppHalfMirror>(x);
   } else if constexpr (S == 16) {
-    return dpp_u32<kDppMirror>(x);
+    return dpp_perm_u32<kDppMirror>(x);
   } else if constexpr (S == 32) {
     return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x7C1F);  // and 31, xor 31
   } else {

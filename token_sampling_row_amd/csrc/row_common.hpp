@@ -324,9 +324,14 @@ __device__ __forceinline__ void wave_resolve_draw_w(Lds& L, unsigned long long k
   const uint32_t kM = fkey(M);
   const bool seq_kp = f.seq && f.k_on && f.p_on;
   const bool k_cuts = f.k_on && n > f.k;
-  bool keep;
   int n_in;
   float tau;
+  // token-id order for the draw: (~id) << 32 | value key, descending; sorted
+  // alongside the value order (two independent chains the scheduler can
+  // interleave) and masked by S = {v >= tau} afterwards
+  const unsigned long long idkey =
+      lane < n ? (((unsigned long long)(uint32_t)key << 32) | key_hi(key)) : 0ull;
+  unsigned long long ids;
   bool sorted = k_cuts;
   if (!k_cuts && f.p_on) {
     // top-p is certain to keep every group when the mass above the lowest
@@ -341,6 +346,7 @@ __device__ __forceinline__ void wave_resolve_draw_w(Lds& L, unsigned long long k
     sorted = !(above < thr) && kmin != kM;
   }
   if (sorted) {
+    ids = wave_sort_desc<W>(idkey);
     key = wave_sort_desc<W>(key);
     const bool valid = lane < n;
     const uint32_t kh = key_hi(key);
@@ -366,23 +372,23 @@ __device__ __forceinline__ void wave_resolve_draw_w(Lds& L, unsigned long long k
         return;
       }
     }
-    keep = valid && keep_k && keep_m && keep_p;
+    // every filter keeps a prefix of whole groups: S = {v >= tau}
+    const bool keep = valid && keep_k && keep_m && keep_p;
     n_in = __popcll(__ballot(keep));
     tau = key2f(readlane_u32(kh, n_in - 1));
   } else {
+    ids = wave_sort_desc<W>(idkey);
     const uint32_t kh = key_hi(key);
-    keep = lane < n && key2f(kh) >= f.tau_m;
+    const bool keep = lane < n && key2f(kh) >= f.tau_m;
     n_in = __popcll(__ballot(keep));
     tau = key2f(wave_min_u32(keep ? kh : 0xFFFFFFFFu));
   }
-  // token-id order: (~id) << 32 | value key, descending
-  key = keep ? (((unsigned long long)(uint32_t)key << 32) | key_hi(key)) : 0ull;
-  key = wave_sort_desc<W>(key);
-  const bool in = lane < n_in;
-  const uint32_t idx = ~key_hi(key);
-  const double w = in ? (double)weight(key2f((uint32_t)key), M, c) : 0.0;
+  const float vi = key2f((uint32_t)ids);
+  const bool in = lane < n && vi >= tau;
+  const uint32_t idx = ~key_hi(ids);
+  const double w = in ? (double)weight(vi, M, c) : 0.0;
   const double C = wave_incl_scan(w);
-  const double total = readlane_t(C, n_in - 1);
+  const double total = readlane_t(C, 63);
   const double target = u * total;
   const unsigned long long hit = __ballot(in && C > target);
   int pos;
@@ -405,15 +411,21 @@ __device__ __forceinline__ void wave_resolve_draw_w(Lds& L, unsigned long long k
 __device__ __forceinline__ void wave_resolve_draw(Lds& L, float M, float c, const Filters& f,
                                                   double zref, bool z_exact, double u) {
   const int lane = __lane_id();
-  unsigned long long key = 0ull;
-  int n = 0;
+  // all counts first (independent LDS reads), then one read per lane
+  int cq[kWaves];
+#pragma unroll
+  for (int q = 0; q < kWaves; ++q) cq[q] = L.wcnt[q];
+  int n = 0, sq = 0, so = 0;
 #pragma unroll
   for (int q = 0; q < kWaves; ++q) {
-    const int cq = L.wcnt[q];
-    if (lane >= n && lane < n + cq)
-      key = cand_key(__uint_as_float(L.wc[q].val[lane - n]), (int)L.wc[q].idx[lane - n]);
-    n += cq;
+    if (lane >= n && lane < n + cq[q]) {
+      sq = q;
+      so = lane - n;
+    }
+    n += cq[q];
   }
+  unsigned long long key = 0ull;
+  if (lane < n) key = cand_key(__uint_as_float(L.wc[sq].val[so]), (int)L.wc[sq].idx[so]);
   if (n <= 16)
     wave_resolve_draw_w<16>(L, key, n, M, c, f, zref, z_exact, u);
   else
