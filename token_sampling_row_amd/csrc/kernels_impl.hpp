@@ -86,6 +86,46 @@ __device__ __noinline__ void diag_finish(const StreamRow<DT> s, int row, int tok
   if (dg.probs) stream_probs(s, tau, M, c, zs, dg.probs + (long long)row * s.V);
 }
 
+// A register-resident row seen through the StreamRow interface, so the
+// general kept-set search can run on it without re-reading HBM.
+template <int DT, int NC>
+struct RegView {
+  const RegRow<DT, NC>& r;
+  static constexpr int nct = NC;
+  __device__ __forceinline__ void elems(int j, float* v, float* m) const {
+    r.elems(j, v);
+    *m = r.cmax(j);
+  }
+  __device__ __forceinline__ int base(int j) const { return r.base(j); }
+};
+
+// The kept set of a register-resident row whose candidates did not fit the
+// LDS buffer: the histogram search of the streaming path, over the registers.
+template <int DT, int NC>
+__device__ __forceinline__ Cut reg_general(const RegRow<DT, NC>& r, float M, float c, float cR,
+                                           const Filters& f, Lds& L) {
+  if (!f.k_on && !f.p_on) {   // min-p alone: its cut is the kept set
+    Cut cut;
+    cut.tau = f.tau_m > kNegInf ? f.tau_m : -kFltMax;
+    cut.kept = -1;
+    cut.zs = -1.0;
+    return cut;
+  }
+  const RegView<DT, NC> s{r};
+  if (f.seq && f.k_on && f.p_on) {
+    // SEQUENTIAL: top-k alone first; its kept mass is top-p's reference
+    Filters fk = f;
+    fk.p_on = false;
+    fk.m_on = false;
+    fk.tau_m = kNegInf;
+    const Cut ck = general_search<DT>(s, M, c, cR, fk, 0.0);
+    const double zk = ck.zs >= 0.0 ? ck.zs : reg_kept_mass(r, ck.tau, M, c, L);
+    return general_search<DT>(s, M, c, cR, f, f.top_p * zk);
+  }
+  const double Z = f.p_on ? reg_weight_sum(r, M, c, L) : 0.0;
+  return general_search<DT>(s, M, c, cR, f, f.p_on ? f.top_p * Z : 0.0);
+}
+
 // ---------------------------------------------------------------- greedy
 
 template <int DT, int NC>
@@ -257,7 +297,7 @@ __device__ __forceinline__ RowCut verify_row_cut(RegRow<DT, NC>& r, const unsign
     rc.zs = fo.zs;
     return rc;
   }
-  const Cut cut = general_stream(StreamRow<DT>(p, V, aligned), st.M, -1.0, kp.c, kp.cR, f);
+  const Cut cut = reg_general(r, st.M, kp.c, kp.cR, f, L);
   rc.tau = cut.tau;
   rc.zs = reg_kept_mass(r, rc.tau, st.M, kp.c, L);
   return rc;
@@ -282,6 +322,7 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt
   RegRow<DT, NC> rp, rq;
   rp.template load<UNALIGNED>(tp, V, ragged != 0);
   if (with_draft) rq.template load<UNALIGNED>(dp, V, ragged != 0);
+  asm volatile("" ::: "memory");   // both rows' loads in flight before any use
   int st_t = 0, st_d = 0, acc = 0, tok = -1;
   const int x = j < K ? xs[(long long)b * K + j] : 0;
   const bool x_ok = x >= 0 && x < V;

@@ -128,10 +128,11 @@ __device__ __noinline__ double stream_weight_sum(const StreamRow<DT> s, float ta
 
 // One kept-set search (see the file comment) for the filters f with top-p
 // threshold thr (in weight units). Returns tau; kept / zs are filled when the
-// search resolved them (else -1).
-template <int DT>
-__device__ __forceinline__ Cut general_search(const StreamRow<DT>& s, float M, float c,
-                                              float cR, const Filters& f, double thr) {
+// search resolved them (else -1). Row is a StreamRow, or a view of a row held
+// in registers with the same interface (nct, elems(j, v, &max), base(j)).
+template <int DT, class Row>
+__device__ __forceinline__ Cut general_search(const Row& s, float M, float c, float cR,
+                                              const Filters& f, double thr) {
   constexpr int EPC = Fmt<DT>::EPC;
   Lds& L = tsr_lds;
   const int tid = threadIdx.x;
@@ -145,6 +146,7 @@ __device__ __forceinline__ Cut general_search(const StreamRow<DT>& s, float M, f
     const float t = (M - v) * cR;
     return t < (float)(kBins - 1) ? (int)t : kBins - 1;
   };
+#pragma unroll 1
   for (int j = 0; j < s.nct; ++j) {
     float v[EPC], m;
     s.elems(j, v, &m);
@@ -186,7 +188,8 @@ __device__ __forceinline__ Cut general_search(const StreamRow<DT>& s, float M, f
   bool contains_max = (d == 0);
   for (int level = 0; level < 4 && ncur > kCap; ++level) {
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-    for (int j = 0; j < s.nct; ++j) {
+  #pragma unroll 1
+  for (int j = 0; j < s.nct; ++j) {
       float v[EPC], m;
       s.elems(j, v, &m);
 #pragma unroll
@@ -211,7 +214,8 @@ __device__ __forceinline__ Cut general_search(const StreamRow<DT>& s, float M, f
       L.hmass[i] = 0ull;
     }
     __syncthreads();
-    for (int j = 0; j < s.nct; ++j) {
+  #pragma unroll 1
+  for (int j = 0; j < s.nct; ++j) {
       float v[EPC], m;
       s.elems(j, v, &m);
 #pragma unroll
@@ -249,6 +253,7 @@ __device__ __forceinline__ Cut general_search(const StreamRow<DT>& s, float M, f
     return cut;
   }
   int cnt = 0;
+#pragma unroll 1
   for (int j = 0; j < s.nct; ++j) {
     float v[EPC], m;
     s.elems(j, v, &m);
@@ -258,7 +263,8 @@ __device__ __forceinline__ Cut general_search(const StreamRow<DT>& s, float M, f
   int total;
   int off = block_excl_scan<kBlock>(cnt, &total, L.bs);
   if (cnt) {
-    for (int j = 0; j < s.nct; ++j) {
+  #pragma unroll 1
+  for (int j = 0; j < s.nct; ++j) {
       float v[EPC], m;
       s.elems(j, v, &m);
 #pragma unroll
@@ -302,12 +308,12 @@ __device__ __noinline__ Cut general_stream(const StreamRow<DT> s, float M, doubl
     fk.p_on = false;
     fk.m_on = false;
     fk.tau_m = kNegInf;
-    const Cut ck = general_search(s, M, c, cR, fk, 0.0);
+    const Cut ck = general_search<DT>(s, M, c, cR, fk, 0.0);
     double zk = ck.zs;
     if (zk < 0.0) zk = stream_weight_sum(s, ck.tau, M, c);
-    return general_search(s, M, c, cR, f, f.top_p * zk);
+    return general_search<DT>(s, M, c, cR, f, f.top_p * zk);
   }
-  return general_search(s, M, c, cR, f, f.p_on ? f.top_p * Z : 0.0);
+  return general_search<DT>(s, M, c, cR, f, f.p_on ? f.top_p * Z : 0.0);
 }
 
 // Inverse-CDF draw over S = {v >= tau} in ascending token id, streaming the
