@@ -168,9 +168,10 @@ struct RowStats {
 // detection, chunk maxima, thread max. The empty asm at the end of each chunk
 // pins the running maximum in program order, so chunk j is reduced as soon as
 // its load has arrived instead of after the whole row.
-// need_zlo: also sum, per thread, the weights of its chunk maxima (one
-// exponential per chunk). That is a lower bound of the row's weight sum Z,
-// enough to settle JOINT top-p whenever the nucleus is not close to the cut.
+// need_zlo: also sum the weights of the per-thread maxima (one exponential
+// per thread). That is a lower bound of the row's
+// weight sum Z, enough to settle JOINT top-p whenever the nucleus is not
+// close to the cut.
 template <int DT, int NC>
 __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, float c, Lds& L) {
   float tmax = kNegInf;
@@ -186,13 +187,8 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
     asm volatile("" : "+v"(tmax));
   }
   r.tmax = tmax;
-  double zt = 0.0;
-  if (need_zlo && tmax > kNegInf && tmax < kPosInf) {
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NC; ++j) s += weight(r.cmax(j), tmax, c);
-    zt = (double)s;
-  }
+  // the thread max's own weight, relative to itself
+  const double zt = (need_zlo && tmax > kNegInf && tmax < kPosInf) ? 1.0 : 0.0;
   // wave level
   const float wm = wave_maxn(tmax);
   const float wt = wave_min(tmax > kNegInf ? tmax : kPosInf);
