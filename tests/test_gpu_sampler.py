@@ -216,17 +216,24 @@ def test_small_grid(dtype, V):
           f"support={tally.support_excused}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("V", [70000, 160001])
-def test_general_path_wide_supports(V):
+def test_general_path_wide_supports(V, dtype):
     """Kept sets far larger than the LDS candidate buffer (the histogram path),
-    in rows held in registers and in rows too wide for them (streamed)."""
+    in rows held in registers and in rows too wide for them (streamed). In
+    bf16, rows of large-magnitude logits take the exact value histogram (one
+    bf16 value per bin), rows near zero its per-element bins and fallbacks."""
     rng = np.random.default_rng(5)
     rows = [rng.normal(0, 0.3, V),                          # flat: huge nucleus
             np.round(rng.normal(0, 0.3, V), 2),             # flat with heavy ties
             np.concatenate([np.zeros(V // 2), np.full(V - V // 2, -0.001)]),  # 2 big groups
-            -0.05 * np.log(rng.permutation(V) + 1.0)]
+            -0.05 * np.log(rng.permutation(V) + 1.0),
+            rng.normal(-12.0, 1.5, V),                      # every value |v| >= 8 (in bf16)
+            -np.log(rng.permutation(V) + 1.0) + rng.normal(0, 0.5, V)]   # mixed magnitudes
     data = np.stack(rows).astype(np.float32)
-    values = vals(data, "f32")
+    if dtype == "bf16":
+        data = wl.f32_to_bf16_bits(data)
+    values = vals(data, dtype)
     seed = 77
     grid = [dict(temperature=1.0, top_p=0.9), dict(temperature=1.0, top_p=0.5, mode=1),
             dict(temperature=1.0, min_p=0.5), dict(temperature=1.0, top_k=30000),
@@ -234,9 +241,9 @@ def test_general_path_wide_supports(V):
             dict(temperature=1.0, top_k=60000, top_p=0.7, mode=1),
             dict(temperature=0.7, top_p=0.999, min_p=0.2), dict(temperature=1.0)]
     with make_sampler(seed) as s:
-        x = to_dev(data, "f32")
+        x = to_dev(data, dtype)
         for i, prm in enumerate(grid):
-            print_case("general", V=V, params=prm)
+            print_case("general", V=V, dtype=dtype, params=prm)
             refs = [oracle.sample_row(values[b], prm, seed, b, i) for b in range(len(rows))]
             got = run_sample(s, x, prm, i, diag=True, probs=True)
             compare(got, refs, list(range(len(rows))), values)

@@ -12,10 +12,15 @@ hipError_t launch_sample_dt1(const unsigned char* p, int rows, int V, long long 
                        stride_bytes, V, aligned, kp, out, dg);
     return hipGetLastError();
   }
+  const bool wide = wide_filters(kp, kBlock);
 #define TSR_CASE(N)                                                                      \
   case N:                                                                                \
-    hipLaunchKernelGGL((sample_kernel<1, N>), dim3(rows), dim3(kBlock), 0, s, p,        \
-                       stride_bytes, V, aligned, ragged, kp, out, dg);                   \
+    if (wide)                                                                            \
+      hipLaunchKernelGGL((sample_kernel<1, N, true>), dim3(rows), dim3(kBlock), 0, s, p, \
+                         stride_bytes, V, aligned, ragged, kp, out, dg);                 \
+    else                                                                                 \
+      hipLaunchKernelGGL((sample_kernel<1, N, false>), dim3(rows), dim3(kBlock), 0, s, p,\
+                         stride_bytes, V, aligned, ragged, kp, out, dg);                 \
     break;
   switch (nc) {
     TSR_ROW_NCS(TSR_CASE)

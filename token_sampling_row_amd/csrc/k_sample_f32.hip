@@ -14,7 +14,7 @@ hipError_t launch_sample_dt0(const unsigned char* p, int rows, int V, long long 
   }
 #define TSR_CASE(N)                                                                      \
   case N:                                                                                \
-    hipLaunchKernelGGL((sample_kernel<0, N>), dim3(rows), dim3(kBlock), 0, s, p,        \
+    hipLaunchKernelGGL((sample_kernel<0, N, false>), dim3(rows), dim3(kBlock), 0, s, p,        \
                        stride_bytes, V, aligned, ragged, kp, out, dg);                   \
     break;
   switch (nc) {

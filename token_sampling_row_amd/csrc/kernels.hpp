@@ -26,6 +26,14 @@ enum : int {
   F_SEQ = 16,     // SEQUENTIAL filter mode
   F_Z = 32,       // the full weight sum is wanted (kept-mass diagnostic)
 };
+// Filters whose kept set may be far larger than any candidate buffer: no
+// top-k, or one too large for the per-thread-maxima sketch (the sampling
+// launch then takes the WIDE kernel instance).
+inline bool wide_filters(const KParams& kp, int block) {
+  if (kp.flags & F_GREEDY) return false;
+  if (!(kp.flags & (F_K | F_P | F_M))) return false;
+  return !(kp.flags & F_K) || kp.top_k > block / 4;
+}
 
 struct DiagPtrs {
   int32_t* status;

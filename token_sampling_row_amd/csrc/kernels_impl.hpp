@@ -99,8 +99,125 @@ struct RegView {
   __device__ __forceinline__ int base(int j) const { return r.base(j); }
 };
 
+// JOINT top-k / top-p over a bf16 row held in registers, exactly, from one
+// histogram pass without an exponential per element. Bins are 1/16 logit
+// wide below the row max, bin b = (M - v) * 16 (exact: bf16 differences are
+// exact in float for rows with |M| <= 2^15). Where |v| >= 8 the bf16 grid
+// spacing is at least 1/16, so such a bin holds a single value: its count
+// and the value (stored by every element of the bin, all alike) give its
+// weight exactly. The other bins (|v| < 8 somewhere in the bin, or past the
+// last bin) sum fixed-point weights per element. The bin masses give Z, the
+// boundary bin (find_boundary) and, when that bin holds one value, the cut;
+// otherwise its elements are sorted and resolved exactly (resolve_sorted).
+// ok = false when the boundary bin holds more than kCap elements (the caller
+// then takes the general search). kept / zs are -1 when min-p cuts deeper.
+template <int NC>
+__device__ __forceinline__ Cut bf16_value_cut(const RegRow<1, NC>& r, float M, float c,
+                                              const Filters& f, Lds& L, bool* ok) {
+  constexpr int EPC = Fmt<1>::EPC;
+  const int tid = threadIdx.x;
+  uint32_t* vals = reinterpret_cast<uint32_t*>(L.pref);   // free until the boundary sort
+  for (int i = tid; i < kBins; i += kBlock) {
+    L.hcnt[i] = 0u;
+    L.hmass[i] = 0ull;
+  }
+  // bins b >= bneg lie wholly at or below -8, bins b <= bpos wholly above 8
+  const int bneg = (int)ceilf((M + 8.0f) * 16.0f);
+  const int bpos = (int)floorf((M - 8.0f) * 16.0f) - 1;
+  auto pure = [&](int b) { return b < kBins - 1 && (b >= bneg || b <= bpos); };
+  __syncthreads();
+#pragma unroll 1
+  for (int j = 0; j < NC; ++j) {
+    float v[EPC];
+    r.elems(j, v);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      if (v[e] > kNegInf) {
+        const float t = (M - v[e]) * 16.0f;
+        const int b = t < (float)(kBins - 1) ? (int)t : kBins - 1;
+        atomicAdd(&L.hcnt[b], 1u);
+        if (pure(b))
+          vals[b] = __float_as_uint(v[e]);
+        else
+          atomicAdd(&L.hmass[b], to_fixed(weight(v[e], M, c)));
+      }
+    }
+  }
+  __syncthreads();
+  double zt = 0.0;
+  for (int b = tid; b < kBins; b += kBlock) {
+    const uint32_t n = L.hcnt[b];
+    if (n && pure(b)) {
+      const double m = (double)n * (double)weight(__uint_as_float(vals[b]), M, c);
+      L.hmass[b] = (unsigned long long)(m * kFix + 0.5);
+    }
+    zt += (double)L.hmass[b] * kInvFix;
+  }
+  const double Z = block_sum<kBlock>(zt, L.bs);
+  const double thr = f.p_on ? f.top_p * Z : 0.0;
+  int add_c = 0;
+  double add_m = 0.0;
+  const int d = find_boundary(L, 0, 0.0, f, thr, true, &add_c, &add_m);
+  *ok = true;
+  Cut cut;
+  const float floor_m = f.tau_m > kNegInf ? f.tau_m : -kFltMax;
+  if (d == kBins) {   // no cut inside the bins
+    cut.tau = floor_m;
+    cut.kept = -1;
+    cut.zs = -1.0;
+    return cut;
+  }
+  if (pure(d)) {      // the boundary bin is one value group, kept whole
+    const float vd = __uint_as_float(vals[d]);
+    cut.tau = fmaxf(vd, floor_m);
+    const bool exact = !(floor_m > vd);
+    cut.kept = exact ? add_c + (int)L.hcnt[d] : -1;
+    cut.zs = exact ? add_m + (double)L.hmass[d] * kInvFix : -1.0;
+    __syncthreads();
+    return cut;
+  }
+  // several values in the boundary bin: its elements, sorted, decide
+  const int nd = (int)L.hcnt[d];
+  __syncthreads();
+  if (nd > kCap) {
+    *ok = false;
+    return cut;
+  }
+  if (tid == 0) L.si[6] = 0;
+  __syncthreads();
+#pragma unroll 1
+  for (int j = 0; j < NC; ++j) {
+    float v[EPC];
+    r.elems(j, v);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      if (v[e] > kNegInf) {
+        const float t = (M - v[e]) * 16.0f;
+        const int b = t < (float)(kBins - 1) ? (int)t : kBins - 1;
+        if (b == d) L.key[atomicAdd(&L.si[6], 1)] = cand_key(v[e], r.base(j) + e);
+      }
+    }
+  }
+  __syncthreads();
+  sort_keys_desc(L, nd);
+  const Resolved res = resolve_sorted(L, nd, add_c, add_m, M, c, f, thr, false);
+  if (res.n_in > 0) {
+    cut.tau = fmaxf(res.tau, floor_m);
+    const bool exact = !(floor_m > res.tau);
+    cut.kept = exact ? add_c + res.n_in : -1;
+    cut.zs = exact ? res.zs : -1.0;
+  } else {            // nothing of the bin stays: S is what lies above it
+    cut.tau = fmaxf(next_up(key2f(key_hi(L.key[0]))), floor_m);
+    cut.kept = -1;
+    cut.zs = -1.0;
+  }
+  __syncthreads();
+  return cut;
+}
+
 // The kept set of a register-resident row whose candidates did not fit the
-// LDS buffer: the histogram search of the streaming path, over the registers.
+// LDS buffer: the histogram search of the streaming path, over the registers
+// (for JOINT bf16 rows, the exact value histogram above first).
 template <int DT, int NC>
 __device__ __forceinline__ Cut reg_general(const RegRow<DT, NC>& r, float M, float c, float cR,
                                            const Filters& f, Lds& L) {
@@ -110,6 +227,13 @@ __device__ __forceinline__ Cut reg_general(const RegRow<DT, NC>& r, float M, flo
     cut.kept = -1;
     cut.zs = -1.0;
     return cut;
+  }
+  if constexpr (DT == 1) {
+    if (!(f.seq && f.k_on && f.p_on) && fabsf(M) <= 32768.0f) {
+      bool ok;
+      const Cut cut = bf16_value_cut(r, M, c, f, L, &ok);
+      if (ok) return cut;
+    }
   }
   const RegView<DT, NC> s{r};
   if (f.seq && f.k_on && f.p_on) {
@@ -164,7 +288,11 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel_stream(const unsigned ch
 
 // ---------------------------------------------------------------- sample_rows
 
-template <int DT, int NC>
+// WIDE (bf16): rows whose kept set the candidate bound cannot narrow are
+// finished over the registers (reg_general, then the walk) instead of by the
+// streaming path. A separate instance, chosen on the host for filters without
+// a small top-k, so the common instance keeps its registers and code size.
+template <int DT, int NC, bool WIDE>
 __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* logits,
                                                         long long stride_bytes, int V,
                                                         int aligned, int ragged, KParams kp,
@@ -196,15 +324,23 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   if (f.k_on || f.p_on || f.m_on) {
     // the cut and the draw; the registers are dead afterwards
     const FastOut fo = fast_cut(r, V, M, st.tmin, st.zlo, c, f, u, L);
-    if (!fo.ok) {
-      // the candidates did not fit: the streaming path finishes this row
+    if (fo.ok) {
+      tau = fo.tau;
+      kept = fo.kept;
+      zs = fo.zs;
+      tok = fo.token;
+    } else if constexpr (DT == 1 && WIDE) {
+      // too many candidates for the LDS buffer: the search over the registers
+      // (the exact value histogram of bf16 rows), then the walk
+      const Cut cut = reg_general(r, M, c, kp.cR, f, L);
+      tau = cut.tau;
+      kept = cut.kept;
+      tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs);
+    } else {
+      // the streaming path finishes this row
       stream_finish(StreamRow<DT>(p, V, true), row, M, -1.0, kp, f, u, out, dg);
       return;
     }
-    tau = fo.tau;
-    kept = fo.kept;
-    zs = fo.zs;
-    tok = fo.token;
   } else {
     tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs);
   }
