@@ -100,58 +100,78 @@ struct RegView {
 };
 
 // JOINT top-k / top-p over a bf16 row held in registers, exactly, from one
-// histogram pass without an exponential per element. Bins are 1/16 logit
-// wide below the row max, bin b = (M - v) * 16 (exact: bf16 differences are
-// exact in float for rows with |M| <= 2^15). Where |v| >= 8 the bf16 grid
-// spacing is at least 1/16, so such a bin holds a single value: its count
-// and the value (stored by every element of the bin, all alike) give its
-// weight exactly. The other bins (|v| < 8 somewhere in the bin, or past the
-// last bin) sum fixed-point weights per element. The bin masses give Z, the
-// boundary bin (find_boundary) and, when that bin holds one value, the cut;
-// otherwise its elements are sorted and resolved exactly (resolve_sorted).
-// ok = false when the boundary bin holds more than kCap elements (the caller
-// then takes the general search). kept / zs are -1 when min-p cuts deeper.
+// histogram pass without an exponential per element. Bins are 1/32 logit
+// wide below the row max, bin b = (M - v) * 32, exact for bf16 rows with
+// |M| <= 2^15 (the difference of two such values is exact in float). Where
+// |v| >= 4 the bf16 grid spacing is at least 1/32, so such a bin holds one
+// value, the largest bf16 value at or below M - b/32; its count gives its
+// weight exactly. The other bins (|v| < 4 somewhere in the bin, or the last
+// bin, past 32 logits below the max) sum fixed-point weights per element.
+// Counts go to kVCopies copies by lane, so lanes that fall in the same bin
+// mostly hit different words. The bin masses give Z, the boundary bin
+// (find_boundary) and, when that bin holds one value, the cut; otherwise its
+// elements are sorted and resolved exactly (resolve_sorted). ok = false when
+// the boundary bin holds more than kCap elements (the caller then takes the
+// general search). kept / zs are -1 when min-p cuts deeper.
 template <int NC>
 __device__ __forceinline__ Cut bf16_value_cut(const RegRow<1, NC>& r, float M, float c,
                                               const Filters& f, Lds& L, bool* ok) {
   constexpr int EPC = Fmt<1>::EPC;
   const int tid = threadIdx.x;
-  uint32_t* vals = reinterpret_cast<uint32_t*>(L.pref);   // free until the boundary sort
+  for (int i = tid; i < kVCopies * kVStride; i += kBlock) L.vcnt[i] = 0u;
   for (int i = tid; i < kBins; i += kBlock) {
     L.hcnt[i] = 0u;
     L.hmass[i] = 0ull;
   }
-  // bins b >= bneg lie wholly at or below -8, bins b <= bpos wholly above 8
-  const int bneg = (int)ceilf((M + 8.0f) * 16.0f);
-  const int bpos = (int)floorf((M - 8.0f) * 16.0f) - 1;
-  auto pure = [&](int b) { return b < kBins - 1 && (b >= bneg || b <= bpos); };
+  // bins b >= bneg lie wholly at or below -4, bins b <= bpos wholly above 4
+  const int bneg = (int)ceilf((M + 4.0f) * (float)kVRes);
+  const int bpos = (int)floorf((M - 4.0f) * (float)kVRes) - 1;
+  auto pure = [&](int b) { return (b < kVBins - 1) & ((b >= bneg) | (b <= bpos)); };
+  // the bin of v; -inf goes to the copy's spare word past the bins
+  auto vbin = [&](float x) {
+    const float t = (M - x) * (float)kVRes;
+    const int b = t < (float)(kVBins - 1) ? (int)t : kVBins - 1;
+    return x > kNegInf ? b : kVBins;
+  };
+  uint32_t* cnt = L.vcnt + (__lane_id() & (kVCopies - 1)) * kVStride;
   __syncthreads();
+  // counts, branch-free; the elements of bins without a single value are
+  // weighed too, behind one test per chunk row (they are rare in wide rows)
 #pragma unroll 1
   for (int j = 0; j < NC; ++j) {
     float v[EPC];
     r.elems(j, v);
+    int b[EPC];
+    bool imp = false;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
-      if (v[e] > kNegInf) {
-        const float t = (M - v[e]) * 16.0f;
-        const int b = t < (float)(kBins - 1) ? (int)t : kBins - 1;
-        atomicAdd(&L.hcnt[b], 1u);
-        if (pure(b))
-          vals[b] = __float_as_uint(v[e]);
-        else
-          atomicAdd(&L.hmass[b], to_fixed(weight(v[e], M, c)));
-      }
+      b[e] = vbin(v[e]);
+      atomicAdd(&cnt[b[e]], 1u);
+      imp = imp | ((b[e] < kVBins) & !pure(b[e]));
+    }
+    if (__any(imp)) {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e)
+        if ((b[e] < kVBins) & !pure(b[e]))
+          atomicAdd(&L.hmass[hslot(b[e])], to_fixed(weight(v[e], M, c)));
     }
   }
   __syncthreads();
   double zt = 0.0;
-  for (int b = tid; b < kBins; b += kBlock) {
-    const uint32_t n = L.hcnt[b];
+  for (int b = tid; b < kVBins; b += kBlock) {
+    uint32_t n = 0u;
+#pragma unroll
+    for (int q = 0; q < kVCopies; ++q) n += L.vcnt[q * kVStride + b];
+    L.hcnt[hslot(b)] = n;
     if (n && pure(b)) {
-      const double m = (double)n * (double)weight(__uint_as_float(vals[b]), M, c);
-      L.hmass[b] = (unsigned long long)(m * kFix + 0.5);
+      // the bin's one value: M - b/32 (exact) rounded down to the bf16 grid
+      const uint32_t x = __float_as_uint(M - (float)b * (1.0f / kVRes));
+      const uint32_t xv = (x & 0xFFFFu) == 0u ? x
+                          : ((x >> 31) ? (x & 0xFFFF0000u) + 0x10000u : (x & 0xFFFF0000u));
+      const double m = (double)n * (double)weight(__uint_as_float(xv), M, c);
+      L.hmass[hslot(b)] = (unsigned long long)(m * kFix + 0.5);
     }
-    zt += (double)L.hmass[b] * kInvFix;
+    zt += (double)L.hmass[hslot(b)] * kInvFix;
   }
   const double Z = block_sum<kBlock>(zt, L.bs);
   const double thr = f.p_on ? f.top_p * Z : 0.0;
@@ -168,16 +188,19 @@ __device__ __forceinline__ Cut bf16_value_cut(const RegRow<1, NC>& r, float M, f
     return cut;
   }
   if (pure(d)) {      // the boundary bin is one value group, kept whole
-    const float vd = __uint_as_float(vals[d]);
+    const uint32_t x = __float_as_uint(M - (float)d * (1.0f / kVRes));
+    const uint32_t xv = (x & 0xFFFFu) == 0u ? x
+                        : ((x >> 31) ? (x & 0xFFFF0000u) + 0x10000u : (x & 0xFFFF0000u));
+    const float vd = __uint_as_float(xv);
     cut.tau = fmaxf(vd, floor_m);
     const bool exact = !(floor_m > vd);
-    cut.kept = exact ? add_c + (int)L.hcnt[d] : -1;
-    cut.zs = exact ? add_m + (double)L.hmass[d] * kInvFix : -1.0;
+    cut.kept = exact ? add_c + (int)L.hcnt[hslot(d)] : -1;
+    cut.zs = exact ? add_m + (double)L.hmass[hslot(d)] * kInvFix : -1.0;
     __syncthreads();
     return cut;
   }
   // several values in the boundary bin: its elements, sorted, decide
-  const int nd = (int)L.hcnt[d];
+  const int nd = (int)L.hcnt[hslot(d)];
   __syncthreads();
   if (nd > kCap) {
     *ok = false;
@@ -192,9 +215,20 @@ __device__ __forceinline__ Cut bf16_value_cut(const RegRow<1, NC>& r, float M, f
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
       if (v[e] > kNegInf) {
-        const float t = (M - v[e]) * 16.0f;
-        const int b = t < (float)(kBins - 1) ? (int)t : kBins - 1;
-        if (b == d) L.key[atomicAdd(&L.si[6], 1)] = cand_key(v[e], r.base(j) + e);
+        const float t = (M - v[e]) * (float)kVRes;
+        const int b = t < (float)(kVBins - 1) ? (int)t : kVBins - 1;
+        const bool hit = b == d;
+        const unsigned long long m = __ballot(hit);
+        if (m) {   // one counter update per wavefront
+          const int first = __builtin_ctzll(m);
+          int at = 0;
+          if (__lane_id() == first) at = atomicAdd(&L.si[6], __popcll(m));
+          at = __builtin_amdgcn_readlane(at, first);
+          if (hit)
+            L.key[at + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
+                cand_key(v[e], r.base(j) + e);
+        }
       }
     }
   }
@@ -322,8 +356,11 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   int kept = -1, tok;
   double zs;
   if (f.k_on || f.p_on || f.m_on) {
-    // the cut and the draw; the registers are dead afterwards
-    const FastOut fo = fast_cut(r, V, M, st.tmin, st.zlo, c, f, u, L);
+    // the cut and the draw; the registers are dead afterwards. Without min-p
+    // the WIDE instance goes straight to its register search (no candidate
+    // bound can narrow a wide kept set).
+    FastOut fo{0, 0, -1, kPosInf, 0, 0.0};
+    if (!(WIDE && DT == 1) || f.m_on) fo = fast_cut(r, V, M, st.tmin, st.zlo, c, f, u, L);
     if (fo.ok) {
       tau = fo.tau;
       kept = fo.kept;

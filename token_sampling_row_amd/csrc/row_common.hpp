@@ -18,6 +18,10 @@ constexpr int kBins = 1024;   // bins of every histogram level
 constexpr int kLogRes = 16;   // log-probability bins per unit of log2(p / p_max)
 constexpr int kWalkBatch = 40;  // chunk rows per step of the inverse-CDF walk
 constexpr int kWaves = kBlock / kWave;
+constexpr int kVRes = 32;        // bf16 value histogram: bins per logit below the max
+constexpr int kVBins = 1024;     //   bins (32 logits)
+constexpr int kVCopies = 4;      //   count copies (lane & 3): fewer lanes per address
+constexpr int kVStride = kVBins + 1;   // copies one bank apart
 
 struct WaveStats {
   float m;       // wave max
@@ -27,8 +31,13 @@ struct WaveStats {
 };
 
 struct Lds {
-  unsigned long long key[kCap];     // candidate sort keys: fkey(v) << 32 | ~index
-  double pref[kCap + 1];            // exclusive prefix of candidate weights
+  union {
+    struct {
+      unsigned long long key[kCap];   // candidate sort keys: fkey(v) << 32 | ~index
+      double pref[kCap + 1];          // exclusive prefix of candidate weights
+    };
+    uint32_t vcnt[kVCopies * kVStride];   // bf16 value histogram: per-copy counts
+  };
   uint32_t hcnt[kBins];             // histogram counts
   unsigned long long hmass[kBins];  // histogram masses, fixed point 2^-40
   double jsum[kWaves * kWalkBatch]; // walk: per (wave, chunk row) sums
@@ -44,6 +53,13 @@ struct Lds {
   float sf[8];
   double sd[8];
 };
+
+// Histogram bin b lives at slot (b % 16) * 64 + b / 16: the 16 consecutive
+// bins one lane scans are 64 words apart, so the reads of a wavefront at one
+// step fall in distinct banks (bins b and b + 1 side by side would put a whole
+// wavefront on two banks).
+static_assert(kBins == 1024, "hslot assumes 1024 bins");
+__device__ __forceinline__ int hslot(int b) { return ((b & 15) << 6) | (b >> 4); }
 
 // One LDS instance per translation unit; every kernel of the unit uses it, as
 // do the non-inlined functions of the streaming path.
@@ -246,8 +262,8 @@ __device__ __forceinline__ int find_boundary(Lds& L, int cnt_above, double mass_
     unsigned long long lm = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      lc += (int)L.hcnt[lane * PER + i];
-      lm += L.hmass[lane * PER + i];
+      lc += (int)L.hcnt[hslot(lane * PER + i)];
+      lm += L.hmass[hslot(lane * PER + i)];
     }
     const int ic = wave_incl_scan(lc);
     const unsigned long long im = wave_incl_scan(lm);
@@ -257,12 +273,12 @@ __device__ __forceinline__ int find_boundary(Lds& L, int cnt_above, double mass_
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int b = lane * PER + i;
-      const int cb = (int)L.hcnt[b];
+      const int cb = (int)L.hcnt[hslot(b)];
       if (cb > 0 && first == kBins) first = b;
       if (f.k_on && dk == kBins && cb > 0 && cnt_above + run_c + cb >= f.k) dk = b;
       if (f.p_on && cb > 0 && mass_above + (double)run_m * kInvFix < thr) dp = b;
       run_c += cb;
-      run_m += L.hmass[b];
+      run_m += L.hmass[hslot(b)];
     }
     dk = wave_min(dk);
     dp = wave_max(dp);
@@ -277,8 +293,8 @@ __device__ __forceinline__ int find_boundary(Lds& L, int cnt_above, double mass_
     for (int i = 0; i < PER; ++i) {
       const int b = lane * PER + i;
       if (b < d) {
-        bc += (int)L.hcnt[b];
-        bm += L.hmass[b];
+        bc += (int)L.hcnt[hslot(b)];
+        bm += L.hmass[hslot(b)];
       }
     }
     bc = wave_sum(bc);

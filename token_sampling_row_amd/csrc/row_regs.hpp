@@ -44,8 +44,11 @@ struct RegRow {
   static_assert(NB <= 32, "chunk rows per thread");
   typename VecU<NA>::type ax, ay, az, aw;   // the chunks, one vector per dword
   typename VecU<NBS>::type bx, by, bz, bw;
-  typename VecF<NA>::type ca;               // chunk maxima; -inf past the end of the row
-  typename VecF<NBS>::type cb;
+  // Chunk maxima (-inf past the end of the row), kept in registers up to 32
+  // chunk rows; wider rows recompute them (their registers are needed more).
+  static constexpr bool kKeepCmax = NC <= 32;
+  typename VecF<kKeepCmax ? NA : 1>::type ca;
+  typename VecF<kKeepCmax ? NBS : 1>::type cb;
   float tmax;     // this thread's maximum
 
   int nwhole;     // whole 16-byte chunks in the row (chunk ids at or past it are not)
@@ -66,11 +69,11 @@ struct RegRow {
       bx[i] = t.x; by[i] = t.y; bz[i] = t.z; bw[i] = t.w;
     }
   }
-  __device__ __forceinline__ float cmax(int j) const {
-    return (NB == 0 || j < NA) ? ca[j] : cb[j - NA];
-  }
+  __device__ __forceinline__ float cmax(int j) const;
   __device__ __forceinline__ void put_cmax(int j, float m) {
-    if (NB == 0 || j < NA) ca[j] = m; else cb[j - NA] = m;
+    if constexpr (kKeepCmax) {
+      if (NB == 0 || j < NA) ca[j] = m; else cb[j - NA] = m;
+    }
   }
 
   // Whole chunks of a 16-byte aligned row are 128-bit buffer loads off one
@@ -155,6 +158,12 @@ __device__ __forceinline__ float chunk_max(uint4 t) {
     m = fmax3n(m, v[5], v[6]);
     return fmaxn(m, v[7]);
   }
+}
+
+template <int DT, int NC>
+__device__ __forceinline__ float RegRow<DT, NC>::cmax(int j) const {
+  if constexpr (kKeepCmax) return (NB == 0 || j < NA) ? ca[j] : cb[j - NA];
+  else return chunk_max<DT>(get(j));
 }
 
 struct RowStats {
@@ -495,12 +504,12 @@ __device__ __forceinline__ float topk_sketch(const RegRow<DT, NC>& r, float M, f
   }
   __syncthreads();
   if (by_thread) {
-    if (r.tmax >= lo) atomicAdd(&L.hcnt[sbin(r.tmax)], 1u);
+    if (r.tmax >= lo) atomicAdd(&L.hcnt[hslot(sbin(r.tmax))], 1u);
   } else {
 #pragma nounroll
     for (int j = 0; j < NC; ++j) {
       const float x = r.cmax(j);
-      if (x >= lo) atomicAdd(&L.hcnt[sbin(x)], 1u);
+      if (x >= lo) atomicAdd(&L.hcnt[hslot(sbin(x))], 1u);
     }
   }
   __syncthreads();
@@ -508,13 +517,13 @@ __device__ __forceinline__ float topk_sketch(const RegRow<DT, NC>& r, float M, f
     constexpr int PER = kBins / kWave;
     int lc = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) lc += (int)L.hcnt[tid * PER + i];
+    for (int i = 0; i < PER; ++i) lc += (int)L.hcnt[hslot(tid * PER + i)];
     const int ic = wave_incl_scan(lc);
     int run = ic - lc;
     int found = kBins;
     if (run < k && ic >= k) {
       for (int i = 0; i < PER; ++i) {
-        run += (int)L.hcnt[tid * PER + i];
+        run += (int)L.hcnt[hslot(tid * PER + i)];
         if (run >= k) {
           found = tid * PER + i;
           break;

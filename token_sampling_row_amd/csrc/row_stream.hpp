@@ -155,8 +155,8 @@ __device__ __forceinline__ Cut general_search(const Row& s, float M, float c, fl
       for (int e = 0; e < EPC; ++e)
         if (v[e] >= tau_m && v[e] > kNegInf) {
           const int b = lbin(v[e]);
-          atomicAdd(&L.hcnt[b], 1u);
-          atomicAdd(&L.hmass[b], to_fixed(weight(v[e], M, c)));
+          atomicAdd(&L.hcnt[hslot(b)], 1u);
+          atomicAdd(&L.hmass[hslot(b)], to_fixed(weight(v[e], M, c)));
         }
     }
   }
@@ -173,7 +173,7 @@ __device__ __forceinline__ Cut general_search(const Row& s, float M, float c, fl
   }
   int cnt_above = add_c;
   double mass_above = add_m;
-  int ncur = (int)L.hcnt[d];
+  int ncur = (int)L.hcnt[hslot(d)];
   __syncthreads();
   bool by_key = false;
   uint32_t klo = 0u, khi = 0xFFFFFFFFu;
@@ -222,15 +222,15 @@ __device__ __forceinline__ Cut general_search(const Row& s, float M, float c, fl
       for (int e = 0; e < EPC; ++e)
         if (in_region(v[e])) {
           const int b = (kBins - 1) - (int)((fkey(v[e]) - klo) >> shift);
-          atomicAdd(&L.hcnt[b], 1u);
-          atomicAdd(&L.hmass[b], to_fixed(weight(v[e], M, c)));
+          atomicAdd(&L.hcnt[hslot(b)], 1u);
+          atomicAdd(&L.hmass[hslot(b)], to_fixed(weight(v[e], M, c)));
         }
     }
     __syncthreads();
     const bool has_max = contains_max && (khi == fkey(M));
     const int d2 = find_boundary(L, cnt_above, mass_above, f, thr, has_max, &add_c, &add_m);
     const int dd = d2 == kBins ? kBins - 1 : d2;
-    ncur = (int)L.hcnt[dd];
+    ncur = (int)L.hcnt[hslot(dd)];
     cnt_above += add_c;
     mass_above += add_m;
     const uint32_t lo2 = klo + ((uint32_t)((kBins - 1) - dd) << shift);
