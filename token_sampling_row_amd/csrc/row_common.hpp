@@ -37,6 +37,7 @@ struct Lds {
       double pref[kCap + 1];          // exclusive prefix of candidate weights
     };
     uint32_t vcnt[kVCopies * kVStride];   // bf16 value histogram: per-copy counts
+    double jrow[kWalkBatch][kWaves * 4];  // walk: per (chunk row, 16-lane row) sums
   };
   uint32_t hcnt[kBins];             // histogram counts
   unsigned long long hmass[kBins];  // histogram masses, fixed point 2^-40

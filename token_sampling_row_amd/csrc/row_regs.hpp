@@ -281,6 +281,8 @@ template <int NC, int EPC, class CW>
 __device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* total_out) {
   static_assert(NC <= kWalkBatch, "walk scratch too small");
   const int tid = threadIdx.x, lane = __lane_id(), wid = tid / kWave;
+  // per chunk row, each 16-lane row's total (a butterfly inside the row, no
+  // cross-row step): 32 partial sums per chunk row, added in fixed order below
 #pragma nounroll
   for (int j = 0; j < NC; ++j) {
     float w[EPC];
@@ -288,16 +290,22 @@ __device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* tota
     double s = 0.0;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) s += (double)w[e];
-    if (__any(s > 0.0)) s = wave_sum(s);   // skip the shuffles for empty wave chunks
-    if (lane == 0) L.jsum[wid * kWalkBatch + j] = s;
+    if (__any(s > 0.0)) {   // skip the lane moves for empty wave chunks
+      s += dpp_perm_t<kDppXor1>(s);
+      s += dpp_perm_t<kDppXor2>(s);
+      s += dpp_perm_t<kDppHalfMirror>(s);
+      s += dpp_perm_t<kDppMirror>(s);
+    }
+    if ((lane & 15) == 0) L.jrow[j][wid * 4 + (lane >> 4)] = s;
   }
   __syncthreads();
   if (tid < kWave) {
-    // lane j < NC totals chunk row j over the waves; a scan over lanes gives
-    // the running total in id order
+    // lane j < NC totals chunk row j; a scan over lanes gives the running
+    // total in id order
     double sj = 0.0;
     if (lane < NC)
-      for (int w = 0; w < kWaves; ++w) sj += L.jsum[w * kWalkBatch + lane];
+#pragma unroll
+      for (int q = 0; q < kWaves * 4; ++q) sj += L.jrow[lane][q];
     const double incl = wave_incl_scan(sj);
     const double tot = readlane_t(incl, 63);
     const double target = u * tot;
