@@ -453,16 +453,39 @@ __device__ __forceinline__ void wave_compact(const RegRow<DT, NC>& r, float Lb, 
       const int j = pop_low(m);
       float v[EPC];
       r.elems(j, v);
-      // all compares first (one VALU op each); the append only for the
-      // elements some lane holds (usually one per chunk)
       bool hit[EPC];
-      unsigned long long b[EPC];
+      int nh = 0;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
         hit[e] = v[e] >= Lb;
-        b[e] = __ballot(hit[e]);
+        nh += hit[e] ? 1 : 0;
       }
       const int ib = r.base(j);
+      if (!__any(nh > 1)) {
+        // at most one hit per lane (the usual case): the hit by selects, its
+        // slot from the ballot of the lanes that hold one; no branch per element
+        float hv = v[0];
+        int he = 0;
+#pragma unroll
+        for (int e = 1; e < EPC; ++e) {
+          hv = hit[e] ? v[e] : hv;
+          he = hit[e] ? e : he;
+        }
+        const unsigned long long hm = __ballot(nh > 0);
+        const int slot = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                    (uint32_t)(hm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)hm, 0u));
+        if (nh > 0 && slot < kWaveCap) {
+          L.wc[wid].val[slot] = __float_as_uint(hv);
+          L.wc[wid].idx[slot] = (uint32_t)(ib + he);
+        }
+        base += __popcll(hm);
+        continue;
+      }
+      // several hits in some lane: per element, the append only for the
+      // elements some lane holds
+      unsigned long long b[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) b[e] = __ballot(hit[e]);
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
         if (b[e]) {
