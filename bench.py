@@ -172,12 +172,14 @@ def main():
     if args.write_traffic:
         from token_sampling_row_amd import workloads as wl
         w3 = wl.config(3, rows=1)
+        # the headline launches the common instance (third template argument false)
+        label = row_kernel_label(w3.dtype, w3.vocab).replace('bf16', '1').replace('f32', '0')
         print(json.dumps(write_traffic(*args.write_traffic, "batch256_128256_bf16",
-                                       f"tsr::{row_kernel_label(w3.dtype, w3.vocab).replace('bf16', '1').replace('f32', '0')}")))
+                                       f"tsr::{label[:-1]}, false>")))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the sampler shards by batch row with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the sampler shards by batch row with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch
