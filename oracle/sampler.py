@@ -34,7 +34,7 @@ __all__ = [
     "softmax", "Support", "support", "draw_from", "sample_row", "sample_batch",
     "greedy_batch", "accept_probability", "residual", "spec_verify_row",
     "spec_verify_batch", "acceptance_probability", "expected_accepted_prefix",
-    "values_from_stored",
+    "values_from_stored", "allowed_from_words", "mask_logits", "log_p_tilde",
 ]
 
 ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BADTOKEN = 0, 1, 2, 3
@@ -107,6 +107,33 @@ def row_status(l: np.ndarray) -> int:
     if l.size == 0 or np.isneginf(l).all():
         return ROW_EMPTY
     return ROW_OK
+
+
+def allowed_from_words(words, vocab: int) -> np.ndarray:
+    """Allowed set from a packed bitmask: token i is allowed iff bit i % 32 of
+    word i // 32 is set (the layout of sample_rows_masked)."""
+    w = np.asarray(words, dtype=np.uint32)
+    i = np.arange(vocab)
+    return ((w[i // 32] >> (i % 32).astype(np.uint32)) & 1).astype(bool)
+
+
+def mask_logits(l: np.ndarray, allowed) -> np.ndarray:
+    """Constrained decoding (P2 section 39.3): every token outside the allowed
+    set gets logit -inf before anything else, so every later step (temperature,
+    softmax, the filters, eq. 39.2) sees the distribution conditioned on the
+    allowed set. Reading: a disallowed entry is replaced whatever its value, a
+    NaN or +inf included (the page's mask_logits selects -inf without reading
+    the logit)."""
+    return np.where(np.asarray(allowed, dtype=bool), np.asarray(l, dtype=np.float64), -np.inf)
+
+
+def log_p_tilde(l: np.ndarray, keep: np.ndarray, token: int, temperature: float) -> float:
+    """log p~(token) under eq. 39.2: z_token - log sum_{j in S} e^{z_j},
+    z = (l - max l) / T, in float64 (shifted so no weight of S underflows
+    before the log)."""
+    l = np.asarray(l, dtype=np.float64)
+    z = (l - l.max()) / temperature
+    return float(z[token] - np.log(np.sum(np.exp(z[keep]))))
 
 
 def greedy_token(l: np.ndarray) -> int:
@@ -237,6 +264,7 @@ class RowResult:
     support: Support | None = None
     u: float = float("nan")
     margin_draw: float = float("inf")
+    logprob: float = float("nan")   # log p~(token); 0 for greedy; nan for bad rows
 
     @property
     def margin(self) -> float:
@@ -245,30 +273,39 @@ class RowResult:
         return min(self.margin_draw, self.support.margin_p, self.support.margin_m)
 
 
-def sample_row(l: np.ndarray, params, seed: int, row: int, step: int) -> RowResult:
+def sample_row(l: np.ndarray, params, seed: int, row: int, step: int,
+               allowed=None) -> RowResult:
     """One row of the sampler: status, greedy or chain + draw.
 
     The uniform is u = w0 * 2^-32 with w0 the first Philox4x32-10 word of
-    counter (row, 0 | SAMPLE << 16, step) under key = seed.
+    counter (row, 0 | SAMPLE << 16, step) under key = seed. ``allowed`` (a
+    bool [V], or None for every token) masks the row first (P2 section 39.3);
+    an allowed set without a finite logit is the empty state. The result
+    carries log p~ of the drawn token (0 under greedy decoding, where p~ is a
+    point mass).
     """
     prm = Params.of(params)
     check_params(prm)
     l = np.asarray(l, dtype=np.float64)
+    if allowed is not None:
+        l = mask_logits(l, allowed)
     st = row_status(l)
     if st != ROW_OK:
         return RowResult(-1, st)
     if prm.temperature == 0.0:
-        return RowResult(greedy_token(l), ROW_OK)
+        return RowResult(greedy_token(l), ROW_OK, logprob=0.0)
     s = support(l, prm)
     u = float(uniforms_from_words(draw_words(seed, [row], 0, step, DOMAIN_SAMPLE)[:, 0])[0])
     tok, margin = draw_from(s.p, s.keep, u)
-    return RowResult(tok, ROW_OK, s, u, margin)
+    return RowResult(tok, ROW_OK, s, u, margin, log_p_tilde(l, s.keep, tok, prm.temperature))
 
 
-def sample_batch(values: np.ndarray, params, seed: int, step: int, rows=None):
-    """sample_row over a [B, V] float64 batch; ``rows`` picks a subset of rows."""
+def sample_batch(values: np.ndarray, params, seed: int, step: int, rows=None, allowed=None):
+    """sample_row over a [B, V] float64 batch; ``rows`` picks a subset of rows;
+    ``allowed`` is a bool [B, V] mask or None."""
     rows = range(values.shape[0]) if rows is None else rows
-    return [sample_row(values[b], params, seed, b, step) for b in rows]
+    return [sample_row(values[b], params, seed, b, step,
+                       None if allowed is None else allowed[b]) for b in rows]
 
 
 def greedy_batch(values: np.ndarray):
