@@ -293,6 +293,27 @@ def run_extra(torch, tsr, wl, steps, warmup):
             res[f"verify64_k4_32000_f32_{name}"] = r
         del tgs, dfs
 
+        # constrained decoding on the headline batch: allowed-token bitmask
+        # (V/8 bytes per row more) and log p~ of each draw
+        w = wl.config(3)
+        bufs = device_batch(torch, w, ROTATE)
+        out = torch.empty(w.rows, dtype=torch.int32, device="cuda:0")
+        lp = torch.empty(w.rows, dtype=torch.float32, device="cuda:0")
+        ms = time_calls(torch, lambda i: s.sample_rows_masked(bufs[i % ROTATE], None, w.runs[0], i,
+                                                              out=out, logprob=lp),
+                        steps, warmup)
+        res["batch256_128256_bf16_chain_logprob"] = _rates(w.rows, w.rows * w.vocab * 2, ms)
+        for kind in ("p=0.5", "few=40"):
+            words = torch.from_numpy(wl.allowed_words(31, w.rows, w.vocab, kind).view("int32"))
+            words = words.to("cuda:0")
+            nbytes = w.rows * w.vocab * 2 + words.numel() * 4
+            ms = time_calls(torch, lambda i: s.sample_rows_masked(bufs[i % ROTATE], words,
+                                                                  w.runs[0], i, out=out,
+                                                                  logprob=lp),
+                            steps, warmup)
+            res[f"batch256_128256_bf16_chain_mask_{kind}"] = _rates(w.rows, nbytes, ms)
+        del bufs
+
         w = wl.config(5)
         bufs = device_batch(torch, w, 2)          # 2 x 311 MB already exceeds the 256 MB cache
         out = torch.empty(w.rows, dtype=torch.int32, device="cuda:0")

@@ -142,6 +142,30 @@ int sample_rows(tsr_handle h, const void* logits, int dtype, int rows, int vocab
                 int64_t row_stride, const tsr_params* params, uint64_t step,
                 int32_t* out_tokens, const tsr_diag* diag, void* hip_stream);
 
+/* The sampler restricted to an allowed-token set (constrained decoding)
+ * [P2 39.3: the disallowed logits become -inf before the softmax, every step;
+ * an empty allowed set is an invalid state], with the log-probability of each
+ * drawn token [P1 "Picking the next token": generation can return it].
+ *  allowed [rows][allowed_stride] uint32 words (nullable: every token is
+ *      allowed, and the call equals sample_rows): token i of row r is allowed
+ *      iff bit (i % 32) of allowed[r * allowed_stride + i / 32] is set; bits
+ *      of ids >= vocab are ignored. allowed_stride >= ceil(vocab / 32); the
+ *      pointer is 4-byte aligned. Disallowed logits are replaced by -inf
+ *      before any other step, so a NaN or +inf there does not make the row
+ *      TSR_ROW_NONFINITE, and a row with no allowed finite logit is
+ *      TSR_ROW_EMPTY (token -1).
+ *  out_logprob [rows] float32 (nullable): log p~(token) of eq. 39.2 over the
+ *      masked and filtered distribution, i.e. (z_tok - M) / T minus the log
+ *      of sum over S of exp((z - M) / T); 0 for greedy rows (temperature 0)
+ *      and NaN for rows whose status is not TSR_ROW_OK.
+ * Every other argument, and the draw itself (the same uniform of counter
+ * (r, 0, step)), is as in sample_rows: the call computes what sample_rows
+ * computes for logits whose disallowed entries are -inf. */
+int sample_rows_masked(tsr_handle h, const void* logits, int dtype, int rows, int vocab,
+                       int64_t row_stride, const uint32_t* allowed, int64_t allowed_stride,
+                       const tsr_params* params, uint64_t step, int32_t* out_tokens,
+                       float* out_logprob, const tsr_diag* diag, void* hip_stream);
+
 /* The speculative verify step [P3 "The Algorithm"; P1, P4 "Speculative
  * decoding"; P2 39.4] for `rows` sequences with K drafted tokens each.
  *  target_logits [rows][K+1][vocab]: the target's logits at the K draft

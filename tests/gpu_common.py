@@ -10,6 +10,11 @@ Parity rule (tolerances written here, used by every GPU test):
     BAND, which can move the interval).
   * kept probabilities p~ (eq. 39.2): relative error <= PROB_RTOL where the
     oracle's p~ is a normal float32; kept mass: relative error <= PROB_RTOL.
+  * log p~ of the drawn token (where token and kept set agree): absolute
+    error <= LOGP_TOL * max(1, |log p~|). The kernel forms it in float64 from
+    float32 weights exp2((v - M) * log2(e) / T), each within a few float32
+    ulps (~3e-7 relative, so ~3e-7 absolute in the log), and rounds the result
+    to float32 (2^-24 relative); 1e-5 covers both with room to spare.
 BAND = 1e-6 and PROB_RTOL = 1e-5 are the tolerances the work is held to.
 """
 from __future__ import annotations
@@ -21,6 +26,7 @@ import pytest
 
 BAND = 1e-6
 PROB_RTOL = 1e-5
+LOGP_TOL = 1e-5
 F32_NORMAL_MIN = 1.1754943508222875e-38
 
 torch = pytest.importorskip("torch")
@@ -60,6 +66,59 @@ def run_sample(sampler, x, params, step, diag=False, probs=False):
             if t is not None:
                 res[k] = t.cpu().numpy()
     return res
+
+
+def run_masked(sampler, x, words, params, step, diag=True, probs=False):
+    """sample_rows_masked through the C ABI; ``words`` is a uint32 [rows, W]
+    numpy array or None. Returns token, logprob and the diagnostics."""
+    rows, V = x.shape
+    allowed = None
+    if words is not None:
+        allowed = torch.from_numpy(np.ascontiguousarray(words).view(np.int32)).to(x.device)
+    d = None
+    if diag:
+        d = dict(status=torch.full((rows,), -7, dtype=torch.int32, device=x.device),
+                 kept_count=torch.full((rows,), -7, dtype=torch.int32, device=x.device),
+                 threshold=torch.full((rows,), float("nan"), dtype=torch.float32, device=x.device),
+                 kept_mass=torch.full((rows,), float("nan"), dtype=torch.float64, device=x.device),
+                 probs=(torch.full((rows, V), float("nan"), dtype=torch.float32, device=x.device)
+                        if probs else None))
+    lp = torch.full((rows,), 12345.0, dtype=torch.float32, device=x.device)
+    out = sampler.sample_rows_masked(x, allowed, params, step, logprob=lp, diag=d)
+    torch.cuda.synchronize()
+    res = {"token": out.cpu().numpy(), "logprob": lp.cpu().numpy()}
+    if d:
+        for k, t in d.items():
+            if t is not None:
+                res[k] = t.cpu().numpy()
+    return res
+
+
+def compare_logprob(gpu: dict, refs: list, rows) -> int:
+    """log p~ of the drawn tokens: NaN on bad rows, 0 on greedy rows, else the
+    oracle's within LOGP_TOL wherever token and kept set agree (elsewhere the
+    band rule of compare() already excused the row). Returns rows checked."""
+    n = 0
+    for i, b in enumerate(rows):
+        r = refs[i]
+        g = float(gpu["logprob"][b])
+        if r.status != 0:
+            assert np.isnan(g), (b, g)
+            continue
+        if r.support is None:          # greedy
+            assert g == 0.0, (b, g)
+            n += 1
+            continue
+        if gpu["token"][b] != r.token:
+            continue
+        s = r.support
+        if "kept_count" in gpu and (gpu["kept_count"][b] != s.kept_count or
+                                    np.float32(gpu["threshold"][b]) != np.float32(s.threshold)):
+            continue
+        assert g <= 0.0 or abs(g) <= LOGP_TOL, (b, g)
+        assert abs(g - r.logprob) <= LOGP_TOL * max(1.0, abs(r.logprob)), (b, g, r.logprob)
+        n += 1
+    return n
 
 
 @dataclass

@@ -22,7 +22,7 @@ F32, BF16 = 0, 1
 JOINT, SEQUENTIAL = 0, 1
 ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BADTOKEN = 0, 1, 2, 3
 EXPORTED_SYMBOLS = ("sampler_init", "sampler_destroy", "greedy_argmax", "sample_rows",
-                    "spec_verify", "sampler_philox", "sampler_strerror")
+                    "sample_rows_masked", "spec_verify", "sampler_philox", "sampler_strerror")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -71,6 +71,9 @@ def load_library():
     lib.greedy_argmax.argtypes = [vp, vp, i32, i32, i32, i64, vp, vp, vp]
     lib.sample_rows.argtypes = [vp, vp, i32, i32, i32, i64, ctypes.POINTER(_Params), u64, vp,
                                 ctypes.POINTER(_Diag), vp]
+    lib.sample_rows_masked.argtypes = [vp, vp, i32, i32, i32, i64, vp, i64,
+                                       ctypes.POINTER(_Params), u64, vp, vp,
+                                       ctypes.POINTER(_Diag), vp]
     lib.spec_verify.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, ctypes.POINTER(_Params),
                                 u64, vp, vp, vp, vp]
     lib.sampler_philox.argtypes = [vp, vp, i32, vp, vp]
@@ -188,6 +191,34 @@ class Sampler:
                                           ctypes.c_uint64(int(step)), _ptr(out),
                                           ctypes.byref(d) if d is not None else None,
                                           _stream_ptr(stream)), "sample_rows")
+        return out
+
+    def sample_rows_masked(self, logits, allowed, params, step: int, out=None, logprob=None,
+                           diag=None, stream=None):
+        """sample_rows over the allowed tokens only. ``allowed``: [rows, W] int32
+        device tensor of bit words (token i = bit i % 32 of word i // 32,
+        W >= ceil(vocab / 32)), or None (every token allowed). ``logprob``: a
+        preallocated [rows] float32 tensor for log p~ of each drawn token, or
+        None. Returns the tokens."""
+        import torch
+        rows, vocab = logits.shape
+        assert logits.stride(1) == 1, "rows must be contiguous"
+        if allowed is not None:
+            assert allowed.dtype == torch.int32 and allowed.stride(1) == 1
+            astride = allowed.stride(0)
+        else:
+            astride = 0
+        out = torch.empty(rows, dtype=torch.int32, device=logits.device) if out is None else out
+        cp = Params.of(params)._c()
+        d = None
+        if diag is not None:
+            d = _Diag(*(ctypes.c_void_p(diag[k].data_ptr()) if diag.get(k) is not None else None
+                        for k in ("status", "kept_count", "threshold", "kept_mass", "probs")))
+        _check(load_library().sample_rows_masked(
+            self._h, _ptr(logits), _dtype_code(logits), rows, vocab, logits.stride(0),
+            _ptr(allowed), astride, ctypes.byref(cp), ctypes.c_uint64(int(step)), _ptr(out),
+            _ptr(logprob), ctypes.byref(d) if d is not None else None, _stream_ptr(stream)),
+            "sample_rows_masked")
         return out
 
     def spec_verify(self, target, draft, draft_tokens, params, step: int, out_tokens=None,

@@ -168,13 +168,18 @@ int greedy_argmax(tsr_handle h, const void* logits, int dtype, int rows, int voc
   });
 }
 
-int sample_rows(tsr_handle h, const void* logits, int dtype, int rows, int vocab,
-                int64_t row_stride, const tsr_params* params, uint64_t step,
-                int32_t* out_tokens, const tsr_diag* diag, void* hip_stream) {
+int sample_rows_masked(tsr_handle h, const void* logits, int dtype, int rows, int vocab,
+                       int64_t row_stride, const uint32_t* allowed, int64_t allowed_stride,
+                       const tsr_params* params, uint64_t step, int32_t* out_tokens,
+                       float* out_logprob, const tsr_diag* diag, void* hip_stream) {
   if (!h || !logits || !out_tokens) return TSR_EINVAL;
   if (dtype != TSR_F32 && dtype != TSR_BF16) return TSR_EINVAL;
   if (rows < 0 || rows > h->max_rows || vocab < 1 || vocab > h->max_vocab) return TSR_EINVAL;
   if (row_stride < vocab || !elem_aligned(logits, dtype)) return TSR_EINVAL;
+  if (allowed) {
+    const int64_t words = ((int64_t)vocab + 31) / 32;
+    if (allowed_stride < words || ((uintptr_t)allowed % 4) != 0) return TSR_EINVAL;
+  }
   const int prc = check_params(params);
   if (prc != TSR_OK) return prc;
   if (vocab > tsr::max_vocab_sample(dtype)) return TSR_EUNSUPPORTED;
@@ -187,7 +192,13 @@ int sample_rows(tsr_handle h, const void* logits, int dtype, int rows, int vocab
     dg.kept_mass = diag->kept_mass;
     dg.probs = diag->probs;
   }
-  const tsr::KParams kp = make_kparams(h, params, vocab, step, dg.kept_mass != nullptr);
+  dg.logprob = out_logprob;
+  tsr::KParams kp = make_kparams(h, params, vocab, step, dg.kept_mass != nullptr);
+  if (allowed) {
+    kp.allowed = allowed;
+    kp.allowed_stride = (long long)allowed_stride;
+    kp.flags |= tsr::F_MASK;
+  }
   const long long sb = (long long)row_stride * esize(dtype);
   const int aligned = ((uintptr_t)logits % 16 == 0) && (sb % 16 == 0);
   const int ragged = !aligned || (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;
@@ -196,6 +207,13 @@ int sample_rows(tsr_handle h, const void* logits, int dtype, int rows, int vocab
                                             out_tokens, dg, (hipStream_t)hip_stream);
     return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
   });
+}
+
+int sample_rows(tsr_handle h, const void* logits, int dtype, int rows, int vocab,
+                int64_t row_stride, const tsr_params* params, uint64_t step,
+                int32_t* out_tokens, const tsr_diag* diag, void* hip_stream) {
+  return sample_rows_masked(h, logits, dtype, rows, vocab, row_stride, nullptr, 0, params, step,
+                            out_tokens, nullptr, diag, hip_stream);
 }
 
 int spec_verify(tsr_handle h, const void* target_logits, const void* draft_logits, int dtype,

@@ -27,11 +27,15 @@ constexpr int kVerifyNcs[] = {1, 2, 4, 8, 16};
 // Each kernel instance is compiled in a translation unit of its own (the
 // build generates them), so the units that launch them only declare them.
 #define TSR_DECLARE_ROW(N)                                                                   \
-  extern template __global__ void sample_kernel<0, N, false>(                                \
+  extern template __global__ void sample_kernel<0, N, false, false>(                         \
       const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
-  extern template __global__ void sample_kernel<1, N, false>(                                \
+  extern template __global__ void sample_kernel<1, N, false, false>(                         \
       const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
-  extern template __global__ void sample_kernel<1, N, true>(                                 \
+  extern template __global__ void sample_kernel<1, N, true, false>(                          \
+      const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
+  extern template __global__ void sample_kernel<0, N, false, true>(                          \
+      const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
+  extern template __global__ void sample_kernel<1, N, true, true>(                           \
       const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
   extern template __global__ void greedy_kernel<0, N>(const unsigned char*, long long, int,  \
                                                       int, int, int32_t*, int32_t*);          \

@@ -12,15 +12,19 @@ hipError_t launch_sample_dt1(const unsigned char* p, int rows, int V, long long 
                        stride_bytes, V, aligned, kp, out, dg);
     return hipGetLastError();
   }
+  const bool mask = (kp.flags & F_MASK) != 0;
   const bool wide = wide_filters(kp, kBlock);
-#define TSR_CASE(N)                                                                      \
-  case N:                                                                                \
-    if (wide)                                                                            \
-      hipLaunchKernelGGL((sample_kernel<1, N, true>), dim3(rows), dim3(kBlock), 0, s, p, \
-                         stride_bytes, V, aligned, ragged, kp, out, dg);                 \
-    else                                                                                 \
-      hipLaunchKernelGGL((sample_kernel<1, N, false>), dim3(rows), dim3(kBlock), 0, s, p,\
-                         stride_bytes, V, aligned, ragged, kp, out, dg);                 \
+#define TSR_CASE(N)                                                                            \
+  case N:                                                                                      \
+    if (mask)                                                                                  \
+      hipLaunchKernelGGL((sample_kernel<1, N, true, true>), dim3(rows), dim3(kBlock), 0, s, p, \
+                         stride_bytes, V, aligned, ragged, kp, out, dg);                       \
+    else if (wide)                                                                             \
+      hipLaunchKernelGGL((sample_kernel<1, N, true, false>), dim3(rows), dim3(kBlock), 0, s,  \
+                         p, stride_bytes, V, aligned, ragged, kp, out, dg);                    \
+    else                                                                                       \
+      hipLaunchKernelGGL((sample_kernel<1, N, false, false>), dim3(rows), dim3(kBlock), 0, s, \
+                         p, stride_bytes, V, aligned, ragged, kp, out, dg);                    \
     break;
   switch (nc) {
     TSR_ROW_NCS(TSR_CASE)

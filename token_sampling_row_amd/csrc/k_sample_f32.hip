@@ -12,10 +12,15 @@ hipError_t launch_sample_dt0(const unsigned char* p, int rows, int V, long long 
                        stride_bytes, V, aligned, kp, out, dg);
     return hipGetLastError();
   }
-#define TSR_CASE(N)                                                                      \
-  case N:                                                                                \
-    hipLaunchKernelGGL((sample_kernel<0, N, false>), dim3(rows), dim3(kBlock), 0, s, p,        \
-                       stride_bytes, V, aligned, ragged, kp, out, dg);                   \
+  const bool mask = (kp.flags & F_MASK) != 0;
+#define TSR_CASE(N)                                                                             \
+  case N:                                                                                       \
+    if (mask)                                                                                   \
+      hipLaunchKernelGGL((sample_kernel<0, N, false, true>), dim3(rows), dim3(kBlock), 0, s, p, \
+                         stride_bytes, V, aligned, ragged, kp, out, dg);                        \
+    else                                                                                        \
+      hipLaunchKernelGGL((sample_kernel<0, N, false, false>), dim3(rows), dim3(kBlock), 0, s,  \
+                         p, stride_bytes, V, aligned, ragged, kp, out, dg);                     \
     break;
   switch (nc) {
     TSR_ROW_NCS(TSR_CASE)

@@ -17,6 +17,8 @@ struct KParams {
   int flags;
   uint32_t key0, key1; // Philox key = seed (low word, high word)
   uint32_t step_lo, step_hi;
+  const uint32_t* allowed;   // allowed-token bitmask rows (F_MASK), token i = bit i % 32 of word i / 32
+  long long allowed_stride;  // words between mask rows
 };
 enum : int {
   F_GREEDY = 1,   // temperature 0
@@ -25,6 +27,7 @@ enum : int {
   F_M = 8,        // min-p active
   F_SEQ = 16,     // SEQUENTIAL filter mode
   F_Z = 32,       // the full weight sum is wanted (kept-mass diagnostic)
+  F_MASK = 64,    // an allowed-token bitmask applies
 };
 // Filters whose kept set may be far larger than any candidate buffer: no
 // top-k, or one too large for the per-thread-maxima sketch (the sampling
@@ -41,6 +44,7 @@ struct DiagPtrs {
   float* threshold;
   double* kept_mass;
   float* probs;
+  float* logprob;   // log p~ of the drawn token
 };
 
 // Per-handle workspace of the verify step: per (sequence, position) results

@@ -38,16 +38,21 @@ __device__ __forceinline__ double draw_uniform(const KParams& kp, uint32_t row, 
   return (double)(word == 0 ? w.x : w.y) * 0x1p-32;
 }
 
+// wtok / zs: weight of the drawn token and of S (log p~ of the draw is their
+// log ratio, eq. 39.2); greedy passes 1, 1 (a point mass) and bad rows NaN.
 __device__ __forceinline__ void write_row(int row, int tok, int status, int kept, float tmin,
-                                          double kmass, int32_t* out, const DiagPtrs& dg) {
+                                          double kmass, double wtok, double zs, int32_t* out,
+                                          const DiagPtrs& dg) {
   if (threadIdx.x == 0) {
     out[row] = tok;
     if (dg.status) dg.status[row] = status;
     if (dg.kept_count) dg.kept_count[row] = kept;
     if (dg.threshold) dg.threshold[row] = tmin;
     if (dg.kept_mass) dg.kept_mass[row] = kmass;
+    if (dg.logprob) dg.logprob[row] = (float)(log(wtok) - log(zs));
   }
 }
+constexpr double kNaN = __builtin_nan("");
 
 __device__ __forceinline__ void zero_probs(const DiagPtrs& dg, int row, int V) {
   if (dg.probs) {
@@ -62,13 +67,13 @@ __device__ __noinline__ void stream_finish(const StreamRow<DT> s, int row, float
                                            const KParams kp, const Filters f, double u,
                                            int32_t* out, const DiagPtrs dg) {
   const Cut cut = general_stream(s, M, Z, kp.c, kp.cR, f);
-  double zs;
-  const int tok = walk_stream(s, cut.tau, M, kp.c, u, &zs);
+  double zs, wt;
+  const int tok = walk_stream(s, cut.tau, M, kp.c, u, &zs, &wt);
   int kept = cut.kept;
   float tmin = cut.tau;
   if (dg.kept_count || dg.threshold) stream_kept_stats(s, cut.tau, &kept, &tmin);
   if (dg.kept_mass && !(Z > 0.0)) Z = stream_weight_sum(s, -kFltMax, M, kp.c);
-  write_row(row, tok, 0, kept, tmin, Z > 0.0 ? zs / Z : 0.0, out, dg);
+  write_row(row, tok, 0, kept, tmin, Z > 0.0 ? zs / Z : 0.0, wt, zs, out, dg);
   if (dg.probs) stream_probs(s, cut.tau, M, kp.c, zs, dg.probs + (long long)row * s.V);
 }
 
@@ -77,12 +82,12 @@ __device__ __noinline__ void stream_finish(const StreamRow<DT> s, int row, float
 // live in the caller after it, so the hot path keeps no values for it.
 template <int DT>
 __device__ __noinline__ void diag_finish(const StreamRow<DT> s, int row, int tok, int kept,
-                                         float tau, float M, float c, double zs, int32_t* out,
-                                         const DiagPtrs dg) {
+                                         float tau, float M, float c, double zs, double wt,
+                                         int32_t* out, const DiagPtrs dg) {
   float tmin = tau;
   if (dg.kept_count || dg.threshold) stream_kept_stats(s, tau, &kept, &tmin);
   const double Z = dg.kept_mass ? stream_weight_sum(s, -kFltMax, M, c) : 0.0;
-  write_row(row, tok, 0, kept, tmin, Z > 0.0 ? zs / Z : 0.0, out, dg);
+  write_row(row, tok, 0, kept, tmin, Z > 0.0 ? zs / Z : 0.0, wt, zs, out, dg);
   if (dg.probs) stream_probs(s, tau, M, c, zs, dg.probs + (long long)row * s.V);
 }
 
@@ -322,11 +327,21 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel_stream(const unsigned ch
 
 // ---------------------------------------------------------------- sample_rows
 
+// The streaming view of row `row` (for the streaming finish and the
+// diagnostics), with its allowed-token mask when MASK.
+template <int DT, bool MASK>
+__device__ __forceinline__ StreamRow<DT> row_stream_view(const unsigned char* p, int V,
+                                                         const KParams& kp, int row) {
+  return StreamRow<DT>(p, V, true, MASK ? kp.allowed + (long long)row * kp.allowed_stride : nullptr);
+}
+
 // WIDE (bf16): rows whose kept set the candidate bound cannot narrow are
 // finished over the registers (reg_general, then the walk) instead of by the
 // streaming path. A separate instance, chosen on the host for filters without
 // a small top-k, so the common instance keeps its registers and code size.
-template <int DT, int NC, bool WIDE>
+// MASK: an allowed-token bitmask applies (constrained decoding), staged in LDS
+// and applied in pass A; its instances are WIDE for bf16.
+template <int DT, int NC, bool WIDE, bool MASK>
 __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* logits,
                                                         long long stride_bytes, int V,
                                                         int aligned, int ragged, KParams kp,
@@ -336,35 +351,39 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   const int row = blockIdx.x;
   const unsigned char* p = logits + (long long)row * stride_bytes;
   RegRow<DT, NC> r;
+  if constexpr (MASK) stage_mask(kp.allowed + (long long)row * kp.allowed_stride, V, L);
   r.load(p, V, ragged != 0);
+  if constexpr (MASK) mask_ready<NC>();
   const bool greedy = (kp.flags & F_GREEDY) != 0;
   const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);   // while the loads fly
-  const RowStats st = reg_stats(r, !greedy && joint_top_p(kp), kp.c, L);
+  const RowStats st = reg_stats<MASK>(r, !greedy && joint_top_p(kp), kp.c, L);
   if (st.status != 0) {
-    write_row(row, -1, st.status, 0, kNegInf, 0.0, out, dg);
+    write_row(row, -1, st.status, 0, kNegInf, 0.0, kNaN, kNaN, out, dg);
     zero_probs(dg, row, V);
     return;
   }
   if (greedy) {
     const int tok = reg_argmax(r, st.M, L);
-    write_row(row, tok, 0, 0, kNegInf, 0.0, out, dg);
+    write_row(row, tok, 0, 0, kNegInf, 0.0, 1.0, 1.0, out, dg);
     return;
   }
   const float M = st.M, c = kp.c;
   const Filters f = make_filters(kp, M);
   float tau = -kFltMax;     // no filter: every finite logit
   int kept = -1, tok;
-  double zs;
+  double zs, wt;
   if (f.k_on || f.p_on || f.m_on) {
     // the cut and the draw; the registers are dead afterwards. Without min-p
-    // the WIDE instance goes straight to its register search (no candidate
-    // bound can narrow a wide kept set).
-    FastOut fo{0, 0, -1, kPosInf, 0, 0.0};
-    if (!(WIDE && DT == 1) || f.m_on) fo = fast_cut(r, V, M, st.tmin, st.zlo, c, f, u, L);
+    // or a small top-k the WIDE instance goes straight to its register search
+    // (no candidate bound can narrow a wide kept set).
+    const bool narrow = f.m_on || (MASK && f.k_on && f.k <= kBlock / 4);
+    FastOut fo{0, 0, -1, kPosInf, 0, 0.0, 0.0};
+    if (!(WIDE && DT == 1) || narrow) fo = fast_cut(r, V, M, st.tmin, st.zlo, c, f, u, L);
     if (fo.ok) {
       tau = fo.tau;
       kept = fo.kept;
       zs = fo.zs;
+      wt = fo.wtok;
       tok = fo.token;
     } else if constexpr (DT == 1 && WIDE) {
       // too many candidates for the LDS buffer: the search over the registers
@@ -372,20 +391,21 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
       const Cut cut = reg_general(r, M, c, kp.cR, f, L);
       tau = cut.tau;
       kept = cut.kept;
-      tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs);
+      tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs, &wt);
     } else {
       // the streaming path finishes this row
-      stream_finish(StreamRow<DT>(p, V, true), row, M, -1.0, kp, f, u, out, dg);
+      stream_finish(row_stream_view<DT, MASK>(p, V, kp, row), row, M, -1.0, kp, f, u, out, dg);
       return;
     }
   } else {
-    tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs);
+    tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs, &wt);
   }
   if (dg.kept_count || dg.threshold || dg.kept_mass || dg.probs) {
-    diag_finish(StreamRow<DT>(p, V, true), row, tok, kept, tau, M, c, zs, out, dg);
+    diag_finish(row_stream_view<DT, MASK>(p, V, kp, row), row, tok, kept, tau, M, c, zs, wt, out,
+                dg);
     return;
   }
-  write_row(row, tok, 0, kept, tau, 0.0, out, dg);
+  write_row(row, tok, 0, kept, tau, 0.0, wt, zs, out, dg);
 }
 
 // Rows wider than the register file: every pass streams the row.
@@ -396,16 +416,18 @@ __global__ __launch_bounds__(kBlock) void sample_kernel_stream(const unsigned ch
                                                                int32_t* out, DiagPtrs dg) {
   const int row = blockIdx.x;
   const unsigned char* p = logits + (long long)row * stride_bytes;
-  const StreamRow<DT> s(p, V, aligned != 0);
+  const StreamRow<DT> s(p, V, aligned != 0,
+                        (kp.flags & F_MASK) ? kp.allowed + (long long)row * kp.allowed_stride
+                                            : nullptr);
   const bool greedy = (kp.flags & F_GREEDY) != 0;
   const StreamStats st = stream_stats(s, !greedy && wants_z(kp), kp.c);
   if (st.status != 0) {
-    write_row(row, -1, st.status, 0, kNegInf, 0.0, out, dg);
+    write_row(row, -1, st.status, 0, kNegInf, 0.0, kNaN, kNaN, out, dg);
     zero_probs(dg, row, V);
     return;
   }
   if (greedy) {
-    write_row(row, stream_argmax(s, st.M), 0, 0, kNegInf, 0.0, out, dg);
+    write_row(row, stream_argmax(s, st.M), 0, 0, kNegInf, 0.0, 1.0, 1.0, out, dg);
     return;
   }
   const Filters f = make_filters(kp, st.M);

@@ -18,6 +18,7 @@ constexpr int kBins = 1024;   // bins of every histogram level
 constexpr int kLogRes = 16;   // log-probability bins per unit of log2(p / p_max)
 constexpr int kWalkBatch = 40;  // chunk rows per step of the inverse-CDF walk
 constexpr int kWaves = kBlock / kWave;
+constexpr int kMaskWords = 8192;   // allowed-token words staged in LDS (262144 tokens)
 constexpr int kVRes = 32;        // bf16 value histogram: bins per logit below the max
 constexpr int kVBins = 1024;     //   bins (32 logits)
 constexpr int kVCopies = 4;      //   count copies (lane & 3): fewer lanes per address
@@ -37,6 +38,7 @@ struct Lds {
       double pref[kCap + 1];          // exclusive prefix of candidate weights
     };
     uint32_t vcnt[kVCopies * kVStride];   // bf16 value histogram: per-copy counts
+    uint32_t vmask[kMaskWords];           // the row's allowed-token bitmask (pass A)
     double jrow[kWalkBatch][kWaves * 4];  // walk: per (chunk row, 16-lane row) sums
   };
   uint32_t hcnt[kBins];             // histogram counts
@@ -61,6 +63,35 @@ struct Lds {
 // wavefront on two banks).
 static_assert(kBins == 1024, "hslot assumes 1024 bins");
 __device__ __forceinline__ int hslot(int b) { return ((b & 15) << 6) | (b >> 4); }
+
+// Allowed-token mask of one 16-byte chunk c: its EPC bits (token i is bit
+// i % 32 of word i / 32), from a word array (global or LDS).
+template <int DT>
+__device__ __forceinline__ uint32_t chunk_mask_bits(const uint32_t* words, long long c) {
+  if constexpr (DT == 0) return (words[c >> 3] >> ((uint32_t)(c & 7) * 4u)) & 0xFu;
+  else return (words[c >> 2] >> ((uint32_t)(c & 3) * 8u)) & 0xFFu;
+}
+// A chunk with its disallowed elements replaced by -inf (constrained decoding:
+// the mask applies before any other step).
+template <int DT>
+__device__ __forceinline__ uint4 apply_mask(uint4 t, uint32_t bits) {
+  uint32_t x[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t keep;
+    uint32_t ninf;
+    if constexpr (DT == 0) {
+      keep = 0u - ((bits >> i) & 1u);
+      ninf = 0xFF800000u;
+    } else {
+      keep = ((0u - ((bits >> (2 * i)) & 1u)) & 0x0000FFFFu) |
+             ((0u - ((bits >> (2 * i + 1)) & 1u)) & 0xFFFF0000u);
+      ninf = 0xFF80FF80u;
+    }
+    x[i] = (x[i] & keep) | (ninf & ~keep);
+  }
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
 
 // One LDS instance per translation unit; every kernel of the unit uses it, as
 // do the non-inlined functions of the streaming path.
@@ -213,7 +244,8 @@ __device__ __forceinline__ Resolved resolve_sorted(Lds& L, int n, int cnt_above,
 // value-sorted candidates): re-keyed by token id, sorted ascending by id, an
 // exclusive scan of their weights, and the first id whose running total
 // exceeds u * Z_S (else the last id with weight). Every thread calls.
-__device__ __forceinline__ int draw_sorted(Lds& L, int n, float M, float c, double u) {
+__device__ __forceinline__ int draw_sorted(Lds& L, int n, float M, float c, double u,
+                                           double* wtok) {
   constexpr int P = kCap / kBlock;
   for (int i = threadIdx.x; i < n; i += kBlock) {
     const unsigned long long k = L.key[i];
@@ -245,6 +277,7 @@ __device__ __forceinline__ int draw_sorted(Lds& L, int n, float M, float c, doub
   int pos = block_min<kBlock>(hit, L.bs);
   if (pos == 0x7FFFFFFF) pos = block_max<kBlock>(lastw, L.bs);
   const int token = (int)~key_hi(L.key[pos]);
+  *wtok = (double)weight(key2f((uint32_t)L.key[pos]), M, c);
   __syncthreads();
   return token;
 }
@@ -416,12 +449,14 @@ __device__ __forceinline__ void wave_resolve_draw_w(Lds& L, unsigned long long k
     pos = 63 - __clzll((long long)pw);
   }
   const int token = (int)readlane_u32(idx, pos);
+  const double wt = readlane_t(w, pos);
   if (lane == 0) {
     L.si[0] = token;
     L.si[1] = n_in;
     L.si[7] = 0;
     L.sf[0] = tau;
     L.sd[1] = total;
+    L.sd[2] = wt;
   }
 }
 

@@ -128,6 +128,32 @@ struct RegRow {
   __device__ __forceinline__ void elems(int j, float* v) const { unpack<DT>(get(j), v); }
 };
 
+// Constrained decoding: row m of the allowed-token mask (ceil(V/32) words)
+// is staged in L.vmask with direct global-to-LDS loads, issued before the
+// row's own loads; mask_ready<NC>() after those waits until at most NC loads
+// are outstanding (so the mask's have landed, the row's may still fly) and a
+// barrier makes every wavefront's words visible. Pass A then replaces the
+// disallowed elements by -inf as each chunk lands.
+__device__ __forceinline__ void stage_mask(const uint32_t* m, int V, Lds& L) {
+  const int words = (V + 31) >> 5;
+  const int wid = threadIdx.x / kWave;
+#pragma nounroll
+  for (int k = 0; k * kBlock < words; ++k) {
+    const int w = k * kBlock + (int)threadIdx.x;
+    if (w < words)
+      __builtin_amdgcn_global_load_lds(m + w, &L.vmask[k * kBlock + wid * kWave], 4, 0, 0);
+  }
+  sched_fence();   // the row's loads are issued after these (mask_ready counts on it)
+}
+template <int NC>
+__device__ __forceinline__ void mask_ready() {
+  static_assert(NC < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((NC & 0xF) | ((NC >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Bit j set iff pred(j) holds in some lane (pred is evaluated by every lane;
 // call with the whole wavefront active). Unrolled: NC compares and a few
 // scalar instructions.
@@ -181,7 +207,8 @@ struct RowStats {
 // per thread). That is a lower bound of the row's
 // weight sum Z, enough to settle JOINT top-p whenever the nucleus is not
 // close to the cut.
-template <int DT, int NC>
+// MASK: apply the staged allowed-token mask (stage_mask) to each chunk first.
+template <bool MASK = false, int DT, int NC>
 __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, float c, Lds& L) {
   float tmax = kNegInf;
 #pragma unroll
@@ -189,6 +216,8 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
     uint4 t = r.get(j);
     asm volatile("" : "+v"(t.x), "+v"(t.y), "+v"(t.z), "+v"(t.w));
     t = r.settle(j, t);
+    if constexpr (MASK)
+      t = apply_mask<DT>(t, chunk_mask_bits<DT>(L.vmask, (long long)j * kBlock + threadIdx.x));
     r.put(j, t);
     const float m = chunk_max<DT>(t);
     r.put_cmax(j, m);
@@ -278,7 +307,8 @@ __device__ __forceinline__ int reg_argmax(const RegRow<DT, NC>& r, float M, Lds&
 // EPC weights of chunk row j (j is wavefront-uniform).
 // Returns the element index; *total_out gets the total weight.
 template <int NC, int EPC, class CW>
-__device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* total_out) {
+__device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* total_out,
+                                         double* wtok = nullptr) {
   static_assert(NC <= kWalkBatch, "walk scratch too small");
   const int tid = threadIdx.x, lane = __lane_id(), wid = tid / kWave;
   // per chunk row, each 16-lane row's total (a butterfly inside the row, no
@@ -352,9 +382,14 @@ __device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* tota
     }
     if (pick < 0) pick = lastpos;
     L.si[3] = (jstar * kBlock + tid) * EPC + pick;
+    double wp = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) wp = e == pick ? (double)wj[e] : wp;
+    L.sd[4] = wp;
   }
   __syncthreads();
   const int tok = L.si[3];
+  if (wtok) *wtok = L.sd[4];
   __syncthreads();
   return tok;
 }
@@ -430,6 +465,7 @@ struct FastOut {
   float tau;
   int kept;
   double zs;      // sum of weights over S
+  double wtok;    // weight of the drawn token
 };
 
 // Single-pass compaction of the logits >= Lb into the wavefront's own LDS
@@ -591,7 +627,7 @@ __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, floa
                                             Lds& L) {
   constexpr int EPC = Fmt<DT>::EPC;
   const int tid = threadIdx.x;
-  FastOut out{0, 0, -1, kPosInf, 0, 0.0};
+  FastOut out{0, 0, -1, kPosInf, 0, 0.0, 0.0};
   // In SEQUENTIAL mode top-p measures against the whole top-k set, so min-p
   // may not narrow the candidates there.
   const bool seq_kp = f.seq && f.k_on && f.p_on;
@@ -632,6 +668,7 @@ __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, floa
     out.kept = L.si[1];
     out.tau = L.sf[0];
     out.zs = L.sd[1];
+    out.wtok = L.sd[2];
     __syncthreads();
     return out;
   }
@@ -669,7 +706,7 @@ __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, floa
   out.tau = res.tau;
   out.kept = res.n_in;
   out.zs = res.zs;
-  out.token = draw_sorted(L, res.n_in, M, c, u);
+  out.token = draw_sorted(L, res.n_in, M, c, u, &out.wtok);
   out.drawn = 1;
   return out;
 }

@@ -21,9 +21,11 @@ struct StreamRow {
   int V;
   int nct;        // chunks per thread
   bool aligned;
+  const uint32_t* mask;   // the row's allowed-token words, or null
 
-  __device__ __forceinline__ StreamRow(const unsigned char* p_, int V_, bool aligned_)
-      : p(p_), V(V_), aligned(aligned_) {
+  __device__ __forceinline__ StreamRow(const unsigned char* p_, int V_, bool aligned_,
+                                       const uint32_t* mask_ = nullptr)
+      : p(p_), V(V_), aligned(aligned_), mask(mask_) {
     const long long chunks = ((long long)V + EPC - 1) / EPC;
     nct = (int)((chunks + kBlock - 1) / kBlock);
   }
@@ -33,10 +35,11 @@ struct StreamRow {
   __device__ __forceinline__ int base(int j) const { return (int)(chunk_id(j) * EPC); }
   __device__ __forceinline__ uint4 chunk(int j) const {
     const long long c = chunk_id(j);
-    if (aligned && (c + 1) * EPC <= V)
-      return *reinterpret_cast<const uint4*>(p + c * EPC * Fmt<DT>::ESZ);
     if (c * EPC >= V) return neg_inf_chunk<DT>();
-    return load_chunk_slow<DT>(p, c, V);
+    const uint4 t = (aligned && (c + 1) * EPC <= V)
+                        ? *reinterpret_cast<const uint4*>(p + c * EPC * Fmt<DT>::ESZ)
+                        : load_chunk_slow<DT>(p, c, V);
+    return mask ? apply_mask<DT>(t, chunk_mask_bits<DT>(mask, c)) : t;
   }
   __device__ __forceinline__ void elems(int j, float* v, float* m) const {
     unpack<DT>(chunk(j), v);
@@ -321,7 +324,7 @@ __device__ __noinline__ Cut general_stream(const StreamRow<DT> s, float M, doubl
 // weight sum over S.
 template <int DT>
 __device__ __noinline__ int walk_stream(const StreamRow<DT> s, float tau, float M, float c,
-                                        double u, double* total_out) {
+                                        double u, double* total_out, double* wtok) {
   constexpr int EPC = Fmt<DT>::EPC;
   Lds& L = tsr_lds;
   const int tid = threadIdx.x, lane = __lane_id(), wid = tid / kWave;
@@ -405,9 +408,14 @@ __device__ __noinline__ int walk_stream(const StreamRow<DT> s, float tau, float 
       }
     if (pick < 0) pick = lastpos;
     L.si[3] = s.base(jstar) + pick;
+    double wp = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) wp = e == pick ? (double)wj[e] : wp;
+    L.sd[4] = wp;
   }
   __syncthreads();
   const int tok = L.si[3];
+  *wtok = L.sd[4];
   __syncthreads();
   return tok;
 }

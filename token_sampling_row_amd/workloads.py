@@ -152,3 +152,40 @@ def random_rows(seed: int, rows: int, vocab: int, a: float = 1.0, sigma: float =
     for b in range(rows):
         out[b] = zipf_row([seed, b], vocab, a, sigma)
     return _round_rows(out, dtype)
+
+
+def allowed_words(seed: int, rows: int, vocab: int, kind: str) -> np.ndarray:
+    """Seeded allowed-token bitmasks for constrained decoding, packed as the
+    sampler reads them: uint32 [rows, ceil(vocab / 32)], token i allowed iff
+    bit i % 32 of word i // 32 is set. The bits past ``vocab`` in the last
+    word are random (they must be ignored). ``kind``:
+
+      "all"        every token allowed
+      "none"       no token allowed (the invalid state of an empty set)
+      "p=<x>"      each token allowed independently with probability x
+      "few=<n>"    n tokens drawn without replacement (a grammar that allows a
+                   handful of continuations: digits, a quote, a brace)
+      "block"      one contiguous id range of a random length
+    """
+    words = (vocab + 31) // 32
+    out = np.zeros((rows, words * 32), dtype=bool)
+    for b in range(rows):
+        rng = np.random.default_rng([7000, seed, b])
+        if kind == "all":
+            out[b, :vocab] = True
+        elif kind == "none":
+            pass
+        elif kind.startswith("p="):
+            out[b, :vocab] = rng.random(vocab) < float(kind[2:])
+        elif kind.startswith("few="):
+            n = min(int(kind[4:]), vocab)
+            out[b, rng.choice(vocab, n, replace=False)] = True
+        elif kind == "block":
+            lo = int(rng.integers(0, vocab))
+            hi = int(rng.integers(lo + 1, vocab + 1))
+            out[b, lo:hi] = True
+        else:
+            raise ValueError(f"unknown mask kind {kind}")
+        out[b, vocab:] = rng.random(words * 32 - vocab) < 0.5
+    bits = out.reshape(rows, words, 32).astype(np.uint64)
+    return (bits << np.arange(32, dtype=np.uint64)).sum(axis=2).astype(np.uint32)
