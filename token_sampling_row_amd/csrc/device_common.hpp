@@ -101,6 +101,17 @@ __device__ __forceinline__ float weight(float v, float M, float c) {
   return __builtin_amdgcn_exp2f((v - M) * c);
 }
 
+// ln(a / b) for positive a and b (NaN in, NaN out): the binary exponents
+// exactly, the mantissas in [0.5, 1) by the hardware log2 (about 1e-7
+// absolute), instead of two double-precision logarithms.
+__device__ __forceinline__ float log_ratio(double a, double b) {
+  int ea, eb;
+  const double ma = frexp(a, &ea), mb = frexp(b, &eb);
+  const double l2 = (double)(__builtin_amdgcn_logf((float)ma) - __builtin_amdgcn_logf((float)mb)) +
+                    (double)(ea - eb);
+  return (float)(l2 * 0.6931471805599453);
+}
+
 // ------------------------------------------------------------ Philox4x32-10
 // Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11): ten
 // rounds of two 32x32->64 products, each high word xored with the other

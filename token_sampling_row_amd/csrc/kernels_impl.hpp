@@ -49,7 +49,7 @@ __device__ __forceinline__ void write_row(int row, int tok, int status, int kept
     if (dg.kept_count) dg.kept_count[row] = kept;
     if (dg.threshold) dg.threshold[row] = tmin;
     if (dg.kept_mass) dg.kept_mass[row] = kmass;
-    if (dg.logprob) dg.logprob[row] = (float)(log(wtok) - log(zs));
+    if (dg.logprob) dg.logprob[row] = log_ratio(wtok, zs);
   }
 }
 constexpr double kNaN = __builtin_nan("");
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   if constexpr (MASK) mask_ready<NC>();
   const bool greedy = (kp.flags & F_GREEDY) != 0;
   const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);   // while the loads fly
-  const RowStats st = reg_stats<MASK>(r, !greedy && joint_top_p(kp), kp.c, L);
+  const RowStats st = reg_stats<MASK>(r, !greedy && joint_top_p(kp), kp.c, L, V);
   if (st.status != 0) {
     write_row(row, -1, st.status, 0, kNegInf, 0.0, kNaN, kNaN, out, dg);
     zero_probs(dg, row, V);
@@ -378,7 +378,8 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
     // (no candidate bound can narrow a wide kept set).
     const bool narrow = f.m_on || (MASK && f.k_on && f.k <= kBlock / 4);
     FastOut fo{0, 0, -1, kPosInf, 0, 0.0, 0.0};
-    if (!(WIDE && DT == 1) || narrow) fo = fast_cut(r, V, M, st.tmin, st.zlo, c, f, u, L);
+    if (!(WIDE && DT == 1) || narrow)
+      fo = fast_cut<MASK>(r, V, M, st.tmin, st.zlo, c, f, u, L, st.nallow);
     if (fo.ok) {
       tau = fo.tau;
       kept = fo.kept;

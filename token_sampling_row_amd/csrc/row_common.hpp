@@ -29,6 +29,7 @@ struct WaveStats {
   float smin;    // smallest finite chunk maximum in the wave
   double z;      // weight sum relative to m
   int bad;       // NaN or +inf seen
+  int na;        // allowed elements (masked rows)
 };
 
 struct Lds {
@@ -369,8 +370,12 @@ __device__ __forceinline__ int find_boundary(Lds& L, int cnt_above, double mass_
 template <int W>
 __device__ __forceinline__ void wave_resolve_draw_w(Lds& L, unsigned long long key, int n, float M,
                                                     float c, const Filters& f, double zref,
-                                                    bool z_exact, double u) {
+                                                    bool z_exact, bool all_in, double u) {
   const int lane = __lane_id();
+  if (all_in) {   // the candidates are every finite element: their sum is Z
+    zref = wave_sum(lane < n ? (double)weight(key2f(key_hi(key)), M, c) : 0.0);
+    z_exact = true;
+  }
   const uint32_t kM = fkey(M);
   const bool seq_kp = f.seq && f.k_on && f.p_on;
   const bool k_cuts = f.k_on && n > f.k;
@@ -461,7 +466,8 @@ __device__ __forceinline__ void wave_resolve_draw_w(Lds& L, unsigned long long k
 }
 
 __device__ __forceinline__ void wave_resolve_draw(Lds& L, float M, float c, const Filters& f,
-                                                  double zref, bool z_exact, double u) {
+                                                  double zref, bool z_exact, bool all_in,
+                                                  double u) {
   const int lane = __lane_id();
   // all counts first (independent LDS reads), then one read per lane
   int cq[kWaves];
@@ -479,9 +485,9 @@ __device__ __forceinline__ void wave_resolve_draw(Lds& L, float M, float c, cons
   unsigned long long key = 0ull;
   if (lane < n) key = cand_key(__uint_as_float(L.wc[sq].val[so]), (int)L.wc[sq].idx[so]);
   if (n <= 16)
-    wave_resolve_draw_w<16>(L, key, n, M, c, f, zref, z_exact, u);
+    wave_resolve_draw_w<16>(L, key, n, M, c, f, zref, z_exact, all_in, u);
   else
-    wave_resolve_draw_w<64>(L, key, n, M, c, f, zref, z_exact, u);
+    wave_resolve_draw_w<64>(L, key, n, M, c, f, zref, z_exact, all_in, u);
 }
 
 }  // namespace tsr

@@ -197,6 +197,7 @@ struct RowStats {
   float M;        // row max
   float tmin;     // smallest finite per-thread maximum
   double zlo;     // a lower bound of the row's weight sum (when asked for)
+  int nallow;     // at least the number of allowed elements (huge without a mask)
 };
 
 // Row statistics in one pass over the registers as the loads land: NaN/+inf
@@ -207,17 +208,53 @@ struct RowStats {
 // per thread). That is a lower bound of the row's
 // weight sum Z, enough to settle JOINT top-p whenever the nucleus is not
 // close to the cut.
-// MASK: apply the staged allowed-token mask (stage_mask) to each chunk first.
+// MASK: apply the staged allowed-token mask (stage_mask, V tokens) to each
+// chunk first, and count the allowed tokens (a row with few of them is
+// resolved over all its finite elements).
 template <bool MASK = false, int DT, int NC>
-__device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, float c, Lds& L) {
+__device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, float c, Lds& L,
+                                              int V = 0) {
   float tmax = kNegInf;
+  int nallow = 0;
+  // thread t's chunk j takes bits tsh.. of mask word j * kWpr + tw; the words
+  // of the next two chunk rows are read ahead of their use
+  constexpr int kCpw = 32 / Fmt<DT>::EPC;   // chunks per mask word
+  constexpr int kWpr = kBlock / kCpw;       // mask words per chunk row
+  const int tw = (int)threadIdx.x / kCpw;
+  const uint32_t tsh = ((uint32_t)threadIdx.x % kCpw) * Fmt<DT>::EPC;
+  uint32_t mw0 = 0, mw1 = 0;
+  if constexpr (MASK) {
+    // (bits of ids past V in the last word may be set: an over-count)
+    for (int w = threadIdx.x; w < ((V + 31) >> 5); w += kBlock) nallow += __builtin_popcount(L.vmask[w]);
+    mw0 = L.vmask[tw];
+    if (NC > 1) mw1 = L.vmask[kWpr + tw];
+  }
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
+    const uint32_t mwc = mw0;
+    if constexpr (MASK) {
+      mw0 = mw1;
+      if (j + 2 < NC) mw1 = L.vmask[(j + 2) * kWpr + tw];
+    }
     uint4 t = r.get(j);
     asm volatile("" : "+v"(t.x), "+v"(t.y), "+v"(t.z), "+v"(t.w));
     t = r.settle(j, t);
-    if constexpr (MASK)
-      t = apply_mask<DT>(t, chunk_mask_bits<DT>(L.vmask, (long long)j * kBlock + threadIdx.x));
+    if constexpr (MASK) {
+      // element-wise masking only where some lane's chunk is partly allowed;
+      // wholly allowed or wholly disallowed chunks (the common case of a
+      // grammar's small or near-complete sets) take one select per dword
+      constexpr uint32_t kAll = (1u << Fmt<DT>::EPC) - 1u;
+      const uint32_t bits = (mwc >> tsh) & kAll;
+      if (__any(bits != 0u && bits != kAll)) {
+        t = apply_mask<DT>(t, bits);
+      } else {
+        const uint4 ni = neg_inf_chunk<DT>();
+        t.x = bits ? t.x : ni.x;
+        t.y = bits ? t.y : ni.y;
+        t.z = bits ? t.z : ni.z;
+        t.w = bits ? t.w : ni.w;
+      }
+    }
     r.put(j, t);
     const float m = chunk_max<DT>(t);
     r.put_cmax(j, m);
@@ -232,21 +269,25 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
   const float wt = wave_min(tmax > kNegInf ? tmax : kPosInf);
   const int wb = 0;
   double wz = 0.0;
+  int wna = 0;
+  if constexpr (MASK) wna = wave_sum(nallow);
   if (need_zlo)   // relative to the wave max
     wz = wave_sum(tmax > kNegInf && tmax < kPosInf ? zt * (double)weight(tmax, wm, c) : 0.0);
   const int wid = threadIdx.x / kWave;
   __syncthreads();
-  if (__lane_id() == 0) L.ws[wid] = WaveStats{wm, wt, wz, wb};
+  if (__lane_id() == 0) L.ws[wid] = WaveStats{wm, wt, wz, wb, wna};
   __syncthreads();
   RowStats st;
   float M = kNegInf, tmin = kPosInf;
-  int anybad = 0;
+  int anybad = 0, na = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     M = fmaxn(M, L.ws[w].m);
     tmin = fminf(tmin, L.ws[w].smin);
     anybad |= L.ws[w].bad;
+    na += L.ws[w].na;
   }
+  st.nallow = MASK ? na : 0x7FFFFFFF;
   double Z = 0.0;
   if (need_zlo) {
 #pragma unroll
@@ -621,10 +662,11 @@ __device__ __forceinline__ float topk_sketch(const RegRow<DT, NC>& r, float M, f
 // Candidate bound, compaction and exact resolution (see the file comment).
 // zlo is a lower bound of the row's weight sum (JOINT top-p); the exact sum is
 // formed here only when the bound cannot settle the cut. u is the uniform.
-template <int DT, int NC>
+// MASK: nallow bounds the row's allowed tokens from above.
+template <bool MASK = false, int DT, int NC>
 __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, float M, float tmin,
                                             double zlo, float c, const Filters& f, double u,
-                                            Lds& L) {
+                                            Lds& L, int nallow = 0) {
   constexpr int EPC = Fmt<DT>::EPC;
   const int tid = threadIdx.x;
   FastOut out{0, 0, -1, kPosInf, 0, 0.0, 0.0};
@@ -633,7 +675,10 @@ __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, floa
   const bool seq_kp = f.seq && f.k_on && f.p_on;
   const bool joint_p = f.p_on && !seq_kp;
   float Lb = seq_kp ? kNegInf : f.tau_m;
-  if (V <= kWaveCap) Lb = -kFltMax;     // the whole (finite) row fits one wavefront
+  // the whole (finite, allowed) row fits one wavefront: every finite element
+  // is a candidate and their sum is Z
+  bool all_in = MASK && nallow <= kWaveCap;
+  if (all_in || V <= kWaveCap) Lb = -kFltMax;
   bool fits = false;
   if (Lb > kNegInf) {
     wave_compact(r, Lb, L);
@@ -645,6 +690,7 @@ __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, floa
     const float kb = topk_sketch(r, M, fmaxf(Lb, tmin), f.k, L);
     if (kb > Lb) {
       Lb = kb;
+      all_in = false;
       wave_compact(r, Lb, L);
       __syncthreads();
       fits = wave_regions_total(L) <= kWaveCap;
@@ -657,7 +703,7 @@ __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, floa
     bool zx = !joint_p;
 #pragma nounroll
     for (;;) {
-      if (tid < kWave) wave_resolve_draw(L, M, c, f, zref, zx, u);
+      if (tid < kWave) wave_resolve_draw(L, M, c, f, zref, zx, all_in, u);
       __syncthreads();
       if (!L.si[7]) break;
       zref = reg_weight_sum(r, M, c, L);
