@@ -17,8 +17,8 @@ Pages cited:
   [P4] scratchllm.com "Efficient Inference & Compression", section
        "Speculative decoding".
   [P5] legost.in "Choosing the next word", sections "Temperature: one dial for
-       boldness", "Cutting off the tail: top-k and top-p", "Where the
-       randomness comes from, and where it stops".
+       boldness", "The repetition penalty", "Cutting off the tail: top-k and
+       top-p", "Where the randomness comes from, and where it stops".
 """
 from __future__ import annotations
 
@@ -35,6 +35,7 @@ __all__ = [
     "greedy_batch", "accept_probability", "residual", "spec_verify_row",
     "spec_verify_batch", "acceptance_probability", "expected_accepted_prefix",
     "values_from_stored", "allowed_from_words", "mask_logits", "log_p_tilde",
+    "round_to_element", "repetition_penalty", "HISTORY_MAX",
 ]
 
 ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BADTOKEN = 0, 1, 2, 3
@@ -42,6 +43,8 @@ ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BADTOKEN = 0, 1, 2, 3
 # range in the GPU path, so both sides reject it rather than disagree.
 TEMPERATURE_MIN = 1e-30
 JOINT, SEQUENTIAL = 0, 1
+# The look-back window of the repetition penalty (P5 "The repetition penalty").
+HISTORY_MAX = 64
 
 
 class InvalidParams(ValueError):
@@ -125,6 +128,44 @@ def mask_logits(l: np.ndarray, allowed) -> np.ndarray:
     NaN or +inf included (the page's mask_logits selects -inf without reading
     the logit)."""
     return np.where(np.asarray(allowed, dtype=bool), np.asarray(l, dtype=np.float64), -np.inf)
+
+
+def round_to_element(x, dtype: str) -> np.ndarray:
+    """x rounded to the element type of the logits: float32 by round to nearest
+    even, and for bf16 from that float32 to bf16, again to nearest even on the
+    16 dropped bits. NaN and infinities pass unchanged. Returned as float64."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if dtype != "bf16":
+        return f.astype(np.float64)
+    b = f.view(np.uint32).astype(np.uint64)
+    lsb = (b >> 16) & 1                      # ties go to the even bf16 neighbour
+    rounded = ((b + 0x7FFF + lsb) >> 16) << 16
+    keep = ~np.isfinite(f)                   # inf and NaN as they are
+    out = np.where(keep, b, rounded).astype(np.uint32)
+    return out.view(np.float32).astype(np.float64)
+
+
+def repetition_penalty(l: np.ndarray, history, r: float, dtype: str = "f32") -> np.ndarray:
+    """The CTRL repetition penalty as P5 "The repetition penalty" states it:
+    before anything else, every token found in the look-back window (the last
+    HISTORY_MAX tokens) has its logit rescaled by r: z / r if z > 0, z * r if
+    z <= 0, so for r > 1 both branches lower it.
+
+    Readings: a token that occurs several times in the window is rescaled once
+    (the page rescales "each token it finds there", a set); ids outside
+    [0, V) are ignored (window padding); r >= 1 and r = 1 changes nothing. The
+    rescaled logit is rounded to the logits' element type (round_to_element):
+    the sampler keeps each row in its input type, so both sides take every
+    later decision on the same rounded value."""
+    l = np.array(l, dtype=np.float64)
+    ids = np.unique([int(h) for h in history if 0 <= int(h) < l.size]).astype(np.int64)
+    if r == 1.0 or ids.size == 0:
+        return l
+    z = l[ids]
+    with np.errstate(over="ignore"):
+        pen = np.where(z > 0, z / r, z * r)
+    l[ids] = round_to_element(pen, dtype)
+    return l
 
 
 def log_p_tilde(l: np.ndarray, keep: np.ndarray, token: int, temperature: float) -> float:
@@ -274,19 +315,24 @@ class RowResult:
 
 
 def sample_row(l: np.ndarray, params, seed: int, row: int, step: int,
-               allowed=None) -> RowResult:
+               allowed=None, history=None, penalty: float = 1.0,
+               dtype: str = "f32") -> RowResult:
     """One row of the sampler: status, greedy or chain + draw.
 
     The uniform is u = w0 * 2^-32 with w0 the first Philox4x32-10 word of
-    counter (row, 0 | SAMPLE << 16, step) under key = seed. ``allowed`` (a
-    bool [V], or None for every token) masks the row first (P2 section 39.3);
-    an allowed set without a finite logit is the empty state. The result
-    carries log p~ of the drawn token (0 under greedy decoding, where p~ is a
-    point mass).
+    counter (row, 0 | SAMPLE << 16, step) under key = seed. ``history`` (ids
+    of the recent tokens, or None) and ``penalty`` apply the repetition
+    penalty to the raw logits first (P5), ``dtype`` being the logits' element
+    type; ``allowed`` (a bool [V], or None for every token) then masks the row
+    (P2 section 39.3); an allowed set without a finite logit is the empty
+    state. The result carries log p~ of the drawn token (0 under greedy
+    decoding, where p~ is a point mass).
     """
     prm = Params.of(params)
     check_params(prm)
     l = np.asarray(l, dtype=np.float64)
+    if history is not None:
+        l = repetition_penalty(l, history, penalty, dtype)
     if allowed is not None:
         l = mask_logits(l, allowed)
     st = row_status(l)
