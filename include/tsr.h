@@ -166,6 +166,38 @@ int sample_rows_masked(tsr_handle h, const void* logits, int dtype, int rows, in
                        const tsr_params* params, uint64_t step, int32_t* out_tokens,
                        float* out_logprob, const tsr_diag* diag, void* hip_stream);
 
+/* Per-row inputs applied to the logits before temperature and the filters
+ * (device memory; every pointer may be NULL, a NULL struct means none).
+ *  allowed, allowed_stride: the allowed-token bitmask, laid out and applied
+ *      as in sample_rows_masked [P2 39.3].
+ *  history [rows][history_stride] int32: the look-back window of each row,
+ *      its last history_len token ids (0 <= history_len <= 64,
+ *      history_stride >= history_len); ids outside [0, vocab) are padding.
+ *  repetition_penalty: r, finite and >= 1 (TSR_EINVAL otherwise when a
+ *      window is given). Every distinct id of the window has its logit
+ *      rescaled once, z / r if z > 0, z * r otherwise, before anything else
+ *      [P5 "The repetition penalty"]; the rescaled logit is rounded to the
+ *      logits' element type (float32; bf16 to nearest even from that float32).
+ *      r = 1, history NULL or history_len 0: no penalty. */
+typedef struct {
+  const uint32_t* allowed;
+  int64_t allowed_stride;
+  const int32_t* history;
+  int32_t history_len;
+  int64_t history_stride;
+  double repetition_penalty;
+} tsr_constraints;
+
+/* sample_rows with the per-row inputs of `cons` (nullable) and log p~ of each
+ * drawn token (out_logprob, nullable, as in sample_rows_masked). The penalty
+ * applies first, then the mask; everything after is sample_rows.
+ * sample_rows_masked(..., allowed, allowed_stride, ...) is this call with a
+ * constraint holding the mask only. */
+int sample_rows_ex(tsr_handle h, const void* logits, int dtype, int rows, int vocab,
+                   int64_t row_stride, const tsr_constraints* cons, const tsr_params* params,
+                   uint64_t step, int32_t* out_tokens, float* out_logprob,
+                   const tsr_diag* diag, void* hip_stream);
+
 /* The speculative verify step [P3 "The Algorithm"; P1, P4 "Speculative
  * decoding"; P2 39.4] for `rows` sequences with K drafted tokens each.
  *  target_logits [rows][K+1][vocab]: the target's logits at the K draft

@@ -94,6 +94,37 @@ def run_masked(sampler, x, words, params, step, diag=True, probs=False):
     return res
 
 
+def run_ex(sampler, x, params, step, words=None, hist=None, penalty=1.0, diag=True,
+           probs=False):
+    """sample_rows_ex through the C ABI: ``words`` a uint32 [rows, W] mask or
+    None, ``hist`` an int32 [rows, H] window or None. Returns token, logprob
+    and the diagnostics."""
+    rows, V = x.shape
+    allowed = history = None
+    if words is not None:
+        allowed = torch.from_numpy(np.ascontiguousarray(words).view(np.int32)).to(x.device)
+    if hist is not None:
+        history = torch.from_numpy(np.ascontiguousarray(hist, dtype=np.int32)).to(x.device)
+    d = None
+    if diag:
+        d = dict(status=torch.full((rows,), -7, dtype=torch.int32, device=x.device),
+                 kept_count=torch.full((rows,), -7, dtype=torch.int32, device=x.device),
+                 threshold=torch.full((rows,), float("nan"), dtype=torch.float32, device=x.device),
+                 kept_mass=torch.full((rows,), float("nan"), dtype=torch.float64, device=x.device),
+                 probs=(torch.full((rows, V), float("nan"), dtype=torch.float32, device=x.device)
+                        if probs else None))
+    lp = torch.full((rows,), 12345.0, dtype=torch.float32, device=x.device)
+    out = sampler.sample_rows_ex(x, params, step, allowed=allowed, history=history,
+                                 penalty=penalty, logprob=lp, diag=d)
+    torch.cuda.synchronize()
+    res = {"token": out.cpu().numpy(), "logprob": lp.cpu().numpy()}
+    if d:
+        for k, t in d.items():
+            if t is not None:
+                res[k] = t.cpu().numpy()
+    return res
+
+
 def compare_logprob(gpu: dict, refs: list, rows) -> int:
     """log p~ of the drawn tokens: NaN on bad rows, 0 on greedy rows, else the
     oracle's within LOGP_TOL wherever token and kept set agree (elsewhere the

@@ -22,7 +22,8 @@ F32, BF16 = 0, 1
 JOINT, SEQUENTIAL = 0, 1
 ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BADTOKEN = 0, 1, 2, 3
 EXPORTED_SYMBOLS = ("sampler_init", "sampler_destroy", "greedy_argmax", "sample_rows",
-                    "sample_rows_masked", "spec_verify", "sampler_philox", "sampler_strerror")
+                    "sample_rows_masked", "sample_rows_ex", "spec_verify", "sampler_philox",
+                    "sampler_strerror")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -53,6 +54,12 @@ class _Diag(ctypes.Structure):
                 ("probs", ctypes.c_void_p)]
 
 
+class _Constraints(ctypes.Structure):
+    _fields_ = [("allowed", ctypes.c_void_p), ("allowed_stride", ctypes.c_int64),
+                ("history", ctypes.c_void_p), ("history_len", ctypes.c_int32),
+                ("history_stride", ctypes.c_int64), ("repetition_penalty", ctypes.c_double)]
+
+
 _lib = None
 
 
@@ -74,6 +81,9 @@ def load_library():
     lib.sample_rows_masked.argtypes = [vp, vp, i32, i32, i32, i64, vp, i64,
                                        ctypes.POINTER(_Params), u64, vp, vp,
                                        ctypes.POINTER(_Diag), vp]
+    lib.sample_rows_ex.argtypes = [vp, vp, i32, i32, i32, i64, ctypes.POINTER(_Constraints),
+                                   ctypes.POINTER(_Params), u64, vp, vp, ctypes.POINTER(_Diag),
+                                   vp]
     lib.spec_verify.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, ctypes.POINTER(_Params),
                                 u64, vp, vp, vp, vp]
     lib.sampler_philox.argtypes = [vp, vp, i32, vp, vp]
@@ -219,6 +229,36 @@ class Sampler:
             _ptr(allowed), astride, ctypes.byref(cp), ctypes.c_uint64(int(step)), _ptr(out),
             _ptr(logprob), ctypes.byref(d) if d is not None else None, _stream_ptr(stream)),
             "sample_rows_masked")
+        return out
+
+    def sample_rows_ex(self, logits, params, step: int, allowed=None, history=None,
+                       penalty: float = 1.0, out=None, logprob=None, diag=None, stream=None):
+        """sample_rows with an allowed-token mask (as in sample_rows_masked) and
+        a repetition penalty: ``history`` is a [rows, H] int32 device tensor of
+        each row's recent token ids (H <= 64, ids outside [0, vocab) ignored),
+        ``penalty`` the factor r >= 1. Returns the tokens."""
+        import torch
+        rows, vocab = logits.shape
+        assert logits.stride(1) == 1, "rows must be contiguous"
+        cs = _Constraints(None, 0, None, 0, 0, float(penalty))
+        if allowed is not None:
+            assert allowed.dtype == torch.int32 and allowed.stride(1) == 1
+            cs.allowed, cs.allowed_stride = allowed.data_ptr(), allowed.stride(0)
+        if history is not None:
+            assert history.dtype == torch.int32 and history.stride(1) == 1
+            cs.history, cs.history_len = history.data_ptr(), history.shape[1]
+            cs.history_stride = history.stride(0)
+        out = torch.empty(rows, dtype=torch.int32, device=logits.device) if out is None else out
+        cp = Params.of(params)._c()
+        d = None
+        if diag is not None:
+            d = _Diag(*(ctypes.c_void_p(diag[k].data_ptr()) if diag.get(k) is not None else None
+                        for k in ("status", "kept_count", "threshold", "kept_mass", "probs")))
+        _check(load_library().sample_rows_ex(
+            self._h, _ptr(logits), _dtype_code(logits), rows, vocab, logits.stride(0),
+            ctypes.byref(cs), ctypes.byref(cp), ctypes.c_uint64(int(step)), _ptr(out),
+            _ptr(logprob), ctypes.byref(d) if d is not None else None, _stream_ptr(stream)),
+            "sample_rows_ex")
         return out
 
     def spec_verify(self, target, draft, draft_tokens, params, step: int, out_tokens=None,

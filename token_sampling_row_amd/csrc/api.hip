@@ -168,17 +168,28 @@ int greedy_argmax(tsr_handle h, const void* logits, int dtype, int rows, int voc
   });
 }
 
-int sample_rows_masked(tsr_handle h, const void* logits, int dtype, int rows, int vocab,
-                       int64_t row_stride, const uint32_t* allowed, int64_t allowed_stride,
-                       const tsr_params* params, uint64_t step, int32_t* out_tokens,
-                       float* out_logprob, const tsr_diag* diag, void* hip_stream) {
+int sample_rows_ex(tsr_handle h, const void* logits, int dtype, int rows, int vocab,
+                   int64_t row_stride, const tsr_constraints* cons, const tsr_params* params,
+                   uint64_t step, int32_t* out_tokens, float* out_logprob, const tsr_diag* diag,
+                   void* hip_stream) {
   if (!h || !logits || !out_tokens) return TSR_EINVAL;
   if (dtype != TSR_F32 && dtype != TSR_BF16) return TSR_EINVAL;
   if (rows < 0 || rows > h->max_rows || vocab < 1 || vocab > h->max_vocab) return TSR_EINVAL;
   if (row_stride < vocab || !elem_aligned(logits, dtype)) return TSR_EINVAL;
-  if (allowed) {
+  const tsr_constraints none{};
+  const tsr_constraints& cs = cons ? *cons : none;
+  if (cs.allowed) {
     const int64_t words = ((int64_t)vocab + 31) / 32;
-    if (allowed_stride < words || ((uintptr_t)allowed % 4) != 0) return TSR_EINVAL;
+    if (cs.allowed_stride < words || ((uintptr_t)cs.allowed % 4) != 0) return TSR_EINVAL;
+  }
+  const bool rep_given = cs.history && cs.history_len > 0;
+  if (rep_given) {
+    if (cs.history_len > tsr::kHistMax || cs.history_stride < cs.history_len ||
+        ((uintptr_t)cs.history % 4) != 0)
+      return TSR_EINVAL;
+    if (!isfinite(cs.repetition_penalty) || cs.repetition_penalty < 1.0) return TSR_EINVAL;
+  } else if (cs.history_len < 0) {
+    return TSR_EINVAL;
   }
   const int prc = check_params(params);
   if (prc != TSR_OK) return prc;
@@ -194,10 +205,17 @@ int sample_rows_masked(tsr_handle h, const void* logits, int dtype, int rows, in
   }
   dg.logprob = out_logprob;
   tsr::KParams kp = make_kparams(h, params, vocab, step, dg.kept_mass != nullptr);
-  if (allowed) {
-    kp.allowed = allowed;
-    kp.allowed_stride = (long long)allowed_stride;
+  if (cs.allowed) {
+    kp.allowed = cs.allowed;
+    kp.allowed_stride = (long long)cs.allowed_stride;
     kp.flags |= tsr::F_MASK;
+  }
+  if (rep_given && cs.repetition_penalty != 1.0) {
+    kp.hist = cs.history;
+    kp.hist_stride = (long long)cs.history_stride;
+    kp.hist_len = cs.history_len;
+    kp.rpen = cs.repetition_penalty;
+    kp.flags |= tsr::F_REP;
   }
   const long long sb = (long long)row_stride * esize(dtype);
   const int aligned = ((uintptr_t)logits % 16 == 0) && (sb % 16 == 0);
@@ -207,6 +225,17 @@ int sample_rows_masked(tsr_handle h, const void* logits, int dtype, int rows, in
                                             out_tokens, dg, (hipStream_t)hip_stream);
     return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
   });
+}
+
+int sample_rows_masked(tsr_handle h, const void* logits, int dtype, int rows, int vocab,
+                       int64_t row_stride, const uint32_t* allowed, int64_t allowed_stride,
+                       const tsr_params* params, uint64_t step, int32_t* out_tokens,
+                       float* out_logprob, const tsr_diag* diag, void* hip_stream) {
+  tsr_constraints cs{};
+  cs.allowed = allowed;
+  cs.allowed_stride = allowed_stride;
+  return sample_rows_ex(h, logits, dtype, rows, vocab, row_stride, &cs, params, step, out_tokens,
+                        out_logprob, diag, hip_stream);
 }
 
 int sample_rows(tsr_handle h, const void* logits, int dtype, int rows, int vocab,

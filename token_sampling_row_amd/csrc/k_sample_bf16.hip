@@ -12,7 +12,7 @@ hipError_t launch_sample_dt1(const unsigned char* p, int rows, int V, long long 
                        stride_bytes, V, aligned, kp, out, dg);
     return hipGetLastError();
   }
-  const bool mask = (kp.flags & F_MASK) != 0;
+  const bool mask = (kp.flags & (F_MASK | F_REP)) != 0;
   const bool wide = wide_filters(kp, kBlock);
 #define TSR_CASE(N)                                                                            \
   case N:                                                                                      \

@@ -12,7 +12,7 @@ hipError_t launch_sample_dt0(const unsigned char* p, int rows, int V, long long 
                        stride_bytes, V, aligned, kp, out, dg);
     return hipGetLastError();
   }
-  const bool mask = (kp.flags & F_MASK) != 0;
+  const bool mask = (kp.flags & (F_MASK | F_REP)) != 0;
 #define TSR_CASE(N)                                                                             \
   case N:                                                                                       \
     if (mask)                                                                                   \

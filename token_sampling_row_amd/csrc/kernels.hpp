@@ -19,6 +19,10 @@ struct KParams {
   uint32_t step_lo, step_hi;
   const uint32_t* allowed;   // allowed-token bitmask rows (F_MASK), token i = bit i % 32 of word i / 32
   long long allowed_stride;  // words between mask rows
+  const int32_t* hist;       // look-back window rows (F_REP): recent token ids
+  long long hist_stride;     // ids between window rows
+  int hist_len;              // ids per row (<= kHistMax)
+  double rpen;               // repetition penalty r
 };
 enum : int {
   F_GREEDY = 1,   // temperature 0
@@ -28,7 +32,9 @@ enum : int {
   F_SEQ = 16,     // SEQUENTIAL filter mode
   F_Z = 32,       // the full weight sum is wanted (kept-mass diagnostic)
   F_MASK = 64,    // an allowed-token bitmask applies
+  F_REP = 128,    // a repetition penalty applies
 };
+constexpr int kHistMax = 64;   // longest look-back window
 // Filters whose kept set may be far larger than any candidate buffer: no
 // top-k, or one too large for the per-thread-maxima sketch (the sampling
 // launch then takes the WIDE kernel instance).

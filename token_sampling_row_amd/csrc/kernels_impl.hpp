@@ -332,7 +332,13 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel_stream(const unsigned ch
 template <int DT, bool MASK>
 __device__ __forceinline__ StreamRow<DT> row_stream_view(const unsigned char* p, int V,
                                                          const KParams& kp, int row) {
-  return StreamRow<DT>(p, V, true, MASK ? kp.allowed + (long long)row * kp.allowed_stride : nullptr);
+  if constexpr (MASK)
+    return StreamRow<DT>(p, V, true,
+                         (kp.flags & F_MASK) ? kp.allowed + (long long)row * kp.allowed_stride
+                                             : nullptr,
+                         (kp.flags & F_REP) ? kp.hist_len : 0, kp.rpen);
+  else
+    return StreamRow<DT>(p, V, true);
 }
 
 // WIDE (bf16): rows whose kept set the candidate bound cannot narrow are
@@ -351,12 +357,23 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   const int row = blockIdx.x;
   const unsigned char* p = logits + (long long)row * stride_bytes;
   RegRow<DT, NC> r;
-  if constexpr (MASK) stage_mask(kp.allowed + (long long)row * kp.allowed_stride, V, L);
+  RowExtras x;
+  if constexpr (MASK) {
+    x.mask = (kp.flags & F_MASK) != 0;
+    if (kp.flags & F_REP) {   // the window ids, read by wave 0 before the row
+      x.hn = kp.hist_len;
+      x.r = kp.rpen;
+      if ((int)threadIdx.x < x.hn) x.hv = kp.hist[(long long)row * kp.hist_stride + threadIdx.x];
+    }
+    if (x.mask) stage_mask(kp.allowed + (long long)row * kp.allowed_stride, V, L);
+  }
   r.load(p, V, ragged != 0);
-  if constexpr (MASK) mask_ready<NC>();
+  if constexpr (MASK) {
+    if (x.mask) mask_ready<NC>();
+  }
   const bool greedy = (kp.flags & F_GREEDY) != 0;
   const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);   // while the loads fly
-  const RowStats st = reg_stats<MASK>(r, !greedy && joint_top_p(kp), kp.c, L, V);
+  const RowStats st = reg_stats<MASK>(r, !greedy && joint_top_p(kp), kp.c, L, V, x);
   if (st.status != 0) {
     write_row(row, -1, st.status, 0, kNegInf, 0.0, kNaN, kNaN, out, dg);
     zero_probs(dg, row, V);
@@ -417,9 +434,19 @@ __global__ __launch_bounds__(kBlock) void sample_kernel_stream(const unsigned ch
                                                                int32_t* out, DiagPtrs dg) {
   const int row = blockIdx.x;
   const unsigned char* p = logits + (long long)row * stride_bytes;
+  int hn = 0;
+  if (kp.flags & F_REP) {   // publish the look-back window before any read
+    hn = kp.hist_len;
+    if (threadIdx.x < kWave)
+      hist_publish<DT>((int)threadIdx.x < hn ? kp.hist[(long long)row * kp.hist_stride + threadIdx.x]
+                                             : -1,
+                       hn, V, tsr_lds);
+    __syncthreads();
+  }
   const StreamRow<DT> s(p, V, aligned != 0,
                         (kp.flags & F_MASK) ? kp.allowed + (long long)row * kp.allowed_stride
-                                            : nullptr);
+                                            : nullptr,
+                        hn, kp.rpen);
   const bool greedy = (kp.flags & F_GREEDY) != 0;
   const StreamStats st = stream_stats(s, !greedy && wants_z(kp), kp.c);
   if (st.status != 0) {

@@ -50,6 +50,9 @@ struct Lds {
     uint32_t idx[kWaveCap];         // token ids
   } wc[kWaves];
   int wcnt[kWaves];                 // candidates found by each wavefront
+  int hist[kHistMax];               // the look-back window (-1: not a token of the row)
+  uint32_t hbits[kWave];            // chunks holding a window token, hashed (chunk mod 2048)
+  unsigned long long own[kBlock];   // per thread: window entries in its chunks
   WaveStats ws[kWaves];
   BlockScratch bs;
   int si[8];
@@ -94,9 +97,65 @@ __device__ __forceinline__ uint4 apply_mask(uint4 t, uint32_t bits) {
   return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
+// Repetition penalty of one logit (the CTRL rule): z / r above zero, z * r
+// otherwise, in double, rounded to the row's element type (bf16: nearest
+// even from the float32).
+template <int DT>
+__device__ __forceinline__ float penalize(float z, double r) {
+  float f = (float)(z > 0.0f ? (double)z / r : (double)z * r);
+  if constexpr (DT == 1) {
+    const uint32_t b = __float_as_uint(f);
+    if ((b & 0x7F800000u) != 0x7F800000u)
+      f = __uint_as_float((b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u);
+  }
+  return f;
+}
+// A chunk with the elements flagged in `hit` (bit e: element e) penalised.
+template <int DT>
+__device__ __forceinline__ uint4 penalize_chunk(uint4 t, uint32_t hit, double r) {
+  constexpr int EPC = Fmt<DT>::EPC;
+  float v[EPC];
+  unpack<DT>(t, v);
+#pragma unroll
+  for (int e = 0; e < EPC; ++e)
+    if ((hit >> e) & 1u) v[e] = penalize<DT>(v[e], r);
+  uint32_t x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (DT == 0)
+      x[i] = __float_as_uint(v[i]);
+    else
+      x[i] = (__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xFFFF0000u);
+  }
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 // One LDS instance per translation unit; every kernel of the unit uses it, as
 // do the non-inlined functions of the streaming path.
 static __shared__ Lds tsr_lds;
+
+// The look-back window of the repetition penalty, published by wave 0 (all
+// lanes, lane h holding id hv of the window's first n): L.hist[h] = the id if
+// it is a token of the row, else -1; L.own[t] gets bit h when thread t's
+// chunks hold it (chunk id / EPC mod kBlock); L.hbits flags its chunk, hashed
+// to 2048 bits, for the streaming reads. Repeated ids stay in the list (their
+// users apply each distinct id once). A barrier must follow.
+template <int DT>
+__device__ __forceinline__ void hist_publish(int hv, int n, int V, Lds& L) {
+  constexpr int EPC = Fmt<DT>::EPC;
+  const int lane = __lane_id();
+  const bool in = lane < n && hv >= 0 && hv < V;
+#pragma unroll
+  for (int k = 0; k < kBlock / kWave; ++k) L.own[k * kWave + lane] = 0ull;
+  L.hbits[lane] = 0u;
+  if (lane < n) L.hist[lane] = in ? hv : -1;
+  if (in) {   // (a wavefront's LDS operations complete in order: after the clears)
+    const int c = hv / EPC;
+    atomicOr(&L.own[c % kBlock], 1ull << lane);
+    atomicOr(&L.hbits[(c >> 5) & (kWave - 1)], 1u << (c & 31));
+  }
+}
+
 
 constexpr double kFix = 1099511627776.0;  // 2^40
 constexpr double kInvFix = 1.0 / 1099511627776.0;

@@ -192,6 +192,16 @@ __device__ __forceinline__ float RegRow<DT, NC>::cmax(int j) const {
   else return chunk_max<DT>(get(j));
 }
 
+// The per-row extras of the MASK instances, chosen at run time: the allowed
+// mask (staged in LDS), and the look-back window of the repetition penalty
+// (hn ids, lane h of wave 0 holding id hv; r the penalty).
+struct RowExtras {
+  bool mask = false;
+  int hn = 0;
+  int hv = -1;
+  double r = 1.0;
+};
+
 struct RowStats {
   int status;     // TSR_ROW_*
   float M;        // row max
@@ -210,21 +220,25 @@ struct RowStats {
 // close to the cut.
 // MASK: apply the staged allowed-token mask (stage_mask, V tokens) to each
 // chunk first, and count the allowed tokens (a row with few of them is
-// resolved over all its finite elements).
+// resolved over all its finite elements); then the repetition penalty: wave 0
+// publishes the look-back window (x.hv: lane h's id), and the thread that
+// holds a window token rescales it in its registers and refreshes its maxima.
+// x selects both at run time (MASK instances only).
 template <bool MASK = false, int DT, int NC>
 __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, float c, Lds& L,
-                                              int V = 0) {
+                                              int V = 0, const RowExtras& x = RowExtras{}) {
   float tmax = kNegInf;
-  int nallow = 0;
+  int nallow = 0x7FFFFFFF;
   // thread t's chunk j takes bits tsh.. of mask word j * kWpr + tw; the words
   // of the next two chunk rows are read ahead of their use
   constexpr int kCpw = 32 / Fmt<DT>::EPC;   // chunks per mask word
   constexpr int kWpr = kBlock / kCpw;       // mask words per chunk row
   const int tw = (int)threadIdx.x / kCpw;
   const uint32_t tsh = ((uint32_t)threadIdx.x % kCpw) * Fmt<DT>::EPC;
-  uint32_t mw0 = 0, mw1 = 0;
-  if constexpr (MASK) {
+  uint32_t mw0 = ~0u, mw1 = ~0u;
+  if (MASK && x.mask) {
     // (bits of ids past V in the last word may be set: an over-count)
+    nallow = 0;
     for (int w = threadIdx.x; w < ((V + 31) >> 5); w += kBlock) nallow += __builtin_popcount(L.vmask[w]);
     mw0 = L.vmask[tw];
     if (NC > 1) mw1 = L.vmask[kWpr + tw];
@@ -234,7 +248,7 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
     const uint32_t mwc = mw0;
     if constexpr (MASK) {
       mw0 = mw1;
-      if (j + 2 < NC) mw1 = L.vmask[(j + 2) * kWpr + tw];
+      if (j + 2 < NC && x.mask) mw1 = L.vmask[(j + 2) * kWpr + tw];
     }
     uint4 t = r.get(j);
     asm volatile("" : "+v"(t.x), "+v"(t.y), "+v"(t.z), "+v"(t.w));
@@ -261,6 +275,32 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
     tmax = fmaxn(tmax, m);
     asm volatile("" : "+v"(tmax));
   }
+  if (MASK && x.hn > 0) {
+    if (threadIdx.x < kWave) hist_publish<DT>(x.hv, x.hn, V, L);
+    __syncthreads();
+    unsigned long long om = L.own[threadIdx.x];
+    if (om) {   // this thread's chunks hold window tokens: each distinct one once
+      unsigned long long done = 0ull;
+      while (om) {
+        const int h = __builtin_ctzll(om);
+        om &= om - 1ull;
+        const int id = L.hist[h];
+        bool dup = false;
+        for (unsigned long long d = done; d; d &= d - 1ull) dup |= L.hist[__builtin_ctzll(d)] == id;
+        done |= 1ull << h;
+        if (dup) continue;
+        const int cid = id / Fmt<DT>::EPC;
+        const int j = cid / kBlock;
+        const uint4 t = penalize_chunk<DT>(r.get(j), 1u << (id - cid * Fmt<DT>::EPC), x.r);
+        r.put(j, t);
+        r.put_cmax(j, chunk_max<DT>(t));
+      }
+      float m = kNegInf;
+#pragma unroll
+      for (int j = 0; j < NC; ++j) m = fmaxn(m, r.cmax(j));
+      tmax = m;
+    }
+  }
   r.tmax = tmax;
   // the thread max's own weight, relative to itself
   const double zt = (need_zlo && tmax > kNegInf && tmax < kPosInf) ? 1.0 : 0.0;
@@ -270,7 +310,7 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
   const int wb = 0;
   double wz = 0.0;
   int wna = 0;
-  if constexpr (MASK) wna = wave_sum(nallow);
+  if constexpr (MASK) wna = x.mask ? wave_sum(nallow) : 0x7FFFFFFF;
   if (need_zlo)   // relative to the wave max
     wz = wave_sum(tmax > kNegInf && tmax < kPosInf ? zt * (double)weight(tmax, wm, c) : 0.0);
   const int wid = threadIdx.x / kWave;
@@ -287,7 +327,7 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
     anybad |= L.ws[w].bad;
     na += L.ws[w].na;
   }
-  st.nallow = MASK ? na : 0x7FFFFFFF;
+  st.nallow = (MASK && x.mask) ? na : 0x7FFFFFFF;
   double Z = 0.0;
   if (need_zlo) {
 #pragma unroll

@@ -22,10 +22,13 @@ struct StreamRow {
   int nct;        // chunks per thread
   bool aligned;
   const uint32_t* mask;   // the row's allowed-token words, or null
+  int hn;                 // look-back window entries published in LDS (0: no penalty)
+  double rpen;            // repetition penalty
 
   __device__ __forceinline__ StreamRow(const unsigned char* p_, int V_, bool aligned_,
-                                       const uint32_t* mask_ = nullptr)
-      : p(p_), V(V_), aligned(aligned_), mask(mask_) {
+                                       const uint32_t* mask_ = nullptr, int hn_ = 0,
+                                       double rpen_ = 1.0)
+      : p(p_), V(V_), aligned(aligned_), mask(mask_), hn(hn_), rpen(rpen_) {
     const long long chunks = ((long long)V + EPC - 1) / EPC;
     nct = (int)((chunks + kBlock - 1) / kBlock);
   }
@@ -39,7 +42,19 @@ struct StreamRow {
     const uint4 t = (aligned && (c + 1) * EPC <= V)
                         ? *reinterpret_cast<const uint4*>(p + c * EPC * Fmt<DT>::ESZ)
                         : load_chunk_slow<DT>(p, c, V);
-    return mask ? apply_mask<DT>(t, chunk_mask_bits<DT>(mask, c)) : t;
+    uint4 m = mask ? apply_mask<DT>(t, chunk_mask_bits<DT>(mask, c)) : t;
+    if (hn > 0) {   // window tokens in this chunk (the hashed flag first)
+      const Lds& L = tsr_lds;
+      if ((L.hbits[(c >> 5) & (kWave - 1)] >> (c & 31)) & 1u) {
+        uint32_t hit = 0u;
+        for (int h = 0; h < hn; ++h) {
+          const long long d = (long long)L.hist[h] - c * EPC;
+          hit |= (d >= 0 && d < EPC) ? 1u << (uint32_t)d : 0u;
+        }
+        if (hit) m = penalize_chunk<DT>(m, hit, rpen);
+      }
+    }
+    return m;
   }
   __device__ __forceinline__ void elems(int j, float* v, float* m) const {
     unpack<DT>(chunk(j), v);
