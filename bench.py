@@ -249,6 +249,7 @@ def main():
 
 def run_extra(torch, tsr, wl, steps, warmup):
     """Rows/s and GB/s of the other workloads (same timing method)."""
+    import numpy as np
     res = {}
     with tsr.Sampler(0, max_rows=4096, max_vocab=1 << 18, max_k=8, seed=wl.philox_seed(2)) as s:
         w = wl.config(1)
@@ -312,6 +313,15 @@ def run_extra(torch, tsr, wl, steps, warmup):
                                                                   logprob=lp),
                             steps, warmup)
             res[f"batch256_128256_bf16_chain_mask_{kind}"] = _rates(w.rows, nbytes, ms)
+        # repetition penalty r = 1.1 over a 64-token window per row
+        hist = torch.from_numpy(np.random.default_rng(64).integers(0, w.vocab, (w.rows, 64))
+                                .astype(np.int32)).to("cuda:0")
+        ms = time_calls(torch, lambda i: s.sample_rows_ex(bufs[i % ROTATE], w.runs[0], i,
+                                                          history=hist, penalty=1.1, out=out,
+                                                          logprob=lp),
+                        steps, warmup)
+        res["batch256_128256_bf16_chain_rep64"] = _rates(
+            w.rows, w.rows * w.vocab * 2 + hist.numel() * 4, ms)
         del bufs
 
         w = wl.config(5)

@@ -43,17 +43,19 @@ def instance_units() -> dict[str, str]:
     for dt in (0, 1):
         for nc in ROW_NCS:
             units[f"i_sample_{dt}_{nc}.hip"] = head + (
-                f"template __global__ void sample_kernel<{dt}, {nc}, false, false>(const unsigned "
+                f"template __global__ void sample_kernel<{dt}, {nc}, false, 0>(const unsigned "
                 "char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);\n}\n")
             if dt == 1:   # the register-resident finish for wide kept sets (bf16)
                 units[f"i_sample_wide_{dt}_{nc}.hip"] = head + (
-                    f"template __global__ void sample_kernel<{dt}, {nc}, true, false>(const unsigned "
+                    f"template __global__ void sample_kernel<{dt}, {nc}, true, 0>(const unsigned "
                     "char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);\n}\n")
-            # rows restricted to an allowed-token set (bf16 takes the wide finish as well)
+            # an allowed-token set (1) or a repetition penalty only (2); bf16
+            # takes the wide finish as well
             wide = "true" if dt == 1 else "false"
-            units[f"i_sample_mask_{dt}_{nc}.hip"] = head + (
-                f"template __global__ void sample_kernel<{dt}, {nc}, {wide}, true>(const unsigned "
-                "char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);\n}\n")
+            for ext, tag in ((1, "mask"), (2, "rep")):
+                units[f"i_sample_{tag}_{dt}_{nc}.hip"] = head + (
+                    f"template __global__ void sample_kernel<{dt}, {nc}, {wide}, {ext}>(const "
+                    "unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);\n}\n")
             units[f"i_greedy_{dt}_{nc}.hip"] = head + (
                 f"template __global__ void greedy_kernel<{dt}, {nc}>(const unsigned char*, "
                 "long long, int, int, int, int32_t*, int32_t*);\n}\n")

@@ -27,15 +27,19 @@ constexpr int kVerifyNcs[] = {1, 2, 4, 8, 16};
 // Each kernel instance is compiled in a translation unit of its own (the
 // build generates them), so the units that launch them only declare them.
 #define TSR_DECLARE_ROW(N)                                                                   \
-  extern template __global__ void sample_kernel<0, N, false, false>(                         \
+  extern template __global__ void sample_kernel<0, N, false, 0>(                             \
       const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
-  extern template __global__ void sample_kernel<1, N, false, false>(                         \
+  extern template __global__ void sample_kernel<1, N, false, 0>(                             \
       const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
-  extern template __global__ void sample_kernel<1, N, true, false>(                          \
+  extern template __global__ void sample_kernel<1, N, true, 0>(                              \
       const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
-  extern template __global__ void sample_kernel<0, N, false, true>(                          \
+  extern template __global__ void sample_kernel<0, N, false, 1>(                             \
       const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
-  extern template __global__ void sample_kernel<1, N, true, true>(                           \
+  extern template __global__ void sample_kernel<0, N, false, 2>(                             \
+      const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
+  extern template __global__ void sample_kernel<1, N, true, 2>(                              \
+      const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
+  extern template __global__ void sample_kernel<1, N, true, 1>(                           \
       const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
   extern template __global__ void greedy_kernel<0, N>(const unsigned char*, long long, int,  \
                                                       int, int, int32_t*, int32_t*);          \

@@ -12,15 +12,18 @@ hipError_t launch_sample_dt0(const unsigned char* p, int rows, int V, long long 
                        stride_bytes, V, aligned, kp, out, dg);
     return hipGetLastError();
   }
-  const bool mask = (kp.flags & (F_MASK | F_REP)) != 0;
-#define TSR_CASE(N)                                                                             \
-  case N:                                                                                       \
-    if (mask)                                                                                   \
-      hipLaunchKernelGGL((sample_kernel<0, N, false, true>), dim3(rows), dim3(kBlock), 0, s, p, \
-                         stride_bytes, V, aligned, ragged, kp, out, dg);                        \
-    else                                                                                        \
-      hipLaunchKernelGGL((sample_kernel<0, N, false, false>), dim3(rows), dim3(kBlock), 0, s,  \
-                         p, stride_bytes, V, aligned, ragged, kp, out, dg);                     \
+  const int ext = (kp.flags & F_MASK) ? 1 : (kp.flags & F_REP) ? 2 : 0;
+#define TSR_CASE(N)                                                                            \
+  case N:                                                                                      \
+    if (ext == 1)                                                                              \
+      hipLaunchKernelGGL((sample_kernel<0, N, false, 1>), dim3(rows), dim3(kBlock), 0, s, p,   \
+                         stride_bytes, V, aligned, ragged, kp, out, dg);                       \
+    else if (ext == 2)                                                                         \
+      hipLaunchKernelGGL((sample_kernel<0, N, false, 2>), dim3(rows), dim3(kBlock), 0, s, p,   \
+                         stride_bytes, V, aligned, ragged, kp, out, dg);                       \
+    else                                                                                       \
+      hipLaunchKernelGGL((sample_kernel<0, N, false, 0>), dim3(rows), dim3(kBlock), 0, s, p,   \
+                         stride_bytes, V, aligned, ragged, kp, out, dg);                       \
     break;
   switch (nc) {
     TSR_ROW_NCS(TSR_CASE)

@@ -328,26 +328,24 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel_stream(const unsigned ch
 // ---------------------------------------------------------------- sample_rows
 
 // The streaming view of row `row` (for the streaming finish and the
-// diagnostics), with its allowed-token mask when MASK.
-template <int DT, bool MASK>
+// diagnostics), with the allowed-token mask (EXT 1) and the repetition
+// penalty (EXT 1 or 2, when asked for).
+template <int DT, int EXT>
 __device__ __forceinline__ StreamRow<DT> row_stream_view(const unsigned char* p, int V,
                                                          const KParams& kp, int row) {
-  if constexpr (MASK)
-    return StreamRow<DT>(p, V, true,
-                         (kp.flags & F_MASK) ? kp.allowed + (long long)row * kp.allowed_stride
-                                             : nullptr,
-                         (kp.flags & F_REP) ? kp.hist_len : 0, kp.rpen);
-  else
-    return StreamRow<DT>(p, V, true);
+  return StreamRow<DT>(p, V, true,
+                       EXT == 1 ? kp.allowed + (long long)row * kp.allowed_stride : nullptr,
+                       (EXT != 0 && (kp.flags & F_REP)) ? kp.hist_len : 0, kp.rpen);
 }
 
 // WIDE (bf16): rows whose kept set the candidate bound cannot narrow are
 // finished over the registers (reg_general, then the walk) instead of by the
 // streaming path. A separate instance, chosen on the host for filters without
 // a small top-k, so the common instance keeps its registers and code size.
-// MASK: an allowed-token bitmask applies (constrained decoding), staged in LDS
-// and applied in pass A; its instances are WIDE for bf16.
-template <int DT, int NC, bool WIDE, bool MASK>
+// EXT 1: an allowed-token bitmask applies (constrained decoding), staged in
+// LDS and applied in pass A, and a repetition penalty may (F_REP); EXT 2: a
+// repetition penalty applies. Their bf16 instances are WIDE.
+template <int DT, int NC, bool WIDE, int EXT>
 __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* logits,
                                                         long long stride_bytes, int V,
                                                         int aligned, int ragged, KParams kp,
@@ -356,24 +354,21 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   Lds& L = tsr_lds;
   const int row = blockIdx.x;
   const unsigned char* p = logits + (long long)row * stride_bytes;
+  constexpr bool MASK = EXT == 1, REP = EXT != 0;
   RegRow<DT, NC> r;
   RowExtras x;
-  if constexpr (MASK) {
-    x.mask = (kp.flags & F_MASK) != 0;
-    if (kp.flags & F_REP) {   // the window ids, read by wave 0 before the row
-      x.hn = kp.hist_len;
-      x.r = kp.rpen;
-      if ((int)threadIdx.x < x.hn) x.hv = kp.hist[(long long)row * kp.hist_stride + threadIdx.x];
-    }
-    if (x.mask) stage_mask(kp.allowed + (long long)row * kp.allowed_stride, V, L);
+  if (REP && (kp.flags & F_REP)) {   // the window ids, read by wave 0 before the row
+    x.hn = kp.hist_len;
+    x.r = kp.rpen;
+    x.row = p;
+    if ((int)threadIdx.x < x.hn) x.hv = kp.hist[(long long)row * kp.hist_stride + threadIdx.x];
   }
+  if constexpr (MASK) stage_mask(kp.allowed + (long long)row * kp.allowed_stride, V, L);
   r.load(p, V, ragged != 0);
-  if constexpr (MASK) {
-    if (x.mask) mask_ready<NC>();
-  }
+  if constexpr (MASK) mask_ready<NC>();
   const bool greedy = (kp.flags & F_GREEDY) != 0;
   const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);   // while the loads fly
-  const RowStats st = reg_stats<MASK>(r, !greedy && joint_top_p(kp), kp.c, L, V, x);
+  const RowStats st = reg_stats<MASK, REP>(r, !greedy && joint_top_p(kp), kp.c, L, V, x);
   if (st.status != 0) {
     write_row(row, -1, st.status, 0, kNegInf, 0.0, kNaN, kNaN, out, dg);
     zero_probs(dg, row, V);
@@ -393,7 +388,7 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
     // the cut and the draw; the registers are dead afterwards. Without min-p
     // or a small top-k the WIDE instance goes straight to its register search
     // (no candidate bound can narrow a wide kept set).
-    const bool narrow = f.m_on || (MASK && f.k_on && f.k <= kBlock / 4);
+    const bool narrow = f.m_on || (EXT != 0 && f.k_on && f.k <= kBlock / 4);
     FastOut fo{0, 0, -1, kPosInf, 0, 0.0, 0.0};
     if (!(WIDE && DT == 1) || narrow)
       fo = fast_cut<MASK>(r, V, M, st.tmin, st.zlo, c, f, u, L, st.nallow);
@@ -412,14 +407,14 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
       tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs, &wt);
     } else {
       // the streaming path finishes this row
-      stream_finish(row_stream_view<DT, MASK>(p, V, kp, row), row, M, -1.0, kp, f, u, out, dg);
+      stream_finish(row_stream_view<DT, EXT>(p, V, kp, row), row, M, -1.0, kp, f, u, out, dg);
       return;
     }
   } else {
     tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs, &wt);
   }
   if (dg.kept_count || dg.threshold || dg.kept_mass || dg.probs) {
-    diag_finish(row_stream_view<DT, MASK>(p, V, kp, row), row, tok, kept, tau, M, c, zs, wt, out,
+    diag_finish(row_stream_view<DT, EXT>(p, V, kp, row), row, tok, kept, tau, M, c, zs, wt, out,
                 dg);
     return;
   }

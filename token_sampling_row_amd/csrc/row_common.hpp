@@ -40,6 +40,7 @@ struct Lds {
     };
     uint32_t vcnt[kVCopies * kVStride];   // bf16 value histogram: per-copy counts
     uint32_t vmask[kMaskWords];           // the row's allowed-token bitmask (pass A)
+    unsigned long long own[kBlock];       // per thread: window entries in its chunks (after pass A)
     double jrow[kWalkBatch][kWaves * 4];  // walk: per (chunk row, 16-lane row) sums
   };
   uint32_t hcnt[kBins];             // histogram counts
@@ -51,8 +52,8 @@ struct Lds {
   } wc[kWaves];
   int wcnt[kWaves];                 // candidates found by each wavefront
   int hist[kHistMax];               // the look-back window (-1: not a token of the row)
+  float hval[kHistMax];             // its penalised logits (register path)
   uint32_t hbits[kWave];            // chunks holding a window token, hashed (chunk mod 2048)
-  unsigned long long own[kBlock];   // per thread: window entries in its chunks
   WaveStats ws[kWaves];
   BlockScratch bs;
   int si[8];
@@ -109,6 +110,34 @@ __device__ __forceinline__ float penalize(float z, double r) {
       f = __uint_as_float((b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u);
   }
   return f;
+}
+// Element i of a row (exact float value).
+template <int DT>
+__device__ __forceinline__ float load_elem(const unsigned char* p, int i) {
+  if constexpr (DT == 0)
+    return reinterpret_cast<const float*>(p)[i];
+  else
+    return __uint_as_float((uint32_t)reinterpret_cast<const unsigned short*>(p)[i] << 16);
+}
+// A chunk with element e replaced by the value v, unless that element is
+// -inf (a masked-out token: it stays out; an allowed -inf penalises to -inf).
+template <int DT>
+__device__ __forceinline__ uint4 replace_elem(uint4 t, int e, float v) {
+  constexpr int EPC = Fmt<DT>::EPC;
+  float w[EPC];
+  unpack<DT>(t, w);
+#pragma unroll
+  for (int q = 0; q < EPC; ++q)
+    if (q == e && w[q] != kNegInf) w[q] = v;
+  uint32_t x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (DT == 0)
+      x[i] = __float_as_uint(w[i]);
+    else
+      x[i] = (__float_as_uint(w[2 * i]) >> 16) | (__float_as_uint(w[2 * i + 1]) & 0xFFFF0000u);
+  }
+  return make_uint4(x[0], x[1], x[2], x[3]);
 }
 // A chunk with the elements flagged in `hit` (bit e: element e) penalised.
 template <int DT>

@@ -192,14 +192,13 @@ __device__ __forceinline__ float RegRow<DT, NC>::cmax(int j) const {
   else return chunk_max<DT>(get(j));
 }
 
-// The per-row extras of the MASK instances, chosen at run time: the allowed
-// mask (staged in LDS), and the look-back window of the repetition penalty
-// (hn ids, lane h of wave 0 holding id hv; r the penalty).
+// The per-row look-back window of the repetition penalty (hn ids, lane h of
+// wave 0 holding id hv; r the penalty), chosen at run time.
 struct RowExtras {
-  bool mask = false;
   int hn = 0;
   int hv = -1;
   double r = 1.0;
+  const unsigned char* row = nullptr;   // the row's logits (window values are read back)
 };
 
 struct RowStats {
@@ -220,40 +219,38 @@ struct RowStats {
 // close to the cut.
 // MASK: apply the staged allowed-token mask (stage_mask, V tokens) to each
 // chunk first, and count the allowed tokens (a row with few of them is
-// resolved over all its finite elements); then the repetition penalty: wave 0
-// publishes the look-back window (x.hv: lane h's id), and the thread that
-// holds a window token rescales it in its registers and refreshes its maxima.
-// x selects both at run time (MASK instances only).
-template <bool MASK = false, int DT, int NC>
-__device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, float c, Lds& L,
-                                              int V = 0, const RowExtras& x = RowExtras{}) {
+// resolved over all its finite elements). Then, when x holds a look-back
+// window, the repetition penalty: wave 0 reads the window tokens' logits back
+// and publishes their penalised values, and the thread that holds a window
+// token puts its new value in place and refreshes its maxima (REP instances).
+// Pass A over the registers as the loads land (see reg_stats); MASKED: the
+// staged allowed-token mask is applied to each chunk first. Returns the
+// thread's maximum.
+template <bool MASKED, int DT, int NC>
+__device__ __forceinline__ float reg_pass_a(RegRow<DT, NC>& r, const Lds& L) {
   float tmax = kNegInf;
-  int nallow = 0x7FFFFFFF;
   // thread t's chunk j takes bits tsh.. of mask word j * kWpr + tw; the words
   // of the next two chunk rows are read ahead of their use
   constexpr int kCpw = 32 / Fmt<DT>::EPC;   // chunks per mask word
   constexpr int kWpr = kBlock / kCpw;       // mask words per chunk row
   const int tw = (int)threadIdx.x / kCpw;
   const uint32_t tsh = ((uint32_t)threadIdx.x % kCpw) * Fmt<DT>::EPC;
-  uint32_t mw0 = ~0u, mw1 = ~0u;
-  if (MASK && x.mask) {
-    // (bits of ids past V in the last word may be set: an over-count)
-    nallow = 0;
-    for (int w = threadIdx.x; w < ((V + 31) >> 5); w += kBlock) nallow += __builtin_popcount(L.vmask[w]);
+  uint32_t mw0 = 0u, mw1 = 0u;
+  if constexpr (MASKED) {
     mw0 = L.vmask[tw];
     if (NC > 1) mw1 = L.vmask[kWpr + tw];
   }
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     const uint32_t mwc = mw0;
-    if constexpr (MASK) {
+    if constexpr (MASKED) {
       mw0 = mw1;
-      if (j + 2 < NC && x.mask) mw1 = L.vmask[(j + 2) * kWpr + tw];
+      if (j + 2 < NC) mw1 = L.vmask[(j + 2) * kWpr + tw];
     }
     uint4 t = r.get(j);
     asm volatile("" : "+v"(t.x), "+v"(t.y), "+v"(t.z), "+v"(t.w));
     t = r.settle(j, t);
-    if constexpr (MASK) {
+    if constexpr (MASKED) {
       // element-wise masking only where some lane's chunk is partly allowed;
       // wholly allowed or wholly disallowed chunks (the common case of a
       // grammar's small or near-complete sets) take one select per dword
@@ -275,23 +272,40 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
     tmax = fmaxn(tmax, m);
     asm volatile("" : "+v"(tmax));
   }
-  if (MASK && x.hn > 0) {
-    if (threadIdx.x < kWave) hist_publish<DT>(x.hv, x.hn, V, L);
+  return tmax;
+}
+
+template <bool MASK = false, bool REP = false, int DT, int NC>
+__device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, float c, Lds& L,
+                                              int V = 0, const RowExtras& x = RowExtras{}) {
+  int nallow = 0x7FFFFFFF;
+  if constexpr (MASK) {
+    // (bits of ids past V in the last word may be set: an over-count)
+    nallow = 0;
+    for (int w = threadIdx.x; w < ((V + 31) >> 5); w += kBlock) nallow += __builtin_popcount(L.vmask[w]);
+  }
+  float tmax = reg_pass_a<MASK>(r, L);
+  if (REP && x.hn > 0) {
+    if constexpr (MASK) __syncthreads();   // L.own shares LDS with the mask words
+    if (threadIdx.x < kWave) {
+      // wave 0: each window token's logit, read back from the row (one per
+      // lane, in parallel) and penalised once here
+      const bool in = (int)threadIdx.x < x.hn && x.hv >= 0 && x.hv < V;
+      if (in) L.hval[threadIdx.x] = penalize<DT>(load_elem<DT>(x.row, x.hv), x.r);
+      hist_publish<DT>(x.hv, x.hn, V, L);
+    }
     __syncthreads();
     unsigned long long om = L.own[threadIdx.x];
-    if (om) {   // this thread's chunks hold window tokens: each distinct one once
-      unsigned long long done = 0ull;
+    if (om) {   // this thread's chunks hold window tokens: put their penalised
+                // values in place (a repeated id writes the same value again);
+                // a masked-out token stays -inf
       while (om) {
         const int h = __builtin_ctzll(om);
         om &= om - 1ull;
         const int id = L.hist[h];
-        bool dup = false;
-        for (unsigned long long d = done; d; d &= d - 1ull) dup |= L.hist[__builtin_ctzll(d)] == id;
-        done |= 1ull << h;
-        if (dup) continue;
         const int cid = id / Fmt<DT>::EPC;
         const int j = cid / kBlock;
-        const uint4 t = penalize_chunk<DT>(r.get(j), 1u << (id - cid * Fmt<DT>::EPC), x.r);
+        const uint4 t = replace_elem<DT>(r.get(j), id - cid * Fmt<DT>::EPC, L.hval[h]);
         r.put(j, t);
         r.put_cmax(j, chunk_max<DT>(t));
       }
@@ -310,7 +324,7 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
   const int wb = 0;
   double wz = 0.0;
   int wna = 0;
-  if constexpr (MASK) wna = x.mask ? wave_sum(nallow) : 0x7FFFFFFF;
+  if constexpr (MASK) wna = wave_sum(nallow);
   if (need_zlo)   // relative to the wave max
     wz = wave_sum(tmax > kNegInf && tmax < kPosInf ? zt * (double)weight(tmax, wm, c) : 0.0);
   const int wid = threadIdx.x / kWave;
@@ -327,7 +341,7 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
     anybad |= L.ws[w].bad;
     na += L.ws[w].na;
   }
-  st.nallow = (MASK && x.mask) ? na : 0x7FFFFFFF;
+  st.nallow = MASK ? na : 0x7FFFFFFF;
   double Z = 0.0;
   if (need_zlo) {
 #pragma unroll
