@@ -175,7 +175,7 @@ def main():
         # the headline launches the common instance (third template argument false)
         label = row_kernel_label(w3.dtype, w3.vocab).replace('bf16', '1').replace('f32', '0')
         print(json.dumps(write_traffic(*args.write_traffic, "batch256_128256_bf16",
-                                       f"tsr::{label[:-1]}, false>")))
+                                       f"tsr::{label[:-1]}, false, 0>")))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
