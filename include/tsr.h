@@ -222,6 +222,30 @@ int spec_verify(tsr_handle h, const void* target_logits, const void* draft_logit
                 const tsr_params* params, uint64_t step, int32_t* out_tokens,
                 int32_t* out_accepted, int32_t* out_status, void* hip_stream);
 
+/* One beam-search step [P2 39.1: eq. 39.1, Listing 39.1; P4 "Beam search"]
+ * for `groups` independent searches of `beam` beams each (no length penalty
+ * or end token, as in the listing).
+ *  logits [groups * beam][vocab]: row g * beam + b holds beam b of group g,
+ *      row_stride elements apart (vocab beyond 155,648 bf16 or 77,824
+ *      float32 logits: TSR_EUNSUPPORTED).
+ *  beam_scores [groups * beam] double: each beam's running score s_b, the sum
+ *      of its tokens' log-probabilities (eq. 39.1); -inf marks a dead beam.
+ * Every candidate (b, i) scores s_b + log softmax(logits_b)_i (temperature
+ * 1, the row's own normalisation, so a row without a finite logit adds
+ * nothing); the `beam` best of the group's beam * vocab candidates are kept,
+ * best first, equal scores in the order (b, then i) ascending.
+ *  out_parent [groups * beam] int32: the beam (0..beam-1) each kept candidate
+ *      extends; out_token the token; out_score (double) its score. Positions
+ *      past the group's finite candidates hold -1, -1, -inf.
+ *  out_status [groups] (nullable): TSR_ROW_OK; TSR_ROW_NONFINITE when a NaN or
+ *      +inf logit or score is in the group (outputs -1, -1, NaN);
+ *      TSR_ROW_EMPTY when no candidate is finite.
+ * 1 <= beam <= 16 and groups * beam <= max_rows (TSR_EINVAL otherwise). Uses
+ * per-handle workspace: not concurrent with another beam_step on the handle. */
+int beam_step(tsr_handle h, const void* logits, int dtype, int groups, int beam, int vocab,
+              int64_t row_stride, const double* beam_scores, int32_t* out_parent,
+              int32_t* out_token, double* out_score, int32_t* out_status, void* hip_stream);
+
 /* Test hook: out_words[i][0..3] = Philox4x32-10(counters[i][0..3], key = the
  * handle's seed) for i < n, computed on the device by the same function the
  * sampler uses. counters and out_words are device memory. */

@@ -22,8 +22,8 @@ F32, BF16 = 0, 1
 JOINT, SEQUENTIAL = 0, 1
 ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BADTOKEN = 0, 1, 2, 3
 EXPORTED_SYMBOLS = ("sampler_init", "sampler_destroy", "greedy_argmax", "sample_rows",
-                    "sample_rows_masked", "sample_rows_ex", "spec_verify", "sampler_philox",
-                    "sampler_strerror")
+                    "sample_rows_masked", "sample_rows_ex", "spec_verify", "beam_step",
+                    "sampler_philox", "sampler_strerror")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -86,6 +86,7 @@ def load_library():
                                    vp]
     lib.spec_verify.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, ctypes.POINTER(_Params),
                                 u64, vp, vp, vp, vp]
+    lib.beam_step.argtypes = [vp, vp, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp]
     lib.sampler_philox.argtypes = [vp, vp, i32, vp, vp]
     lib.sampler_strerror.argtypes = [i32]
     lib.sampler_strerror.restype = ctypes.c_char_p
@@ -282,6 +283,25 @@ class Sampler:
                                           _ptr(out_accepted), _ptr(out_status),
                                           _stream_ptr(stream)), "spec_verify")
         return out_tokens, out_accepted
+
+    def beam_step(self, logits, beam_scores, beam: int, status=None, stream=None):
+        """logits [groups * beam, V] device tensor (row g * beam + b: beam b
+        of group g), beam_scores [groups * beam] float64 device tensor ->
+        (parent, token, score), each [groups, beam], best first."""
+        import torch
+        rows, vocab = logits.shape
+        assert logits.stride(1) == 1 and rows % beam == 0
+        assert beam_scores.dtype == torch.float64 and beam_scores.is_contiguous()
+        groups = rows // beam
+        dev = logits.device
+        parent = torch.empty(groups, beam, dtype=torch.int32, device=dev)
+        token = torch.empty(groups, beam, dtype=torch.int32, device=dev)
+        score = torch.empty(groups, beam, dtype=torch.float64, device=dev)
+        _check(load_library().beam_step(self._h, _ptr(logits), _dtype_code(logits), groups, beam,
+                                        vocab, logits.stride(0), _ptr(beam_scores), _ptr(parent),
+                                        _ptr(token), _ptr(score), _ptr(status),
+                                        _stream_ptr(stream)), "beam_step")
+        return parent, token, score
 
     def philox(self, counters, stream=None):
         """counters: [n, 4] int32/uint32 device tensor -> [n, 4] words (int32 view)."""

@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libtsr.so")
 ARCH = os.environ.get("TSR_OFFLOAD_ARCH", "gfx950")
 ROW_NCS = (1, 2, 4, 8, 16, 24, 32, 38)      # must match kRowNcs in dispatch.hpp
 VERIFY_NCS = (1, 2, 4, 8, 16)               # must match kVerifyNcs
-DISPATCH = ["k_greedy.hip", "k_sample_f32.hip", "k_sample_bf16.hip", "k_verify_f32.hip",
+DISPATCH = ["k_greedy.hip", "k_beam.hip", "k_sample_f32.hip", "k_sample_bf16.hip", "k_verify_f32.hip",
             "k_verify_bf16.hip", "k_misc.hip", "api.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
          # no packed fp32 instructions (v_pk_add/mul/fma_f32) anywhere
@@ -56,6 +56,10 @@ def instance_units() -> dict[str, str]:
                 units[f"i_sample_{tag}_{dt}_{nc}.hip"] = head + (
                     f"template __global__ void sample_kernel<{dt}, {nc}, {wide}, {ext}>(const "
                     "unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);\n}\n")
+            units[f"i_beam_{dt}_{nc}.hip"] = head + (
+                f"template __global__ void beam_kernel<{dt}, {nc}>(const unsigned char*, long long, "
+                "int, int, int, int, const double*, BeamWs, int32_t*, int32_t*, double*, "
+                "int32_t*);\n}\n")
             units[f"i_greedy_{dt}_{nc}.hip"] = head + (
                 f"template __global__ void greedy_kernel<{dt}, {nc}>(const unsigned char*, "
                 "long long, int, int, int, int32_t*, int32_t*);\n}\n")

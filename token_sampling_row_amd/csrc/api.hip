@@ -16,6 +16,7 @@ struct tsr_ctx {
   int max_k;
   uint64_t seed;
   tsr::VerifyWs ws;
+  tsr::BeamWs bws;
   void* ws_block;
 };
 
@@ -116,7 +117,10 @@ int sampler_init(tsr_handle* out, int device, int max_rows, int max_vocab, int m
   h->seed = seed;
   const int rc = on_device(device, [&]() -> int {
     const size_t slots = (size_t)max_rows * (size_t)(max_k + 1);
-    const size_t bytes = 4 * slots * sizeof(int32_t) + (size_t)max_rows * sizeof(uint32_t);
+    const size_t vbytes = 4 * slots * sizeof(int32_t) + (size_t)max_rows * sizeof(uint32_t);
+    const size_t bslots = (size_t)max_rows * tsr::kBeamMax;
+    const size_t bytes = ((vbytes + 7) & ~(size_t)7) + bslots * (sizeof(double) + sizeof(int32_t)) +
+                         2 * (size_t)max_rows * sizeof(uint32_t);
     if (hipMalloc(&h->ws_block, bytes) != hipSuccess) return TSR_ENOMEM;
     if (hipMemset(h->ws_block, 0, bytes) != hipSuccess) return TSR_EDEVICE;
     if (hipDeviceSynchronize() != hipSuccess) return TSR_EDEVICE;
@@ -127,6 +131,12 @@ int sampler_init(tsr_handle* out, int device, int max_rows, int max_vocab, int m
     h->ws.st_d = base + 3 * slots;
     h->ws.counter = (uint32_t*)(base + 4 * slots);
     h->ws.kmax1 = max_k + 1;
+    // beam step: per row kBeamMax (score, token), per group a flag and a counter
+    char* bb = (char*)h->ws_block + ((vbytes + 7) & ~(size_t)7);
+    h->bws.score = (double*)bb;
+    h->bws.tok = (int32_t*)(bb + bslots * sizeof(double));
+    h->bws.bad = (uint32_t*)(bb + bslots * (sizeof(double) + sizeof(int32_t)));
+    h->bws.counter = h->bws.bad + max_rows;
     return TSR_OK;
   });
   if (rc != TSR_OK) {
@@ -269,6 +279,28 @@ int spec_verify(tsr_handle h, const void* target_logits, const void* draft_logit
     const hipError_t e = tsr::launch_verify(target_logits, draft_logits, dtype, draft_tokens,
                                             rows, K, vocab, aligned, ragged, kp, h->ws, out_tokens,
                                             out_accepted, out_status, (hipStream_t)hip_stream);
+    return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
+  });
+}
+
+int beam_step(tsr_handle h, const void* logits, int dtype, int groups, int beam, int vocab,
+              int64_t row_stride, const double* beam_scores, int32_t* out_parent,
+              int32_t* out_token, double* out_score, int32_t* out_status, void* hip_stream) {
+  if (!h || !logits || !beam_scores || !out_parent || !out_token || !out_score) return TSR_EINVAL;
+  if (dtype != TSR_F32 && dtype != TSR_BF16) return TSR_EINVAL;
+  if (beam < 1 || beam > tsr::kBeamMax || groups < 0) return TSR_EINVAL;
+  if ((int64_t)groups * beam > h->max_rows || vocab < 1 || vocab > h->max_vocab) return TSR_EINVAL;
+  if (row_stride < vocab || !elem_aligned(logits, dtype) || ((uintptr_t)beam_scores % 8) != 0)
+    return TSR_EINVAL;
+  if (vocab > tsr::max_vocab_beam(dtype)) return TSR_EUNSUPPORTED;
+  const long long sb = (long long)row_stride * esize(dtype);
+  if (groups == 0) return TSR_OK;
+  const int aligned = ((uintptr_t)logits % 16 == 0) && (sb % 16 == 0);
+  const int ragged = !aligned || (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;
+  return on_device(h->device, [&]() -> int {
+    const hipError_t e = tsr::launch_beam(logits, dtype, groups, beam, vocab, sb, aligned, ragged,
+                                          beam_scores, h->bws, out_parent, out_token, out_score,
+                                          out_status, (hipStream_t)hip_stream);
     return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
   });
 }

@@ -53,6 +53,17 @@ struct DiagPtrs {
   float* logprob;   // log p~ of the drawn token
 };
 
+// Per-handle workspace of the beam step: each beam row's best candidates,
+// best first (score, token), kBeamMax per row; per group a bad-input flag and
+// an arrival counter (both zero between calls).
+constexpr int kBeamMax = 16;
+struct BeamWs {
+  double* score;
+  int32_t* tok;
+  uint32_t* bad;
+  uint32_t* counter;
+};
+
 // Per-handle workspace of the verify step: per (sequence, position) results
 // and one arrival counter per sequence (zero between calls).
 struct VerifyWs {
@@ -78,6 +89,11 @@ hipError_t launch_verify(const void* tgt, const void* dft, int dtype, const int3
                          int rows, int K, int V, int aligned, int ragged, const KParams& kp,
                          const VerifyWs& ws, int32_t* out_tokens, int32_t* out_acc,
                          int32_t* out_status, hipStream_t s);
+hipError_t launch_beam(const void* logits, int dtype, int groups, int beam, int V,
+                       long long stride_bytes, int aligned, int ragged, const double* scores, BeamWs ws,
+                       int32_t* out_parent, int32_t* out_tok, double* out_score,
+                       int32_t* out_status, hipStream_t s);
+int max_vocab_beam(int dtype);
 hipError_t launch_philox(const uint32_t* ctr, int n, uint32_t k0, uint32_t k1, uint32_t* out,
                          hipStream_t s);
 

@@ -458,6 +458,190 @@ __global__ __launch_bounds__(kBlock) void sample_kernel_stream(const unsigned ch
   stream_finish(s, row, st.M, st.z, kp, f, u, out, dg);
 }
 
+// ---------------------------------------------------------------- beam step
+
+// The k (<= kBeamMax) largest finite logits of a register-resident row, lowest
+// id first among equals, as order keys fkey(v) << 32 | ~id in L.key[0, n),
+// descending; returns n = min(k, finite elements). The top-k sketch bounds the
+// candidates; up to one wavefront's worth are sorted in registers, up to kCap
+// in LDS; beyond that (a tie group of thousands at the boundary) k rounds of a
+// block-wide maximum below the previous key.
+template <int DT, int NC>
+__device__ __noinline__ int reg_top_keys(const RegRow<DT, NC>& r, float M, float tmin, int k,
+                                         Lds& L) {
+  constexpr int EPC = Fmt<DT>::EPC;
+  const int tid = threadIdx.x, lane = __lane_id(), wid = tid / kWave;
+  float Lb = topk_sketch(r, M, tmin, k, L);
+  if (!(Lb > -kFltMax)) Lb = -kFltMax;   // fewer than k maxima: every finite element
+  __syncthreads();
+  wave_compact(r, Lb, L);
+  __syncthreads();
+  const int total = wave_regions_total(L);
+  if (total <= kWaveCap) {
+    if (tid < kWave) {
+      int n = 0, sq = 0, so = 0;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) {
+        const int cq = L.wcnt[q];
+        if (lane >= n && lane < n + cq) {
+          sq = q;
+          so = lane - n;
+        }
+        n += cq;
+      }
+      unsigned long long key = 0ull;
+      if (lane < n) key = cand_key(__uint_as_float(L.wc[sq].val[so]), (int)L.wc[sq].idx[so]);
+      key = wave_sort_desc<kWave>(key);
+      if (lane < k) L.key[lane] = key;
+    }
+    __syncthreads();
+    return total < k ? total : k;
+  }
+  // one thread's candidates >= Lb, counted, then compacted in thread order
+  const unsigned long long cmask = wave_chunk_mask<NC>([&](int j) { return r.cmax(j) >= Lb; });
+  int cnt = 0;
+  for (unsigned long long m = cmask; m;) {
+    const int j = pop_low(m);
+    float v[EPC];
+    r.elems(j, v);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) cnt += (v[e] >= Lb) ? 1 : 0;
+  }
+  int all;
+  int off = block_excl_scan<kBlock>(cnt, &all, L.bs);
+  if (all <= kCap) {
+    for (unsigned long long m = __any(cnt != 0) ? cmask : 0ull; m;) {
+      const int j = pop_low(m);
+      float v[EPC];
+      r.elems(j, v);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e)
+        if (v[e] >= Lb) L.key[off++] = cand_key(v[e], r.base(j) + e);
+    }
+    __syncthreads();
+    sort_keys_desc(L, all);
+    return all < k ? all : k;
+  }
+  unsigned long long prev = ~0ull;
+  int n = 0;
+  for (; n < k; ++n) {
+    unsigned long long best = 0ull;
+    for (unsigned long long m = cmask; m;) {
+      const int j = pop_low(m);
+      float v[EPC];
+      r.elems(j, v);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const unsigned long long key = cand_key(v[e], r.base(j) + e);
+        if (v[e] >= Lb && key < prev && key > best) best = key;
+      }
+    }
+    best = wave_reduce(best, [](unsigned long long a, unsigned long long b) { return a > b ? a : b; });
+    __syncthreads();
+    if (lane == 0) L.hmass[wid] = best;   // (histogram masses: free here)
+    __syncthreads();
+    best = 0ull;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) best = L.hmass[q] > best ? L.hmass[q] : best;
+    if (best == 0ull) break;
+    __syncthreads();
+    if (tid == 0) L.key[n] = best;
+    prev = best;
+  }
+  __syncthreads();
+  return n;
+}
+
+// One beam-search step [P2 39.1, eq. 39.1 and Listing 39.1]: workgroup row =
+// g * beam + b holds beam b of group g. It writes its best candidates
+// (score s_b + log p_b(i), token), best first, to the workspace; the last of
+// the group's workgroups to arrive merges the beam sorted lists (equal scores:
+// lower b first) and writes the group's output.
+template <int DT, int NC>
+__global__ __launch_bounds__(kBlock) void beam_kernel(const unsigned char* logits,
+                                                      long long stride_bytes, int V, int aligned,
+                                                      int ragged, int beam, const double* scores,
+                                                      BeamWs ws, int32_t* out_parent,
+                                                      int32_t* out_tok, double* out_score,
+                                                      int32_t* out_status) {
+  Lds& L = tsr_lds;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x, g = row / beam;
+  const unsigned char* p = logits + (long long)row * stride_bytes;
+  RegRow<DT, NC> r;
+  if (aligned)
+    r.load(p, V, ragged != 0);
+  else
+    r.template load<true>(p, V, true);
+  const double sb = scores[row];
+  const RowStats st = reg_stats(r, false, kLog2e, L);
+  const bool bad = st.status == 1 || sb != sb || sb == (double)kPosInf;
+  int n = 0;
+  double lnz = 0.0;
+  if (!bad && st.status == 0 && sb > (double)kNegInf) {
+    lnz = log(reg_weight_sum(r, st.M, kLog2e, L));
+    n = reg_top_keys(r, st.M, st.tmin, beam, L);
+  }
+  if (tid < beam) {
+    double sc = (double)kNegInf;
+    int tk = -1;
+    if (tid < n) {
+      const unsigned long long key = L.key[tid];
+      sc = sb + ((double)key2f(key_hi(key)) - (double)st.M) - lnz;
+      tk = (int)~(uint32_t)key;
+    }
+    const long long slot = (long long)row * kBeamMax + tid;
+    __hip_atomic_store(&ws.score[slot], sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ws.tok[slot], tk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  }
+  if (tid == 0 && bad) __hip_atomic_fetch_or(&ws.bad[g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&ws.counter[g], 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    L.si[0] = prev == (uint32_t)(beam - 1);
+  }
+  __syncthreads();
+  if (!L.si[0] || tid >= kWave) return;
+  // the group's last workgroup, wave 0: lane b < beam walks beam b's list
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int lane = tid;
+  const long long base = (long long)g * beam * kBeamMax;
+  int ptr = 0;
+  auto head = [&](int q) -> double {
+    return (lane < beam && q < beam)
+               ? __hip_atomic_load(&ws.score[base + (long long)lane * kBeamMax + q],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+               : (double)kNegInf;
+  };
+  double hs = head(0);
+  const bool gbad = __hip_atomic_load(&ws.bad[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+  int any_finite = 0;
+  for (int q = 0; q < beam; ++q) {
+    const double best = wave_reduce(hs, [](double a, double b) { return a > b ? a : b; });
+    const int w = __ffsll((long long)__ballot(lane < beam && hs == best)) - 1;
+    const long long o = (long long)g * beam + q;
+    if (lane == w) {
+      const bool fin = best > (double)kNegInf;
+      const int tk = fin ? __hip_atomic_load(&ws.tok[base + (long long)w * kBeamMax + ptr],
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : -1;
+      out_parent[o] = gbad ? -1 : (fin ? w : -1);
+      out_tok[o] = gbad ? -1 : tk;
+      out_score[o] = gbad ? __builtin_nan("") : best;
+      ++ptr;
+      hs = head(ptr);
+    }
+    any_finite |= best > (double)kNegInf;
+  }
+  if (lane == 0) {
+    if (out_status) out_status[g] = gbad ? 1 : (any_finite ? 0 : 2);
+    __hip_atomic_store(&ws.bad[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ws.counter[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // ---------------------------------------------------------------- verify
 
 // Residual weights max(0, p~ - q~) of one verify position (eq. 39.4), both
