@@ -324,6 +324,14 @@ def run_extra(torch, tsr, wl, steps, warmup):
             w.rows, w.rows * w.vocab * 2 + hist.numel() * 4, ms)
         del bufs
 
+        # beam-search step: 64 groups of 4 beams over the same 256 x 128256 bf16 logits
+        w = wl.config(3)
+        bufs = device_batch(torch, w, ROTATE)
+        bsc = torch.from_numpy(np.random.default_rng(4).normal(-5.0, 2.0, w.rows)).to("cuda:0")
+        ms = time_calls(torch, lambda i: s.beam_step(bufs[i % ROTATE], bsc, 4), steps, warmup)
+        res["beam64x4_128256_bf16"] = _rates(w.rows, w.rows * w.vocab * 2, ms)
+        del bufs
+
         w = wl.config(5)
         bufs = device_batch(torch, w, 2)          # 2 x 311 MB already exceeds the 256 MB cache
         out = torch.empty(w.rows, dtype=torch.int32, device="cuda:0")

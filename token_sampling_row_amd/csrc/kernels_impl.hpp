@@ -467,7 +467,7 @@ __global__ __launch_bounds__(kBlock) void sample_kernel_stream(const unsigned ch
 // in LDS; beyond that (a tie group of thousands at the boundary) k rounds of a
 // block-wide maximum below the previous key.
 template <int DT, int NC>
-__device__ __noinline__ int reg_top_keys(const RegRow<DT, NC>& r, float M, float tmin, int k,
+__device__ __forceinline__ int reg_top_keys(const RegRow<DT, NC>& r, float M, float tmin, int k,
                                          Lds& L) {
   constexpr int EPC = Fmt<DT>::EPC;
   const int tid = threadIdx.x, lane = __lane_id(), wid = tid / kWave;
@@ -574,12 +574,13 @@ __global__ __launch_bounds__(kBlock) void beam_kernel(const unsigned char* logit
   else
     r.template load<true>(p, V, true);
   const double sb = scores[row];
-  const RowStats st = reg_stats(r, false, kLog2e, L);
+  // the row's weight sum Z is formed as the chunks land (log p = v - M - ln Z)
+  const RowStats st = reg_stats<false, false, true>(r, true, kLog2e, L);
   const bool bad = st.status == 1 || sb != sb || sb == (double)kPosInf;
   int n = 0;
   double lnz = 0.0;
   if (!bad && st.status == 0 && sb > (double)kNegInf) {
-    lnz = log(reg_weight_sum(r, st.M, kLog2e, L));
+    lnz = log(st.zlo);
     n = reg_top_keys(r, st.M, st.tmin, beam, L);
   }
   if (tid < beam) {
@@ -604,16 +605,19 @@ __global__ __launch_bounds__(kBlock) void beam_kernel(const unsigned char* logit
   }
   __syncthreads();
   if (!L.si[0] || tid >= kWave) return;
-  // the group's last workgroup, wave 0: lane b < beam walks beam b's list
+  // the group's last workgroup, wave 0: the beam lists into LDS at once (one
+  // round trip), then lane b < beam walks beam b's list
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const int lane = tid;
   const long long base = (long long)g * beam * kBeamMax;
+  for (int q = lane; q < beam * kBeamMax; q += kWave) {
+    L.pref[q] = __hip_atomic_load(&ws.score[base + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    L.hcnt[q] = (uint32_t)__hip_atomic_load(&ws.tok[base + q], __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+  }
   int ptr = 0;
   auto head = [&](int q) -> double {
-    return (lane < beam && q < beam)
-               ? __hip_atomic_load(&ws.score[base + (long long)lane * kBeamMax + q],
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-               : (double)kNegInf;
+    return (lane < beam && q < beam) ? L.pref[lane * kBeamMax + q] : (double)kNegInf;
   };
   double hs = head(0);
   const bool gbad = __hip_atomic_load(&ws.bad[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
@@ -624,9 +628,7 @@ __global__ __launch_bounds__(kBlock) void beam_kernel(const unsigned char* logit
     const long long o = (long long)g * beam + q;
     if (lane == w) {
       const bool fin = best > (double)kNegInf;
-      const int tk = fin ? __hip_atomic_load(&ws.tok[base + (long long)w * kBeamMax + ptr],
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                         : -1;
+      const int tk = fin ? (int)L.hcnt[w * kBeamMax + ptr] : -1;
       out_parent[o] = gbad ? -1 : (fin ? w : -1);
       out_tok[o] = gbad ? -1 : tk;
       out_score[o] = gbad ? __builtin_nan("") : best;

@@ -226,9 +226,14 @@ struct RowStats {
 // Pass A over the registers as the loads land (see reg_stats); MASKED: the
 // staged allowed-token mask is applied to each chunk first. Returns the
 // thread's maximum.
-template <bool MASKED, int DT, int NC>
-__device__ __forceinline__ float reg_pass_a(RegRow<DT, NC>& r, const Lds& L) {
+// ONLINE: also the thread's weight sum relative to its own maximum, formed as
+// the chunks land (the running sum is rescaled whenever the running maximum
+// grows), in *z; c = log2(e) / T.
+template <bool MASKED, bool ONLINE = false, int DT, int NC>
+__device__ __forceinline__ float reg_pass_a(RegRow<DT, NC>& r, const Lds& L, float c = 0.0f,
+                                            double* z = nullptr) {
   float tmax = kNegInf;
+  double zr = 0.0;
   // thread t's chunk j takes bits tsh.. of mask word j * kWpr + tw; the words
   // of the next two chunk rows are read ahead of their use
   constexpr int kCpw = 32 / Fmt<DT>::EPC;   // chunks per mask word
@@ -269,13 +274,28 @@ __device__ __forceinline__ float reg_pass_a(RegRow<DT, NC>& r, const Lds& L) {
     r.put(j, t);
     const float m = chunk_max<DT>(t);
     r.put_cmax(j, m);
+    if constexpr (ONLINE) {
+      const float mn = fmaxn(tmax, m);
+      if (mn > kNegInf) {
+        zr = tmax > kNegInf ? zr * (double)weight(tmax, mn, c) : 0.0;
+        float v[Fmt<DT>::EPC];
+        unpack<DT>(t, v);
+        float sw = 0.0f;
+#pragma unroll
+        for (int e = 0; e < Fmt<DT>::EPC; ++e) sw += weight(v[e], mn, c);
+        zr += (double)sw;
+      }
+    }
     tmax = fmaxn(tmax, m);
     asm volatile("" : "+v"(tmax));
   }
+  if constexpr (ONLINE) *z = zr;
   return tmax;
 }
 
-template <bool MASK = false, bool REP = false, int DT, int NC>
+// ZEXACT: need_zlo's sum is the exact Z (every element's weight, formed in
+// pass A) instead of a lower bound.
+template <bool MASK = false, bool REP = false, bool ZEXACT = false, int DT, int NC>
 __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, float c, Lds& L,
                                               int V = 0, const RowExtras& x = RowExtras{}) {
   int nallow = 0x7FFFFFFF;
@@ -284,7 +304,8 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
     nallow = 0;
     for (int w = threadIdx.x; w < ((V + 31) >> 5); w += kBlock) nallow += __builtin_popcount(L.vmask[w]);
   }
-  float tmax = reg_pass_a<MASK>(r, L);
+  double zown = 0.0;
+  float tmax = reg_pass_a<MASK, ZEXACT>(r, L, c, &zown);
   if (REP && x.hn > 0) {
     if constexpr (MASK) __syncthreads();   // L.own shares LDS with the mask words
     if (threadIdx.x < kWave) {
@@ -317,7 +338,8 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
   }
   r.tmax = tmax;
   // the thread max's own weight, relative to itself
-  const double zt = (need_zlo && tmax > kNegInf && tmax < kPosInf) ? 1.0 : 0.0;
+  static_assert(!(ZEXACT && REP), "the exact sum is formed before the penalty");
+  const double zt = (need_zlo && tmax > kNegInf && tmax < kPosInf) ? (ZEXACT ? zown : 1.0) : 0.0;
   // wave level
   const float wm = wave_maxn(tmax);
   const float wt = wave_min(tmax > kNegInf ? tmax : kPosInf);
