@@ -69,7 +69,8 @@ enum {
   TSR_ROW_OK = 0,
   TSR_ROW_NONFINITE = 1, /* the row holds NaN or +inf */
   TSR_ROW_EMPTY = 2,     /* every logit is -inf: the kept set is empty [P2 39.3] */
-  TSR_ROW_BADTOKEN = 3   /* verify only: a draft token outside [0, vocab) */
+  TSR_ROW_BADTOKEN = 3,  /* verify only: a draft token outside [0, vocab) */
+  TSR_ROW_BADPARAM = 4   /* the row's own parameters (tsr_constraints.row_params) are invalid */
 };
 
 /* Sampling parameters, one set per call [P1 "Picking the next token"].
@@ -178,7 +179,11 @@ int sample_rows_masked(tsr_handle h, const void* logits, int dtype, int rows, in
  *      rescaled once, z / r if z > 0, z * r otherwise, before anything else
  *      [P5 "The repetition penalty"]; the rescaled logit is rounded to the
  *      logits' element type (float32; bf16 to nearest even from that float32).
- *      r = 1, history NULL or history_len 0: no penalty. */
+ *      r = 1, history NULL or history_len 0: no penalty.
+ *  row_params [rows] tsr_params (device memory): each row's own sampling
+ *      parameters in place of the call's `params` (which may then be NULL);
+ *      a row whose parameters tsr_params would reject gets
+ *      TSR_ROW_BADPARAM and token -1 (checked on the device, per row). */
 typedef struct {
   const uint32_t* allowed;
   int64_t allowed_stride;
@@ -186,6 +191,7 @@ typedef struct {
   int32_t history_len;
   int64_t history_stride;
   double repetition_penalty;
+  const tsr_params* row_params;
 } tsr_constraints;
 
 /* sample_rows with the per-row inputs of `cons` (nullable) and log p~ of each

@@ -15,12 +15,12 @@ from dataclasses import dataclass
 __all__ = [
     "TsrError", "TsrUnavailable", "Params", "Sampler", "library_path", "load_library",
     "F32", "BF16", "JOINT", "SEQUENTIAL", "ROW_OK", "ROW_NONFINITE", "ROW_EMPTY",
-    "ROW_BADTOKEN", "EXPORTED_SYMBOLS",
+    "ROW_BADTOKEN", "ROW_BADPARAM", "EXPORTED_SYMBOLS", "pack_row_params",
 ]
 
 F32, BF16 = 0, 1
 JOINT, SEQUENTIAL = 0, 1
-ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BADTOKEN = 0, 1, 2, 3
+ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BADTOKEN, ROW_BADPARAM = 0, 1, 2, 3, 4
 EXPORTED_SYMBOLS = ("sampler_init", "sampler_destroy", "greedy_argmax", "sample_rows",
                     "sample_rows_masked", "sample_rows_ex", "spec_verify", "beam_step",
                     "sampler_philox", "sampler_strerror")
@@ -57,7 +57,8 @@ class _Diag(ctypes.Structure):
 class _Constraints(ctypes.Structure):
     _fields_ = [("allowed", ctypes.c_void_p), ("allowed_stride", ctypes.c_int64),
                 ("history", ctypes.c_void_p), ("history_len", ctypes.c_int32),
-                ("history_stride", ctypes.c_int64), ("repetition_penalty", ctypes.c_double)]
+                ("history_stride", ctypes.c_int64), ("repetition_penalty", ctypes.c_double),
+                ("row_params", ctypes.c_void_p)]
 
 
 _lib = None
@@ -141,6 +142,14 @@ def _stream_ptr(stream):
 
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def pack_row_params(params_list):
+    """Per-row parameters as the bytes of a tsr_params array (host uint8
+    numpy array; copy it to the device for sample_rows_ex's row_params)."""
+    import numpy as np
+    arr = (_Params * len(params_list))(*[Params.of(p)._c() for p in params_list])
+    return np.frombuffer(bytes(arr), dtype=np.uint8).copy()
 
 
 class Sampler:
@@ -233,7 +242,8 @@ class Sampler:
         return out
 
     def sample_rows_ex(self, logits, params, step: int, allowed=None, history=None,
-                       penalty: float = 1.0, out=None, logprob=None, diag=None, stream=None):
+                       penalty: float = 1.0, out=None, logprob=None, diag=None, stream=None,
+                       row_params=None):
         """sample_rows with an allowed-token mask (as in sample_rows_masked) and
         a repetition penalty: ``history`` is a [rows, H] int32 device tensor of
         each row's recent token ids (H <= 64, ids outside [0, vocab) ignored),
@@ -241,7 +251,9 @@ class Sampler:
         import torch
         rows, vocab = logits.shape
         assert logits.stride(1) == 1, "rows must be contiguous"
-        cs = _Constraints(None, 0, None, 0, 0, float(penalty))
+        cs = _Constraints(None, 0, None, 0, 0, float(penalty), None)
+        if row_params is not None:   # a device tensor of packed tsr_params (see pack_row_params)
+            cs.row_params = row_params.data_ptr()
         if allowed is not None:
             assert allowed.dtype == torch.int32 and allowed.stride(1) == 1
             cs.allowed, cs.allowed_stride = allowed.data_ptr(), allowed.stride(0)
@@ -250,14 +262,14 @@ class Sampler:
             cs.history, cs.history_len = history.data_ptr(), history.shape[1]
             cs.history_stride = history.stride(0)
         out = torch.empty(rows, dtype=torch.int32, device=logits.device) if out is None else out
-        cp = Params.of(params)._c()
+        cp = Params.of(params)._c() if params is not None else None
         d = None
         if diag is not None:
             d = _Diag(*(ctypes.c_void_p(diag[k].data_ptr()) if diag.get(k) is not None else None
                         for k in ("status", "kept_count", "threshold", "kept_mass", "probs")))
         _check(load_library().sample_rows_ex(
             self._h, _ptr(logits), _dtype_code(logits), rows, vocab, logits.stride(0),
-            ctypes.byref(cs), ctypes.byref(cp), ctypes.c_uint64(int(step)), _ptr(out),
+            ctypes.byref(cs), ctypes.byref(cp) if cp is not None else None, ctypes.c_uint64(int(step)), _ptr(out),
             _ptr(logprob), ctypes.byref(d) if d is not None else None, _stream_ptr(stream)),
             "sample_rows_ex")
         return out

@@ -1,6 +1,7 @@
 // C-ABI host layer: argument validation, workspace, dispatch and error mapping.
 // Nothing here computes on logits; every step of the path runs in kernels.hip.
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -21,6 +22,15 @@ struct tsr_ctx {
 };
 
 namespace {
+
+// Per-row parameters are read on the device with this layout.
+static_assert(sizeof(tsr::RowParams) == sizeof(tsr_params), "tsr_params layout");
+static_assert(offsetof(tsr::RowParams, temperature) == offsetof(tsr_params, temperature) &&
+                  offsetof(tsr::RowParams, top_k) == offsetof(tsr_params, top_k) &&
+                  offsetof(tsr::RowParams, top_p) == offsetof(tsr_params, top_p) &&
+                  offsetof(tsr::RowParams, min_p) == offsetof(tsr_params, min_p) &&
+                  offsetof(tsr::RowParams, filter_mode) == offsetof(tsr_params, filter_mode),
+              "tsr_params layout");
 
 constexpr double kTemperatureMin = 1e-30;
 constexpr int kMaxDraft = 32;
@@ -201,6 +211,9 @@ int sample_rows_ex(tsr_handle h, const void* logits, int dtype, int rows, int vo
   } else if (cs.history_len < 0) {
     return TSR_EINVAL;
   }
+  if (cs.row_params && ((uintptr_t)cs.row_params % alignof(tsr_params)) != 0) return TSR_EINVAL;
+  const tsr_params unit{1.0, 0, 1.0, 0.0, TSR_JOINT};
+  if (!params && cs.row_params) params = &unit;   // the rows carry their own
   const int prc = check_params(params);
   if (prc != TSR_OK) return prc;
   if (vocab > tsr::max_vocab_sample(dtype)) return TSR_EUNSUPPORTED;
@@ -215,6 +228,11 @@ int sample_rows_ex(tsr_handle h, const void* logits, int dtype, int rows, int vo
   }
   dg.logprob = out_logprob;
   tsr::KParams kp = make_kparams(h, params, vocab, step, dg.kept_mass != nullptr);
+  if (cs.row_params) {
+    kp.rowp = reinterpret_cast<const tsr::RowParams*>(cs.row_params);
+    kp.flags |= tsr::F_ROWP;
+    if (dg.kept_mass) kp.flags |= tsr::F_Z;
+  }
   if (cs.allowed) {
     kp.allowed = cs.allowed;
     kp.allowed_stride = (long long)cs.allowed_stride;

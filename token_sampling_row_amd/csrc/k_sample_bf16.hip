@@ -13,7 +13,7 @@ hipError_t launch_sample_dt1(const unsigned char* p, int rows, int V, long long 
     return hipGetLastError();
   }
   const int ext = (kp.flags & F_MASK) ? 1 : (kp.flags & F_REP) ? 2 : 0;
-  const bool wide = wide_filters(kp, kBlock);
+  const bool wide = (kp.flags & F_ROWP) != 0 || wide_filters(kp, kBlock);
 #define TSR_CASE(N)                                                                            \
   case N:                                                                                      \
     if (ext == 1)                                                                              \

@@ -7,6 +7,15 @@
 
 namespace tsr {
 
+// One row's sampling parameters, laid out as the C ABI's tsr_params.
+struct RowParams {
+  double temperature;
+  int32_t top_k;
+  double top_p;
+  double min_p;
+  int32_t filter_mode;
+};
+
 // Sampling parameters after host-side validation.
 struct KParams {
   float c;             // log2(e) / T
@@ -23,6 +32,7 @@ struct KParams {
   long long hist_stride;     // ids between window rows
   int hist_len;              // ids per row (<= kHistMax)
   double rpen;               // repetition penalty r
+  const RowParams* rowp;     // per-row parameters (F_ROWP), validated and derived per row
 };
 enum : int {
   F_GREEDY = 1,   // temperature 0
@@ -33,6 +43,7 @@ enum : int {
   F_Z = 32,       // the full weight sum is wanted (kept-mass diagnostic)
   F_MASK = 64,    // an allowed-token bitmask applies
   F_REP = 128,    // a repetition penalty applies
+  F_ROWP = 256,   // each row has its own parameters (rowp)
 };
 constexpr int kHistMax = 64;   // longest look-back window
 // Filters whose kept set may be far larger than any candidate buffer: no

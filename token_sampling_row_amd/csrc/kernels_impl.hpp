@@ -21,6 +21,44 @@ __device__ __forceinline__ Filters make_filters(const KParams& kp, float M) {
   return f;
 }
 
+// Row `row`'s own parameters (F_ROWP) in place of the call's: validated as
+// the host validates a call's (false: the row is TSR_ROW_BADPARAM), then
+// derived as the host derives them (temperature to c, the filters' switches).
+__device__ __forceinline__ bool row_kparams(KParams& kp, int row, int V) {
+  const RowParams q = kp.rowp[row];
+  const double T = q.temperature;
+  if (!isfinite(T) || !isfinite(q.top_p) || !isfinite(q.min_p)) return false;
+  if (T < 0.0 || (T > 0.0 && T < 1e-30) || q.top_p < 0.0) return false;
+  if (q.filter_mode != 0 && q.filter_mode != 1) return false;
+  const int keep = kp.flags & (F_MASK | F_REP | F_ROWP);
+  const bool want_z = (kp.flags & F_Z) != 0;
+  kp.flags = keep;
+  kp.top_k = 0;
+  if (T == 0.0) {
+    kp.flags |= F_GREEDY;
+    kp.c = 1.0f;
+    return true;
+  }
+  kp.c = (float)(1.4426950408889634 / T);
+  kp.cR = kp.c * 16.0f;
+  if (q.top_k > 0 && q.top_k < V) {
+    kp.top_k = q.top_k;
+    kp.flags |= F_K;
+  }
+  if (q.top_p < 1.0) {
+    kp.top_p = q.top_p;
+    kp.flags |= F_P;
+  }
+  if (q.min_p > 0.0 && q.min_p < 1.0) {
+    kp.minp_off = T * log(q.min_p);
+    kp.flags |= F_M;
+  }
+  if (q.filter_mode == 1) kp.flags |= F_SEQ;
+  if (want_z) kp.flags |= F_Z;
+  return true;
+}
+constexpr int kRowBadParam = 4;
+
 // JOINT top-p measures mass against the row's full weight sum.
 __device__ __forceinline__ bool joint_top_p(const KParams& kp) {
   const bool k_on = kp.flags & F_K, p_on = kp.flags & F_P, seq = kp.flags & F_SEQ;
@@ -348,13 +386,19 @@ __device__ __forceinline__ StreamRow<DT> row_stream_view(const unsigned char* p,
 template <int DT, int NC, bool WIDE, int EXT>
 __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* logits,
                                                         long long stride_bytes, int V,
-                                                        int aligned, int ragged, KParams kp,
+                                                        int aligned, int ragged, KParams kp0,
                                                         int32_t* out, DiagPtrs dg) {
   constexpr int EPC = Fmt<DT>::EPC;
   Lds& L = tsr_lds;
   const int row = blockIdx.x;
   const unsigned char* p = logits + (long long)row * stride_bytes;
   constexpr bool MASK = EXT == 1, REP = EXT != 0;
+  KParams kp = kp0;
+  if ((kp.flags & F_ROWP) && !row_kparams(kp, row, V)) {
+    write_row(row, -1, kRowBadParam, 0, kNegInf, 0.0, kNaN, kNaN, out, dg);
+    zero_probs(dg, row, V);
+    return;
+  }
   RegRow<DT, NC> r;
   RowExtras x;
   if (REP && (kp.flags & F_REP)) {   // the window ids, read by wave 0 before the row
@@ -388,7 +432,8 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
     // the cut and the draw; the registers are dead afterwards. Without min-p
     // or a small top-k the WIDE instance goes straight to its register search
     // (no candidate bound can narrow a wide kept set).
-    const bool narrow = f.m_on || (EXT != 0 && f.k_on && f.k <= kBlock / 4);
+    const bool narrow =
+        f.m_on || ((EXT != 0 || (kp.flags & F_ROWP)) && f.k_on && f.k <= kBlock / 4);
     FastOut fo{0, 0, -1, kPosInf, 0, 0.0, 0.0};
     if (!(WIDE && DT == 1) || narrow)
       fo = fast_cut<MASK>(r, V, M, st.tmin, st.zlo, c, f, u, L, st.nallow);
@@ -425,10 +470,16 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
 template <int DT>
 __global__ __launch_bounds__(kBlock) void sample_kernel_stream(const unsigned char* logits,
                                                                long long stride_bytes, int V,
-                                                               int aligned, KParams kp,
+                                                               int aligned, KParams kp0,
                                                                int32_t* out, DiagPtrs dg) {
   const int row = blockIdx.x;
   const unsigned char* p = logits + (long long)row * stride_bytes;
+  KParams kp = kp0;
+  if ((kp.flags & F_ROWP) && !row_kparams(kp, row, V)) {
+    write_row(row, -1, kRowBadParam, 0, kNegInf, 0.0, kNaN, kNaN, out, dg);
+    zero_probs(dg, row, V);
+    return;
+  }
   int hn = 0;
   if (kp.flags & F_REP) {   // publish the look-back window before any read
     hn = kp.hist_len;
