@@ -767,8 +767,13 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt
                                                         int32_t* out_acc, int32_t* out_status) {
   constexpr int EPC = Fmt<DT>::EPC;
   Lds& L = tsr_lds;
-  const int b = blockIdx.x / (K + 1);
-  const int j = blockIdx.x - b * (K + 1);
+  // the draft positions (two rows each) first, then every sequence's bonus
+  // position (the target row only): when the grid exceeds the device, the
+  // lighter workgroups are the ones that wait
+  const int nseq = (int)gridDim.x / (K + 1);
+  const int blk = (int)blockIdx.x;
+  const int b = blk < nseq * K ? blk / K : blk - nseq * K;
+  const int j = blk < nseq * K ? blk - b * K : K;
   const long long rowbytes = (long long)V * Fmt<DT>::ESZ;
   const unsigned char* tp = tgt + ((long long)b * (K + 1) + j) * rowbytes;
   const unsigned char* dp = dft + ((long long)b * K + (j < K ? j : 0)) * rowbytes;
@@ -828,35 +833,40 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt
     __hip_atomic_store(&ws.st_d[slot], st_d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t prev = __hip_atomic_fetch_add(&ws.counter[b], 1u, __ATOMIC_ACQ_REL,
                                                  __HIP_MEMORY_SCOPE_AGENT);
-    if (prev == (uint32_t)K) {
-      // last of the K+1 workgroups of this sequence: assemble its output
-      const int s0 = b * ws.kmax1;
-      int status = 0;
-      for (int q = 0; q <= K && !status; ++q)
-        status = __hip_atomic_load(&ws.st_t[s0 + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int q = 0; q < K && !status; ++q)
-        status = __hip_atomic_load(&ws.st_d[s0 + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int q = 0; q < K && !status; ++q) {
-        const int xq = xs[(long long)b * K + q];
-        if (xq < 0 || xq >= V) status = 3;
-      }
-      int32_t* o = out_tokens + (long long)b * (K + 1);
-      int n = 0;
-      if (status) {
-        for (int q = 0; q <= K; ++q) o[q] = -1;
-      } else {
-        while (n < K &&
-               __hip_atomic_load(&ws.acc[s0 + n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-          o[n] = xs[(long long)b * K + n];
-          ++n;
-        }
-        o[n] = __hip_atomic_load(&ws.tok[s0 + n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int q = n + 1; q <= K; ++q) o[q] = -1;
-      }
-      out_acc[b] = n;
-      if (out_status) out_status[b] = status;
-      __hip_atomic_store(&ws.counter[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    L.si[0] = prev == (uint32_t)K;
+  }
+  __syncthreads();
+  if (!L.si[0] || threadIdx.x >= kWave) return;
+  // last of the K+1 workgroups of this sequence, wave 0: every position's
+  // results read at once (lane q: position q), then the output
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int q = threadIdx.x;
+  const int s0 = b * ws.kmax1;
+  const bool inq = q <= K, dq = q < K;
+  const int qt = inq ? __hip_atomic_load(&ws.st_t[s0 + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+  const int qd = dq ? __hip_atomic_load(&ws.st_d[s0 + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+  const int qa = dq ? __hip_atomic_load(&ws.acc[s0 + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1;
+  const int qk = inq ? __hip_atomic_load(&ws.tok[s0 + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -1;
+  const int xq = dq ? xs[(long long)b * K + q] : 0;
+  // status: the target's of the first position that has one, else the
+  // draft's, else a draft token out of range
+  const unsigned long long bt = __ballot(qt != 0), bd = __ballot(qd != 0);
+  const unsigned long long bx = __ballot(dq && (xq < 0 || xq >= V));
+  const int status = bt ? readlane_u32((uint32_t)qt, __ffsll((long long)bt) - 1)
+                        : bd ? readlane_u32((uint32_t)qd, __ffsll((long long)bd) - 1)
+                             : (bx ? 3 : 0);
+  // accepted prefix: up to the first rejection
+  const unsigned long long rej = __ballot(dq && !qa);
+  const int n = rej ? __ffsll((long long)rej) - 1 : K;
+  const int tn = readlane_u32((uint32_t)qk, n);
+  if (inq) {
+    int32_t* o = out_tokens + (long long)b * (K + 1);
+    o[q] = status ? -1 : (q < n ? xq : (q == n ? tn : -1));
+  }
+  if (q == 0) {
+    out_acc[b] = status ? 0 : n;
+    if (out_status) out_status[b] = status;
+    __hip_atomic_store(&ws.counter[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
