@@ -65,7 +65,8 @@ def instance_units() -> dict[str, str]:
                 "long long, int, int, int, int32_t*, int32_t*);\n}\n")
         for nc in VERIFY_NCS:
             for un in ("false", "true"):
-                units[f"i_verify_{dt}_{nc}_{un}.hip"] = head + (
+                # two rows per workgroup: no chunk maxima kept in registers
+                units[f"i_verify_{dt}_{nc}_{un}.hip"] = "#define TSR_ROW_NO_CMAX 1\n" + head + (
                     f"template __global__ void verify_kernel<{dt}, {nc}, {un}>(const unsigned char*, "
                     "const unsigned char*, const int32_t*, int, int, int, int, KParams, VerifyWs, "
                     "int32_t*, int32_t*, int32_t*);\n}\n")

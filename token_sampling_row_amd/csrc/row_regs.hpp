@@ -18,6 +18,10 @@
 
 #include "row_common.hpp"
 
+#ifndef TSR_ROW_NO_CMAX
+#define TSR_ROW_NO_CMAX 0
+#endif
+
 namespace tsr {
 
 // Cache policy of the row loads: non-temporal, so the streamed logits are the
@@ -45,8 +49,10 @@ struct RegRow {
   typename VecU<NA>::type ax, ay, az, aw;   // the chunks, one vector per dword
   typename VecU<NBS>::type bx, by, bz, bw;
   // Chunk maxima (-inf past the end of the row), kept in registers up to 32
-  // chunk rows; wider rows recompute them (their registers are needed more).
-  static constexpr bool kKeepCmax = NC <= 32;
+  // chunk rows; wider rows recompute them (their registers are needed more),
+  // as do the units that hold two rows (TSR_ROW_NO_CMAX defined to 1 before
+  // this header: the verify step).
+  static constexpr bool kKeepCmax = NC <= 32 && !TSR_ROW_NO_CMAX;
   typename VecF<kKeepCmax ? NA : 1>::type ca;
   typename VecF<kKeepCmax ? NBS : 1>::type cb;
   float tmax;     // this thread's maximum
