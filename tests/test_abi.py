@@ -63,7 +63,23 @@ def test_calls_reject_null_handle(lib):
     assert lib.spec_verify(None, None, None, 0, None, 1, 1, 1, ctypes.byref(p), 0, None, None,
                            None, None) == 1
     assert lib.sampler_philox(None, None, 1, None, None) == 1
+    assert lib.sample_rows_masked(None, None, 0, 1, 1, 1, None, 0, ctypes.byref(p), 0, None,
+                                  None, None, None) == 1
+    cs = tsr._Constraints(None, 0, None, 0, 0, 1.0, None)
+    assert lib.sample_rows_ex(None, None, 0, 1, 1, 1, ctypes.byref(cs), ctypes.byref(p), 0, None,
+                              None, None, None) == 1
+    assert lib.beam_step(None, None, 0, 1, 4, 1, 1, None, None, None, None, None, None) == 1
     assert lib.sampler_destroy(None) == 0
+
+
+def test_struct_layouts_match_the_header():
+    """The ctypes mirrors of tsr_params, tsr_diag and tsr_constraints have the
+    C layout (x86-64 alignment: doubles and pointers on 8 bytes)."""
+    assert ctypes.sizeof(tsr._Params) == 40
+    assert tsr._Params.top_p.offset == 16 and tsr._Params.filter_mode.offset == 32
+    assert ctypes.sizeof(tsr._Diag) == 5 * 8
+    assert ctypes.sizeof(tsr._Constraints) == 7 * 8
+    assert tsr._Constraints.history_len.offset == 24 and tsr._Constraints.row_params.offset == 48
 
 
 def test_binding_has_no_cpu_fallback(monkeypatch, tmp_path):
