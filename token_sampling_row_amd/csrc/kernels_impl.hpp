@@ -634,22 +634,22 @@ __global__ __launch_bounds__(kBlock) void beam_kernel(const unsigned char* logit
     lnz = log(st.zlo);
     n = reg_top_keys(r, st.M, st.tmin, beam, L);
   }
-  if (tid < beam) {
-    double sc = (double)kNegInf;
-    int tk = -1;
-    if (tid < n) {
-      const unsigned long long key = L.key[tid];
-      sc = sb + ((double)key2f(key_hi(key)) - (double)st.M) - lnz;
-      tk = (int)~(uint32_t)key;
-    }
-    const long long slot = (long long)row * kBeamMax + tid;
-    __hip_atomic_store(&ws.score[slot], sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&ws.tok[slot], tk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  }
-  if (tid == 0 && bad) __hip_atomic_fetch_or(&ws.bad[g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
   if (tid == 0) {
+    // the row's list, then the arrival (its release orders this thread's
+    // stores before the counter)
+    for (int q = 0; q < beam; ++q) {
+      double sc = (double)kNegInf;
+      int tk = -1;
+      if (q < n) {
+        const unsigned long long key = L.key[q];
+        sc = sb + ((double)key2f(key_hi(key)) - (double)st.M) - lnz;
+        tk = (int)~(uint32_t)key;
+      }
+      const long long slot = (long long)row * kBeamMax + q;
+      __hip_atomic_store(&ws.score[slot], sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ws.tok[slot], tk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (bad) __hip_atomic_fetch_or(&ws.bad[g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t prev = __hip_atomic_fetch_add(&ws.counter[g], 1u, __ATOMIC_ACQ_REL,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     L.si[0] = prev == (uint32_t)(beam - 1);
