@@ -14,6 +14,7 @@ Modules
 philox   Philox4x32-10 counter-based generator (Salmon, Moraes, Dror, Shaw,
          "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11), written from its
          published definition, and the counter layout the sampler uses.
+tree     The tree (multi-candidate) verify step.
 beam     One beam-search step (eq. 39.1, Listing 39.1) and the search built on it.
 sampler  The filter chain (temperature, softmax, top-k, top-p, min-p,
          renormalisation by eq. 39.2), the draw, greedy decoding, and the
@@ -26,3 +27,4 @@ Philox, an independent library implementation (rocRAND's host-callable engine).
 from .philox import philox4x32_10, sampler_counters, uniforms_from_words  # noqa: F401
 from .sampler import *  # noqa: F401,F403
 from .beam import *  # noqa: F401,F403
+from .tree import *  # noqa: F401,F403

@@ -31,6 +31,7 @@ MASK32 = 0xFFFFFFFF
 # Domains of the counter's second word (bits 16..31).
 DOMAIN_SAMPLE = 0   # one draw per row of sample_rows
 DOMAIN_SPEC = 1     # the verify step: accept test, residual draw, bonus draw
+DOMAIN_TREE = 2     # the tree verify step: node v, child c at position v * 32 + c
 
 
 def philox4x32_10(counters: np.ndarray, key) -> np.ndarray:
