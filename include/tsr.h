@@ -228,6 +228,38 @@ int spec_verify(tsr_handle h, const void* target_logits, const void* draft_logit
                 const tsr_params* params, uint64_t step, int32_t* out_tokens,
                 int32_t* out_accepted, int32_t* out_status, void* hip_stream);
 
+/* Tree (multi-candidate) verify [P3 "Extensions and Variants": the draft
+ * proposes a tree of candidates with several branches and the target
+ * verifies every path; P2 39.4 for the rule at one candidate] for `rows`
+ * sequences of `nodes` tree nodes each (1 <= nodes <= 32 and <= max_k + 1).
+ *  parent [rows][nodes] int32: node 0 is the current context (parent -1);
+ *      node n > 0 extends node parent[n] < n (else the sequence gets status 5).
+ *  tokens [rows][nodes] int32: the token node n appends (tokens[0] unused).
+ *  target_logits, draft_logits [rows][nodes][vocab]: the target's and the
+ *      draft's logits for the token after node n's path (the draft's only read
+ *      for nodes with children, and not at all at temperature 0).
+ * The children of a node (in node order) are its candidates, taken as
+ * independent draws from the draft's distribution q~ there. From the root:
+ * child c of the current node v is kept iff w0 * 2^-32 < min(1, p_c(x) /
+ * q~(x)), p_1 = p~_v and p_{c+1} = max(0, p_c - q~) normalised after each
+ * rejection (w0 of the Philox counter (row, v * 32 + c | 2 << 16, step)); a
+ * kept child becomes v; when every child of v is rejected, or v has none, one
+ * token is drawn from the current p with w1 of (row, v * 32 | 2 << 16, step)
+ * and the step ends. Temperature and filters shape p~ and q~ as in
+ * spec_verify. Greedy (temperature 0): the first child holding the target's
+ * argmax is kept, else the argmax is emitted.
+ *  out_tokens [rows][nodes]: the kept children's tokens then the drawn one,
+ *      -1 after; out_path [rows][nodes]: the kept nodes, -1 after;
+ *  out_accepted [rows]: how many nodes were kept; out_status [rows]
+ *      (nullable): TSR_ROW_* (NONFINITE/EMPTY for a bad target row or a bad
+ *      draft row of a node with children, BADTOKEN for a token outside
+ *      [0, vocab), 5 for a parent that is not an earlier node).
+ * Shares the verify workspace: not concurrent with spec_verify on the handle. */
+int tree_verify(tsr_handle h, const void* target_logits, const void* draft_logits, int dtype,
+                const int32_t* parent, const int32_t* tokens, int rows, int nodes, int vocab,
+                const tsr_params* params, uint64_t step, int32_t* out_tokens, int32_t* out_path,
+                int32_t* out_accepted, int32_t* out_status, void* hip_stream);
+
 /* One beam-search step [P2 39.1: eq. 39.1, Listing 39.1; P4 "Beam search"]
  * for `groups` independent searches of `beam` beams each (no length penalty
  * or end token, as in the listing).

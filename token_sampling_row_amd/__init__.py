@@ -22,7 +22,8 @@ F32, BF16 = 0, 1
 JOINT, SEQUENTIAL = 0, 1
 ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BADTOKEN, ROW_BADPARAM = 0, 1, 2, 3, 4
 EXPORTED_SYMBOLS = ("sampler_init", "sampler_destroy", "greedy_argmax", "sample_rows",
-                    "sample_rows_masked", "sample_rows_ex", "spec_verify", "beam_step",
+                    "sample_rows_masked", "sample_rows_ex", "spec_verify", "tree_verify",
+                    "beam_step",
                     "sampler_philox", "sampler_strerror")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +88,8 @@ def load_library():
                                    vp]
     lib.spec_verify.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, ctypes.POINTER(_Params),
                                 u64, vp, vp, vp, vp]
+    lib.tree_verify.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, ctypes.POINTER(_Params),
+                                u64, vp, vp, vp, vp, vp]
     lib.beam_step.argtypes = [vp, vp, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp]
     lib.sampler_philox.argtypes = [vp, vp, i32, vp, vp]
     lib.sampler_strerror.argtypes = [i32]
@@ -295,6 +298,28 @@ class Sampler:
                                           _ptr(out_accepted), _ptr(out_status),
                                           _stream_ptr(stream)), "spec_verify")
         return out_tokens, out_accepted
+
+    def tree_verify(self, target, draft, parent, tokens, params, step: int, status=None,
+                    stream=None):
+        """target, draft [rows, N, V] (draft None at temperature 0), parent and
+        tokens [rows, N] int32 -> (tokens [rows, N], path [rows, N],
+        accepted [rows])."""
+        import torch
+        rows, N, vocab = target.shape
+        assert target.is_contiguous() and (draft is None or draft.is_contiguous())
+        assert parent.dtype == torch.int32 and parent.is_contiguous()
+        assert tokens.dtype == torch.int32 and tokens.is_contiguous()
+        dev = target.device
+        out_t = torch.empty(rows, N, dtype=torch.int32, device=dev)
+        out_p = torch.empty(rows, N, dtype=torch.int32, device=dev)
+        acc = torch.empty(rows, dtype=torch.int32, device=dev)
+        cp = Params.of(params)._c()
+        _check(load_library().tree_verify(self._h, _ptr(target), _ptr(draft), _dtype_code(target),
+                                          _ptr(parent), _ptr(tokens), rows, N, vocab,
+                                          ctypes.byref(cp), ctypes.c_uint64(int(step)),
+                                          _ptr(out_t), _ptr(out_p), _ptr(acc), _ptr(status),
+                                          _stream_ptr(stream)), "tree_verify")
+        return out_t, out_p, acc
 
     def beam_step(self, logits, beam_scores, beam: int, status=None, stream=None):
         """logits [groups * beam, V] device tensor (row g * beam + b: beam b

@@ -69,7 +69,10 @@ def instance_units() -> dict[str, str]:
                 units[f"i_verify_{dt}_{nc}_{un}.hip"] = "#define TSR_ROW_NO_CMAX 1\n" + head + (
                     f"template __global__ void verify_kernel<{dt}, {nc}, {un}>(const unsigned char*, "
                     "const unsigned char*, const int32_t*, int, int, int, int, KParams, VerifyWs, "
-                    "int32_t*, int32_t*, int32_t*);\n}\n")
+                    "int32_t*, int32_t*, int32_t*);\n"
+                    f"template __global__ void tree_kernel<{dt}, {nc}, {un}>(const unsigned char*, "
+                    "const unsigned char*, const int32_t*, const int32_t*, int, int, int, KParams, "
+                    "VerifyWs, int32_t*, int32_t*, int32_t*, int32_t*);\n}\n")
         units[f"i_stream_{dt}.hip"] = head + (
             f"template __global__ void sample_kernel_stream<{dt}>(const unsigned char*, long long, "
             "int, int, KParams, int32_t*, DiagPtrs);\n"

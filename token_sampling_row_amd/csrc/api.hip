@@ -34,6 +34,7 @@ static_assert(offsetof(tsr::RowParams, temperature) == offsetof(tsr_params, temp
 
 constexpr double kTemperatureMin = 1e-30;
 constexpr int kMaxDraft = 32;
+constexpr int kMaxTreeNodes = 32;
 
 // Runs f with the handle's device current and restores the caller's device.
 template <class F>
@@ -297,6 +298,36 @@ int spec_verify(tsr_handle h, const void* target_logits, const void* draft_logit
     const hipError_t e = tsr::launch_verify(target_logits, draft_logits, dtype, draft_tokens,
                                             rows, K, vocab, aligned, ragged, kp, h->ws, out_tokens,
                                             out_accepted, out_status, (hipStream_t)hip_stream);
+    return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
+  });
+}
+
+int tree_verify(tsr_handle h, const void* target_logits, const void* draft_logits, int dtype,
+                const int32_t* parent, const int32_t* tokens, int rows, int nodes, int vocab,
+                const tsr_params* params, uint64_t step, int32_t* out_tokens, int32_t* out_path,
+                int32_t* out_accepted, int32_t* out_status, void* hip_stream) {
+  if (!h || !target_logits || !parent || !tokens || !out_tokens || !out_path || !out_accepted)
+    return TSR_EINVAL;
+  if (dtype != TSR_F32 && dtype != TSR_BF16) return TSR_EINVAL;
+  if (rows < 0 || rows > h->max_rows || vocab < 1 || vocab > h->max_vocab) return TSR_EINVAL;
+  if (nodes < 1 || nodes > kMaxTreeNodes || nodes > h->max_k + 1) return TSR_EINVAL;
+  const int prc = check_params(params);
+  if (prc != TSR_OK) return prc;
+  if (params->temperature > 0.0 && !draft_logits) return TSR_EINVAL;
+  if (!elem_aligned(target_logits, dtype) || (draft_logits && !elem_aligned(draft_logits, dtype)))
+    return TSR_EINVAL;
+  if (vocab > tsr::max_vocab_verify(dtype)) return TSR_EUNSUPPORTED;
+  if (rows == 0) return TSR_OK;
+  const tsr::KParams kp = make_kparams(h, params, vocab, step, false);
+  const long long rb = (long long)vocab * esize(dtype);
+  const int aligned = ((uintptr_t)target_logits % 16 == 0) &&
+                      (!draft_logits || (uintptr_t)draft_logits % 16 == 0) && (rb % 16 == 0);
+  const int ragged = !aligned || (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;
+  return on_device(h->device, [&]() -> int {
+    const hipError_t e = tsr::launch_tree(target_logits, draft_logits, dtype, parent, tokens, rows,
+                                          nodes, vocab, aligned, ragged, kp, h->ws, out_tokens,
+                                          out_path, out_accepted, out_status,
+                                          (hipStream_t)hip_stream);
     return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
   });
 }

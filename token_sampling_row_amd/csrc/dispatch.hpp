@@ -54,7 +54,10 @@ constexpr int kVerifyNcs[] = {1, 2, 4, 8, 16};
 #define TSR_DECLARE_VERIFY_DT(D, N, U)                                                        \
   extern template __global__ void verify_kernel<D, N, U>(                                     \
       const unsigned char*, const unsigned char*, const int32_t*, int, int, int, int, KParams,  \
-      VerifyWs, int32_t*, int32_t*, int32_t*);
+      VerifyWs, int32_t*, int32_t*, int32_t*);                                                 \
+  extern template __global__ void tree_kernel<D, N, U>(                                       \
+      const unsigned char*, const unsigned char*, const int32_t*, const int32_t*, int, int,    \
+      int, KParams, VerifyWs, int32_t*, int32_t*, int32_t*, int32_t*);
 #define TSR_DECLARE_VERIFY(N)                                                                \
   TSR_DECLARE_VERIFY_DT(0, N, false) TSR_DECLARE_VERIFY_DT(0, N, true)                       \
   TSR_DECLARE_VERIFY_DT(1, N, false) TSR_DECLARE_VERIFY_DT(1, N, true)

@@ -31,6 +31,29 @@ hipError_t launch_verify(const void* tgt, const void* dft, int dtype, const int3
                                         out_tokens, out_acc, out_status, s);
 }
 
+hipError_t launch_tree_dt0(const unsigned char* tp, const unsigned char* dp,
+                           const int32_t* parent, const int32_t* tokens, int rows, int N, int V,
+                           int aligned, int ragged, const KParams& kp, const VerifyWs& ws,
+                           int32_t* out_tokens, int32_t* out_path, int32_t* out_acc,
+                           int32_t* out_status, hipStream_t s);
+hipError_t launch_tree_dt1(const unsigned char* tp, const unsigned char* dp,
+                           const int32_t* parent, const int32_t* tokens, int rows, int N, int V,
+                           int aligned, int ragged, const KParams& kp, const VerifyWs& ws,
+                           int32_t* out_tokens, int32_t* out_path, int32_t* out_acc,
+                           int32_t* out_status, hipStream_t s);
+
+hipError_t launch_tree(const void* tgt, const void* dft, int dtype, const int32_t* parent,
+                       const int32_t* tokens, int rows, int N, int V, int aligned, int ragged,
+                       const KParams& kp, const VerifyWs& ws, int32_t* out_tokens,
+                       int32_t* out_path, int32_t* out_acc, int32_t* out_status, hipStream_t s) {
+  const unsigned char* tp = static_cast<const unsigned char*>(tgt);
+  const unsigned char* dp = static_cast<const unsigned char*>(dft ? dft : tgt);
+  return dtype == 0 ? launch_tree_dt0(tp, dp, parent, tokens, rows, N, V, aligned, ragged, kp, ws,
+                                      out_tokens, out_path, out_acc, out_status, s)
+                    : launch_tree_dt1(tp, dp, parent, tokens, rows, N, V, aligned, ragged, kp, ws,
+                                      out_tokens, out_path, out_acc, out_status, s);
+}
+
 hipError_t launch_sample(const void* logits, int dtype, int rows, int V, long long stride_bytes,
                          int aligned, int ragged, const KParams& kp, int32_t* out,
                          const DiagPtrs& dg, hipStream_t s) {

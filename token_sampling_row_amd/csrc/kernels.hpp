@@ -100,6 +100,10 @@ hipError_t launch_verify(const void* tgt, const void* dft, int dtype, const int3
                          int rows, int K, int V, int aligned, int ragged, const KParams& kp,
                          const VerifyWs& ws, int32_t* out_tokens, int32_t* out_acc,
                          int32_t* out_status, hipStream_t s);
+hipError_t launch_tree(const void* tgt, const void* dft, int dtype, const int32_t* parent,
+                       const int32_t* tokens, int rows, int N, int V, int aligned, int ragged,
+                       const KParams& kp, const VerifyWs& ws, int32_t* out_tokens,
+                       int32_t* out_path, int32_t* out_acc, int32_t* out_status, hipStream_t s);
 hipError_t launch_beam(const void* logits, int dtype, int groups, int beam, int V,
                        long long stride_bytes, int aligned, int ragged, const double* scores, BeamWs ws,
                        int32_t* out_parent, int32_t* out_tok, double* out_score,

@@ -725,6 +725,63 @@ struct ResidualWeights {
   }
 };
 
+// Tree verify: the target distribution left at a node after k rejected
+// candidates, p_{k+1} = max(0, p_k - q~) normalised (p_1 = p~; a step whose
+// residual sum is zero leaves p unchanged: zinv 0), per element; L.tz[s]
+// holds 1 / Z of step s. LAST: the unnormalised residual of one more step
+// (for its sum). The weights are relative (the walk normalises).
+template <int DT, int NC, bool LAST>
+struct TreeWeights {
+  const RegRow<DT, NC>& rp;
+  const RegRow<DT, NC>& rq;
+  float tp, Mp, tq, Mq, c;
+  double inv_zp, inv_zq;
+  int k;
+  const Lds& L;
+  __device__ __forceinline__ double pk(double pe, double qe) const {
+    for (int s2 = 0; s2 < k; ++s2) {
+      const double zi = L.tz[s2];
+      if (zi > 0.0) pe = fmax(0.0, pe - qe) * zi;
+    }
+    return pe;
+  }
+  __device__ __forceinline__ void operator()(int j, float* w) const {
+    constexpr int EPC = Fmt<DT>::EPC;
+    if (rp.cmax(j) >= tp) {
+      float a[EPC], b[EPC];
+      rp.elems(j, a);
+      rq.elems(j, b);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const double pe = a[e] >= tp ? (double)weight(a[e], Mp, c) * inv_zp : 0.0;
+        const double qe = b[e] >= tq ? (double)weight(b[e], Mq, c) * inv_zq : 0.0;
+        double x = pk(pe, qe);
+        if (LAST) x = fmax(0.0, x - qe);
+        w[e] = (float)x;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) w[e] = 0.0f;
+    }
+  }
+};
+
+// Block-wide sum of a per-element weight functor over the register row.
+template <int NC, int EPC, class CW>
+__device__ __forceinline__ double reg_functor_sum(const CW& cw, Lds& L) {
+  double acc = 0.0;
+#pragma nounroll
+  for (int j = 0; j < NC; ++j) {
+    float w[EPC];
+    cw(j, w);
+    float t = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) t += w[e];
+    acc += (double)t;
+  }
+  return block_sum<kBlock>(acc, L.bs);
+}
+
 struct RowCut {
   int status;
   float M;
@@ -865,6 +922,150 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt
   }
   if (q == 0) {
     out_acc[b] = status ? 0 : n;
+    if (out_status) out_status[b] = status;
+    __hip_atomic_store(&ws.counter[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Tree (multi-candidate) verify [P3 "Extensions and Variants"; P2 39.4]: one
+// workgroup per (sequence b, node v). Node v's children (nodes whose parent
+// is v, in node order) are its candidates, tested in order against the
+// target distribution the earlier rejections left (p_1 = p~_v, then
+// max(0, p_c - q~_v) normalised); the first kept child, or else a draw from
+// the final p (w1 of the node's counter), is the node's result. The
+// sequence's last workgroup follows kept children from the root and writes
+// the emitted tokens and the accepted path. The tree (parent ids, tokens) is
+// read by every workgroup; N <= 32.
+template <int DT, int NC, bool UNALIGNED>
+__global__ __launch_bounds__(kBlock) void tree_kernel(const unsigned char* tgt,
+                                                      const unsigned char* dft,
+                                                      const int32_t* parent, const int32_t* tokens,
+                                                      int N, int V, int ragged, KParams kp,
+                                                      VerifyWs ws, int32_t* out_tokens,
+                                                      int32_t* out_path, int32_t* out_acc,
+                                                      int32_t* out_status) {
+  constexpr int EPC = Fmt<DT>::EPC;
+  Lds& L = tsr_lds;
+  const int b = (int)blockIdx.x / N;
+  const int v = (int)blockIdx.x - b * N;
+  const long long rowbytes = (long long)V * Fmt<DT>::ESZ;
+  const unsigned char* tp = tgt + ((long long)b * N + v) * rowbytes;
+  const unsigned char* dp = dft + ((long long)b * N + v) * rowbytes;
+  const bool greedy = (kp.flags & F_GREEDY) != 0;
+  // the tree, one node per lane (every wavefront reads it)
+  const int lane = __lane_id();
+  const bool ln = lane < N;
+  const int pa = ln ? parent[(long long)b * N + lane] : 0;
+  const int tk = ln ? tokens[(long long)b * N + lane] : 0;
+  const bool bad_tree =
+      __ballot(ln && (lane == 0 ? pa != -1 : (pa < 0 || pa >= lane))) != 0ull;
+  const bool bad_tok = __ballot(ln && lane > 0 && (tk < 0 || tk >= V)) != 0ull;
+  const unsigned long long chm = __ballot(ln && lane > 0 && pa == v);
+  const bool with_draft = !greedy && chm != 0ull;
+  RegRow<DT, NC> rp, rq;
+  rp.template load<UNALIGNED>(tp, V, ragged != 0);
+  if (with_draft) rq.template load<UNALIGNED>(dp, V, ragged != 0);
+  asm volatile("" ::: "memory");
+  int st_t = 0, st_d = 0, kept = -1, tok = -1;
+  if (greedy) {
+    const RowStats st = reg_stats(rp, false, 1.0f, L);
+    st_t = st.status;
+    if (st_t == 0) {
+      tok = reg_argmax(rp, st.M, L);
+      const unsigned long long hit = chm & __ballot(tk == tok);
+      kept = hit ? __ffsll((long long)hit) - 1 : -1;
+    }
+  } else {
+    const RowCut cp = verify_row_cut(rp, tp, V, true, kp, L);
+    st_t = cp.status;
+    RowCut cq{0, 0.0f, kPosInf, 1.0};
+    if (with_draft) {
+      cq = verify_row_cut(rq, dp, V, true, kp, L);
+      st_d = cq.status;
+    }
+    if (st_t == 0 && st_d == 0 && !bad_tree && !bad_tok) {
+      const double izp = 1.0 / cp.zs, izq = with_draft ? 1.0 / cq.zs : 0.0;
+      int k = 0;
+      for (unsigned long long m = chm; m; m &= m - 1ull, ++k) {
+        const int child = __ffsll((long long)m) - 1;
+        const int x = readlane_u32((uint32_t)tk, child);
+        const float lp = load_elem<DT>(tp, x), lq = load_elem<DT>(dp, x);
+        const double pe = lp >= cp.tau ? (double)weight(lp, cp.M, kp.c) * izp : 0.0;
+        const double qe = lq >= cq.tau ? (double)weight(lq, cq.M, kp.c) * izq : 0.0;
+        const TreeWeights<DT, NC, false> tw{rp, rq, cp.tau, cp.M, cq.tau, cq.M, kp.c, izp, izq, k, L};
+        const double pc = tw.pk(pe, qe);
+        const double a = fmin(1.0, pc / fmax(qe, 1e-300));
+        if (draw_uniform(kp, (uint32_t)b, (uint32_t)(v * 32 + k), 2u, 0) < a) {
+          kept = child;
+          break;
+        }
+        // rejected: the next residual's normaliser
+        const double z = reg_functor_sum<NC, EPC>(
+            TreeWeights<DT, NC, true>{rp, rq, cp.tau, cp.M, cq.tau, cq.M, kp.c, izp, izq, k, L}, L);
+        if (threadIdx.x == 0) L.tz[k] = z > 0.0 ? 1.0 / z : 0.0;
+        __syncthreads();
+      }
+      if (kept < 0) {
+        const double u1 = draw_uniform(kp, (uint32_t)b, (uint32_t)(v * 32), 2u, 1);
+        double zt;
+        if (k == 0)
+          tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{rp, cp.tau, cp.M, kp.c}, u1, L, &zt);
+        else
+          tok = walk_regs<NC, EPC>(
+              TreeWeights<DT, NC, false>{rp, rq, cp.tau, cp.M, cq.tau, cq.M, kp.c, izp, izq, k, L},
+              u1, L, &zt);
+      }
+    }
+  }
+  if (threadIdx.x == 0) {
+    const int slot = b * ws.kmax1 + v;
+    __hip_atomic_store(&ws.acc[slot], kept, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ws.tok[slot], tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ws.st_t[slot], st_t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ws.st_d[slot], st_d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t prev = __hip_atomic_fetch_add(&ws.counter[b], 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    L.si[0] = prev == (uint32_t)(N - 1);
+  }
+  __syncthreads();
+  if (!L.si[0] || threadIdx.x >= kWave) return;
+  // the sequence's last workgroup, wave 0 (lane n: node n)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int s0 = b * ws.kmax1;
+  const int nt = ln ? __hip_atomic_load(&ws.st_t[s0 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+  const int nd = ln ? __hip_atomic_load(&ws.st_d[s0 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+  const int nk = ln ? __hip_atomic_load(&ws.acc[s0 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -1;
+  const int ntok = ln ? __hip_atomic_load(&ws.tok[s0 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -1;
+  const unsigned long long bt = __ballot(nt != 0), bd = __ballot(nd != 0);
+  const int status = bad_tree ? 5
+                     : bt ? readlane_u32((uint32_t)nt, __ffsll((long long)bt) - 1)
+                     : bd ? readlane_u32((uint32_t)nd, __ffsll((long long)bd) - 1)
+                     : (bad_tok ? 3 : 0);
+  int32_t* ot = out_tokens + (long long)b * N;
+  int32_t* op = out_path + (long long)b * N;
+  // follow the kept children from the root (every lane in step); lane q
+  // keeps the q-th step's node and token
+  int n = 0, my_node = -1, my_tok = -1;
+  if (!status) {
+    int node = 0;
+    for (int guard = 0; guard < N; ++guard) {
+      const int ch = (int)readlane_u32((uint32_t)nk, node);
+      if (ch < 0) break;
+      const int t = (int)readlane_u32((uint32_t)tk, ch);
+      my_node = lane == n ? ch : my_node;
+      my_tok = lane == n ? t : my_tok;
+      ++n;
+      node = ch;
+    }
+    const int last = (int)readlane_u32((uint32_t)ntok, node);
+    my_tok = lane == n ? last : my_tok;
+  }
+  if (ln) {
+    ot[lane] = my_tok;
+    op[lane] = my_node;
+  }
+  if (lane == 0) {
+    out_acc[b] = n;
     if (out_status) out_status[b] = status;
     __hip_atomic_store(&ws.counter[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

@@ -53,6 +53,7 @@ struct Lds {
   int wcnt[kWaves];                 // candidates found by each wavefront
   int hist[kHistMax];               // the look-back window (-1: not a token of the row)
   float hval[kHistMax];             // its penalised logits (register path)
+  double tz[32];                    // tree verify: 1 / Z of each residual step
   uint32_t hbits[kWave];            // chunks holding a window token, hashed (chunk mod 2048)
   WaveStats ws[kWaves];
   BlockScratch bs;
