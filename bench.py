@@ -332,6 +332,26 @@ def run_extra(torch, tsr, wl, steps, warmup):
         res["beam64x4_128256_bf16"] = _rates(w.rows, w.rows * w.vocab * 2, ms)
         del bufs
 
+        # tree verify: 64 sequences, 8-node trees (root with two children, each
+        # with two, one more level on node 3), 32000 fp32 logits per node
+        w = wl.config(4)
+        nseq, N, V = 64, 8, w.vocab
+        rng = np.random.default_rng(8)
+        tgt = torch.from_numpy(rng.normal(0, 1.5, (nseq, N, V)).astype(np.float32)).to(dev)
+        dft = (tgt + torch.from_numpy(rng.normal(0, 0.7, (nseq, N, V)).astype(np.float32)).to(dev))
+        parent = torch.tensor([[-1, 0, 0, 1, 1, 2, 2, 3]] * nseq, dtype=torch.int32, device=dev)
+        # each node's token drawn from the draft at its parent, as a draft model would
+        draws = s.sample_rows(dft.view(nseq * N, V), {"temperature": 1.0}, 555).view(nseq, N)
+        toks = torch.gather(draws, 1, parent.clamp(min=0).long()).to(torch.int32).contiguous()
+        tgts = [tgt.clone() for _ in range(ROTATE // 2)]
+        dfts = [dft.clone() for _ in range(ROTATE // 2)]
+        ms = time_calls(torch, lambda i: s.tree_verify(tgts[i % (ROTATE // 2)],
+                                                       dfts[i % (ROTATE // 2)], parent, toks,
+                                                       {"temperature": 1.0}, i),
+                        steps, warmup)
+        res["tree64_n8_32000_f32_T1"] = _rates(nseq, nseq * (N + 4) * V * 4, ms)
+        del tgts, dfts, tgt, dft
+
         w = wl.config(5)
         bufs = device_batch(torch, w, 2)          # 2 x 311 MB already exceeds the 256 MB cache
         out = torch.empty(w.rows, dtype=torch.int32, device="cuda:0")

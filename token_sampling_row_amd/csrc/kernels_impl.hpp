@@ -946,8 +946,11 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(const unsigned char* tgt,
                                                       int32_t* out_status) {
   constexpr int EPC = Fmt<DT>::EPC;
   Lds& L = tsr_lds;
-  const int b = (int)blockIdx.x / N;
-  const int v = (int)blockIdx.x - b * N;
+  // node-major order: earlier nodes (the ones likely to have children, two
+  // rows to read) are dispatched before the later ones (leaves, one row)
+  const int nseq = (int)gridDim.x / N;
+  const int v = (int)blockIdx.x / nseq;
+  const int b = (int)blockIdx.x - v * nseq;
   const long long rowbytes = (long long)V * Fmt<DT>::ESZ;
   const unsigned char* tp = tgt + ((long long)b * N + v) * rowbytes;
   const unsigned char* dp = dft + ((long long)b * N + v) * rowbytes;
