@@ -170,28 +170,32 @@ __device__ __forceinline__ Cut bf16_value_cut(const RegRow<1, NC>& r, float M, f
   const int bneg = (int)ceilf((M + 4.0f) * (float)kVRes);
   const int bpos = (int)floorf((M - 4.0f) * (float)kVRes) - 1;
   auto pure = [&](int b) { return (b < kVBins - 1) & ((b >= bneg) | (b <= bpos)); };
-  // the bin of v; -inf goes to the copy's spare word past the bins
-  auto vbin = [&](float x) {
-    const float t = (M - x) * (float)kVRes;
-    const int b = t < (float)(kVBins - 1) ? (int)t : kVBins - 1;
-    return x > kNegInf ? b : kVBins;
-  };
+  // (M - v) * kVRes as one fused rounding of 32 (M - v): the same value
+  // wherever the difference is exact, i.e. in every bin but the last
+  const float M32 = M * (float)kVRes;
   uint32_t* cnt = L.vcnt + (__lane_id() & (kVCopies - 1)) * kVStride;
   __syncthreads();
-  // counts, branch-free; the elements of bins without a single value are
-  // weighed too, behind one test per chunk row (they are rare in wide rows)
+  // counts, branch-free (-inf goes to the copy's spare word past the bins);
+  // the elements of bins without a single value are weighed too, behind one
+  // test per chunk row from the chunk's lowest and highest bin (every bin in
+  // [bneg, kVBins - 2], or every bin at or below bpos, means none is there;
+  // -inf, placed in the last bin for that test, sends its chunk to the
+  // per-element test)
 #pragma unroll 1
   for (int j = 0; j < NC; ++j) {
     float v[EPC];
     r.elems(j, v);
     int b[EPC];
-    bool imp = false;
+    int lo = kVBins, hi = 0;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
-      b[e] = vbin(v[e]);
+      const int bc = (int)fminf(fmaf(v[e], -(float)kVRes, M32), (float)(kVBins - 1));
+      lo = min(lo, bc);
+      hi = max(hi, bc);
+      b[e] = v[e] > kNegInf ? bc : kVBins;
       atomicAdd(&cnt[b[e]], 1u);
-      imp = imp | ((b[e] < kVBins) & !pure(b[e]));
     }
+    const bool imp = !((hi <= kVBins - 2) & ((lo >= bneg) | (hi <= bpos)));
     if (__any(imp)) {
 #pragma unroll
       for (int e = 0; e < EPC; ++e)
@@ -258,8 +262,7 @@ __device__ __forceinline__ Cut bf16_value_cut(const RegRow<1, NC>& r, float M, f
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
       if (v[e] > kNegInf) {
-        const float t = (M - v[e]) * (float)kVRes;
-        const int b = t < (float)(kVBins - 1) ? (int)t : kVBins - 1;
+        const int b = (int)fminf(fmaf(v[e], -(float)kVRes, M32), (float)(kVBins - 1));
         const bool hit = b == d;
         const unsigned long long m = __ballot(hit);
         if (m) {   // one counter update per wavefront

@@ -440,9 +440,12 @@ __device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* tota
   for (int j = 0; j < NC; ++j) {
     float w[EPC];
     cw(j, w);
-    double s = 0.0;
+    // a chunk's EPC weights add in float (within the draw's tolerance), the
+    // partial sums beyond it in double
+    float sf = 0.0f;
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) s += (double)w[e];
+    for (int e = 0; e < EPC; ++e) sf += w[e];
+    double s = (double)sf;
     if (__any(s > 0.0)) {   // skip the lane moves for empty wave chunks
       s += dpp_perm_t<kDppXor1>(s);
       s += dpp_perm_t<kDppXor2>(s);
@@ -480,9 +483,10 @@ __device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* tota
   *total_out = L.sd[3];
   float wj[EPC];
   cw(jstar, wj);
-  double mine = 0.0;
+  float minef = 0.0f;   // the same float sum as above
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) mine += (double)wj[e];
+  for (int e = 0; e < EPC; ++e) minef += wj[e];
+  const double mine = (double)minef;
   double tot2;
   const double ex = block_excl_scan<kBlock>(mine, &tot2, L.bs);
   const bool own = mine > 0.0 && ex <= r1 && r1 < ex + mine;
