@@ -529,9 +529,12 @@ struct KeptWeights {
   float tau, M, c;
   __device__ __forceinline__ void operator()(int j, float* w) const {
     constexpr int EPC = Fmt<DT>::EPC;
-    if (r.cmax(j) >= tau) {
-      float v[EPC];
-      r.elems(j, v);
+    float v[EPC];
+    r.elems(j, v);
+    float mx = v[0];   // the chunk maximum, where the row keeps none in registers
+#pragma unroll
+    for (int e = 1; e < EPC; ++e) mx = fmaxf(mx, v[e]);
+    if ((RegRow<DT, NC>::kKeepCmax ? r.cmax(j) : mx) >= tau) {
 #pragma unroll
       for (int e = 0; e < EPC; ++e) w[e] = v[e] >= tau ? weight(v[e], M, c) : 0.0f;
     } else {
