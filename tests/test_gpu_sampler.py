@@ -217,19 +217,26 @@ def test_small_grid(dtype, V):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("V", [70000, 160001])
+@pytest.mark.parametrize("V", [70000, 151936, 160001])
 def test_general_path_wide_supports(V, dtype):
     """Kept sets far larger than the LDS candidate buffer (the histogram path),
     in rows held in registers and in rows too wide for them (streamed). In
     bf16, rows of large-magnitude logits take the exact value histogram (one
-    bf16 value per bin), rows near zero its per-element bins and fallbacks."""
+    bf16 value per bin), rows near zero its per-element bins and fallbacks;
+    a row of large positive logits spanning more than 32 below its maximum
+    puts many values in the histogram's last (mixed) bin, and -inf holes sit
+    inside chunks of otherwise single-value bins."""
     rng = np.random.default_rng(5)
     rows = [rng.normal(0, 0.3, V),                          # flat: huge nucleus
             np.round(rng.normal(0, 0.3, V), 2),             # flat with heavy ties
             np.concatenate([np.zeros(V // 2), np.full(V - V // 2, -0.001)]),  # 2 big groups
             -0.05 * np.log(rng.permutation(V) + 1.0),
             rng.normal(-12.0, 1.5, V),                      # every value |v| >= 8 (in bf16)
-            -np.log(rng.permutation(V) + 1.0) + rng.normal(0, 0.5, V)]   # mixed magnitudes
+            -np.log(rng.permutation(V) + 1.0) + rng.normal(0, 0.5, V),   # mixed magnitudes
+            rng.normal(40.0, 12.0, V)]                      # large positive, wide span
+    holes = -np.log(rng.permutation(V) + 1.0) + rng.normal(-6.0, 0.5, V)
+    holes[rng.random(V) < 0.05] = -np.inf                   # -inf holes among |v| >= 4
+    rows.append(holes)
     data = np.stack(rows).astype(np.float32)
     if dtype == "bf16":
         data = wl.f32_to_bf16_bits(data)
@@ -239,7 +246,8 @@ def test_general_path_wide_supports(V, dtype):
             dict(temperature=1.0, min_p=0.5), dict(temperature=1.0, top_k=30000),
             dict(temperature=1.0, top_k=60000, top_p=0.7),
             dict(temperature=1.0, top_k=60000, top_p=0.7, mode=1),
-            dict(temperature=0.7, top_p=0.999, min_p=0.2), dict(temperature=1.0)]
+            dict(temperature=0.7, top_p=0.999, min_p=0.2), dict(temperature=1.0),
+            dict(temperature=40.0, top_p=0.9)]   # mass far below the maximum counts
     with make_sampler(seed) as s:
         x = to_dev(data, dtype)
         for i, prm in enumerate(grid):
