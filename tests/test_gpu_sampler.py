@@ -100,7 +100,7 @@ def test_sample_strided_and_unaligned():
     rng = np.random.default_rng(4)
     V = 3001
     base = rng.normal(0, 1.5, (24, V + 5)).astype(np.float32)
-    x = to_dev(base, "f32")[:, 3:V + 3]          # unaligned rows: the streaming kernel
+    x = to_dev(base, "f32")[:, 3:V + 3]          # unaligned rows, element-wise register loads
     values = oracle.values_from_stored(np.ascontiguousarray(base[:, 3:V + 3]), "f32")
     seed = 5150
     with make_sampler(seed) as s:
@@ -110,6 +110,38 @@ def test_sample_strided_and_unaligned():
             refs = [oracle.sample_row(values[b], prm, seed, b, i) for b in range(24)]
             got = run_sample(s, x, prm, i, diag=True)
             compare(got, refs, list(range(24)), values, greedy=prm["temperature"] == 0.0)
+
+
+@pytest.mark.parametrize("dtype,V", [("f32", 50257), ("f32", 77823), ("bf16", 50257),
+                                     ("bf16", 128255), ("bf16", 151935), ("bf16", 160001)])
+def test_sample_unaligned_contiguous(dtype, V):
+    """A contiguous batch of an odd vocabulary: rows start on every 2- or
+    4-byte offset, so they are read element-wise into the register rows (the
+    last case is wider than the register file and streams); narrow and wide
+    kept sets, no filter and greedy, against the oracle on every row."""
+    rng = np.random.default_rng(V + (7 if dtype == "bf16" else 0))
+    rows = [-a * np.log(rng.permutation(V) + 1.0) + rng.normal(0, 0.5, V)
+            for a in np.linspace(0.2, 1.4, 11)]
+    r = rng.normal(0, 1, V)
+    r[rng.random(V) < 0.3] = -np.inf
+    rows.append(r)
+    data = np.stack(rows).astype(np.float32)
+    if dtype == "bf16":
+        data = wl.f32_to_bf16_bits(data)
+    values = vals(data, dtype)
+    seed = 6060 + V
+    grid = [dict(temperature=0.9, top_k=50, top_p=0.95, min_p=0.1), dict(temperature=1.0),
+            dict(temperature=1.5, top_p=0.9), dict(temperature=0.0),
+            dict(temperature=0.8, min_p=0.2)]
+    with make_sampler(seed) as s:
+        x = to_dev(data, dtype)
+        assert x.stride(0) == V
+        for i, prm in enumerate(grid):
+            print_case("unaligned_contiguous", dtype=dtype, V=V, params=prm)
+            refs = [oracle.sample_row(values[b], prm, seed, b, i) for b in range(len(rows))]
+            got = run_sample(s, x, prm, i, diag=True)
+            compare(got, refs, list(range(len(rows))), values,
+                    greedy=prm["temperature"] == 0.0)
 
 
 def test_greedy_strided_and_unaligned(sampler):

@@ -49,10 +49,10 @@ def instance_units() -> dict[str, str]:
                 units[f"i_sample_wide_{dt}_{nc}.hip"] = head + (
                     f"template __global__ void sample_kernel<{dt}, {nc}, true, 0>(const unsigned "
                     "char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);\n}\n")
-            # an allowed-token set (1) or a repetition penalty only (2); bf16
-            # takes the wide finish as well
+            # an allowed-token set (1), a repetition penalty only (2), rows
+            # not 16-byte aligned (3); bf16 takes the wide finish as well
             wide = "true" if dt == 1 else "false"
-            for ext, tag in ((1, "mask"), (2, "rep")):
+            for ext, tag in ((1, "mask"), (2, "rep"), (3, "unal")):
                 units[f"i_sample_{tag}_{dt}_{nc}.hip"] = head + (
                     f"template __global__ void sample_kernel<{dt}, {nc}, {wide}, {ext}>(const "
                     "unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);\n}\n")

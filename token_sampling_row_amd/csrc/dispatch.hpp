@@ -39,6 +39,10 @@ constexpr int kVerifyNcs[] = {1, 2, 4, 8, 16};
       const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
   extern template __global__ void sample_kernel<1, N, true, 2>(                              \
       const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
+  extern template __global__ void sample_kernel<0, N, false, 3>(                             \
+      const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
+  extern template __global__ void sample_kernel<1, N, true, 3>(                              \
+      const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
   extern template __global__ void beam_kernel<0, N>(const unsigned char*, long long, int, int,  \
                                                     int, int, const double*, BeamWs,          \
                                                     int32_t*, int32_t*, double*, int32_t*);   \

@@ -370,13 +370,14 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel_stream(const unsigned ch
 
 // The streaming view of row `row` (for the streaming finish and the
 // diagnostics), with the allowed-token mask (EXT 1) and the repetition
-// penalty (EXT 1 or 2, when asked for).
+// penalty (EXT 1 or 2, when asked for); EXT 3 rows are not 16-byte aligned.
 template <int DT, int EXT>
 __device__ __forceinline__ StreamRow<DT> row_stream_view(const unsigned char* p, int V,
                                                          const KParams& kp, int row) {
-  return StreamRow<DT>(p, V, true,
+  return StreamRow<DT>(p, V, EXT != 3,
                        EXT == 1 ? kp.allowed + (long long)row * kp.allowed_stride : nullptr,
-                       (EXT != 0 && (kp.flags & F_REP)) ? kp.hist_len : 0, kp.rpen);
+                       ((EXT == 1 || EXT == 2) && (kp.flags & F_REP)) ? kp.hist_len : 0,
+                       kp.rpen);
 }
 
 // WIDE (bf16): rows whose kept set the candidate bound cannot narrow are
@@ -385,7 +386,9 @@ __device__ __forceinline__ StreamRow<DT> row_stream_view(const unsigned char* p,
 // a small top-k, so the common instance keeps its registers and code size.
 // EXT 1: an allowed-token bitmask applies (constrained decoding), staged in
 // LDS and applied in pass A, and a repetition penalty may (F_REP); EXT 2: a
-// repetition penalty applies. Their bf16 instances are WIDE.
+// repetition penalty applies; EXT 3: rows that do not start on a 16-byte
+// boundary (an odd row stride), read element-wise into the same registers.
+// The bf16 instances of EXT 1-3 are WIDE.
 template <int DT, int NC, bool WIDE, int EXT>
 __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* logits,
                                                         long long stride_bytes, int V,
@@ -395,7 +398,7 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   Lds& L = tsr_lds;
   const int row = blockIdx.x;
   const unsigned char* p = logits + (long long)row * stride_bytes;
-  constexpr bool MASK = EXT == 1, REP = EXT != 0;
+  constexpr bool MASK = EXT == 1, REP = EXT == 1 || EXT == 2, UNAL = EXT == 3;
   KParams kp = kp0;
   if ((kp.flags & F_ROWP) && !row_kparams(kp, row, V)) {
     write_row(row, -1, kRowBadParam, 0, kNegInf, 0.0, kNaN, kNaN, out, dg);
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
     if ((int)threadIdx.x < x.hn) x.hv = kp.hist[(long long)row * kp.hist_stride + threadIdx.x];
   }
   if constexpr (MASK) stage_mask(kp.allowed + (long long)row * kp.allowed_stride, V, L);
-  r.load(p, V, ragged != 0);
+  r.template load<UNAL>(p, V, ragged != 0);
   if constexpr (MASK) mask_ready<NC>();
   const bool greedy = (kp.flags & F_GREEDY) != 0;
   const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);   // while the loads fly
