@@ -87,7 +87,7 @@ struct RegRow {
   // Chunks at or past `nwhole` come back as zeros from the range check and are
   // replaced in pass A of reg_stats (by -inf, or by `tail` for the partial
   // chunk of a ragged row), so no wait is forced here. UNALIGNED rows are read
-  // element-wise.
+  // in dwords (load_chunk_unaligned).
   template <bool UNALIGNED = false>
   __device__ __forceinline__ void load(const unsigned char* p, int V, bool ragged) {
     if constexpr (UNALIGNED) {
@@ -96,7 +96,7 @@ struct RegRow {
       tail = neg_inf_chunk<DT>();
 #pragma unroll
       for (int j = 0; j < NC; ++j)
-        put(j, load_chunk_slow<DT>(p, (long long)j * kBlock + threadIdx.x, V));
+        put(j, load_chunk_unaligned<DT>(p, (long long)j * kBlock + threadIdx.x, V));
     } else {
       nwhole = V / EPC;
       jfull = nwhole / kBlock;

@@ -39,9 +39,9 @@ struct StreamRow {
   __device__ __forceinline__ uint4 chunk(int j) const {
     const long long c = chunk_id(j);
     if (c * EPC >= V) return neg_inf_chunk<DT>();
-    const uint4 t = (aligned && (c + 1) * EPC <= V)
-                        ? *reinterpret_cast<const uint4*>(p + c * EPC * Fmt<DT>::ESZ)
-                        : load_chunk_slow<DT>(p, c, V);
+    const uint4 t = !aligned                ? load_chunk_unaligned<DT>(p, c, V)
+                    : ((c + 1) * EPC <= V) ? *reinterpret_cast<const uint4*>(p + c * EPC * Fmt<DT>::ESZ)
+                                           : load_chunk_slow<DT>(p, c, V);
     uint4 m = mask ? apply_mask<DT>(t, chunk_mask_bits<DT>(mask, c)) : t;
     if (hn > 0) {   // window tokens in this chunk (the hashed flag first)
       const Lds& L = tsr_lds;
