@@ -322,7 +322,13 @@ def run_extra(torch, tsr, wl, steps, warmup):
                         steps, warmup)
         res["batch256_128256_bf16_chain_rep64"] = _rates(
             w.rows, w.rows * w.vocab * 2 + hist.numel() * 4, ms)
-        del bufs
+        # the same rows one id shorter, contiguous: rows start 2 bytes apart
+        # from a 16-byte boundary (an odd vocabulary)
+        odd = [b[:, : w.vocab - 1].contiguous() for b in bufs]
+        ms = time_calls(torch, lambda i: s.sample_rows(odd[i % ROTATE], w.runs[0], i, out=out),
+                        steps, warmup)
+        res["batch256_128255_bf16_chain_unaligned"] = _rates(w.rows, w.rows * (w.vocab - 1) * 2, ms)
+        del bufs, odd
 
         # beam-search step: 64 groups of 4 beams over the same 256 x 128256 bf16 logits
         w = wl.config(3)
