@@ -144,6 +144,24 @@ def test_sample_unaligned_contiguous(dtype, V):
                     greedy=prm["temperature"] == 0.0)
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 50257), ("bf16", 128255), ("f32", 160001)])
+def test_greedy_unaligned_contiguous(sampler, dtype, V):
+    """greedy_argmax over a contiguous batch of an odd vocabulary (rows off
+    16-byte boundaries; the last case streams), ties and -inf included."""
+    rng = np.random.default_rng(V)
+    data = np.round(rng.normal(0, 2, (9, V)), 1).astype(np.float32)
+    data[1, :] = -np.inf
+    data[1, V - 1] = 0.5                       # only the last id is finite
+    data[2, :] = 3.0                           # one tie group: id 0
+    data[3, ::2] = -np.inf
+    if dtype == "bf16":
+        data = wl.f32_to_bf16_bits(data)
+    values = vals(data, dtype)
+    print_case("greedy_unaligned", dtype=dtype, V=V)
+    got = sampler.greedy_argmax(to_dev(data, dtype)).cpu().numpy()
+    assert got.tolist() == [int(np.argmax(r)) for r in values]
+
+
 def test_greedy_strided_and_unaligned(sampler):
     rng = np.random.default_rng(3)
     V = 1001
