@@ -413,12 +413,12 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
     x.row = p;
     if ((int)threadIdx.x < x.hn) x.hv = kp.hist[(long long)row * kp.hist_stride + threadIdx.x];
   }
-  if constexpr (MASK) stage_mask(kp.allowed + (long long)row * kp.allowed_stride, V, L);
+  MaskRegs<DT, NC> mk;
+  if constexpr (MASK) mk.load(kp.allowed + (long long)row * kp.allowed_stride, V);
   r.template load<UNAL>(p, V, ragged != 0);
-  if constexpr (MASK) mask_ready<NC>();
   const bool greedy = (kp.flags & F_GREEDY) != 0;
   const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);   // while the loads fly
-  const RowStats st = reg_stats<MASK, REP>(r, !greedy && joint_top_p(kp), kp.c, L, V, x);
+  const RowStats st = reg_stats<MASK, REP>(r, !greedy && joint_top_p(kp), kp.c, L, V, x, &mk);
   if (st.status != 0) {
     write_row(row, -1, st.status, 0, kNegInf, 0.0, kNaN, kNaN, out, dg);
     zero_probs(dg, row, V);

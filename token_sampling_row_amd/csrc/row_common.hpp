@@ -18,7 +18,6 @@ constexpr int kBins = 1024;   // bins of every histogram level
 constexpr int kLogRes = 16;   // log-probability bins per unit of log2(p / p_max)
 constexpr int kWalkBatch = 40;  // chunk rows per step of the inverse-CDF walk
 constexpr int kWaves = kBlock / kWave;
-constexpr int kMaskWords = 8192;   // allowed-token words staged in LDS (262144 tokens)
 constexpr int kVRes = 32;        // bf16 value histogram: bins per logit below the max
 constexpr int kVBins = 1024;     //   bins (32 logits)
 constexpr int kVCopies = 4;      //   count copies (lane & 3): fewer lanes per address
@@ -39,7 +38,6 @@ struct Lds {
       double pref[kCap + 1];          // exclusive prefix of candidate weights
     };
     uint32_t vcnt[kVCopies * kVStride];   // bf16 value histogram: per-copy counts
-    uint32_t vmask[kMaskWords];           // the row's allowed-token bitmask (pass A)
     unsigned long long own[kBlock];       // per thread: window entries in its chunks (after pass A)
     double jrow[kWalkBatch][kWaves * 4];  // walk: per (chunk row, 16-lane row) sums
   };

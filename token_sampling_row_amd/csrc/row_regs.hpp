@@ -134,31 +134,43 @@ struct RegRow {
   __device__ __forceinline__ void elems(int j, float* v) const { unpack<DT>(get(j), v); }
 };
 
-// Constrained decoding: row m of the allowed-token mask (ceil(V/32) words)
-// is staged in L.vmask with direct global-to-LDS loads, issued before the
-// row's own loads; mask_ready<NC>() after those waits until at most NC loads
-// are outstanding (so the mask's have landed, the row's may still fly) and a
-// barrier makes every wavefront's words visible. Pass A then replaces the
-// disallowed elements by -inf as each chunk lands.
-__device__ __forceinline__ void stage_mask(const uint32_t* m, int V, Lds& L) {
-  const int words = (V + 31) >> 5;
-  const int wid = threadIdx.x / kWave;
-#pragma nounroll
-  for (int k = 0; k * kBlock < words; ++k) {
-    const int w = k * kBlock + (int)threadIdx.x;
-    if (w < words)
-      __builtin_amdgcn_global_load_lds(m + w, &L.vmask[k * kBlock + wid * kWave], 4, 0, 0);
+// Constrained decoding: the allowed-token mask words of a register row, in
+// registers. Every chunk row j of a G-lane group (G = 32 / EPC chunks per
+// word) reads one mask word, so lane t of the group loads the word of chunk
+// row q*G + (t mod G) for q < NQ, and chunk row j's word reaches the group's
+// lanes from lane j mod G (DPP quad permute for bf16, a swizzle for fp32).
+// Ordinary loads issued before the row's: their waits are the compiler's, no
+// LDS and no barrier. Words past the mask read as 0 (disallowed).
+template <int DT, int NC>
+struct MaskRegs {
+  static constexpr int G = 32 / Fmt<DT>::EPC;
+  static constexpr int NQ = (NC + G - 1) / G;
+  uint32_t w[NQ];
+  __device__ __forceinline__ void load(const uint32_t* m, int V) {
+    const int words = (V + 31) >> 5;
+    const int t = (int)threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int jr = q * G + t % G;
+      const int wi = jr * (kBlock / G) + t / G;
+      const uint32_t x = m[wi < words ? wi : words - 1];
+      w[q] = (jr < NC && wi < words) ? x : 0u;
+    }
+    sched_fence();   // issued before the row's loads, so they land first
   }
-  sched_fence();   // the row's loads are issued after these (mask_ready counts on it)
-}
-template <int NC>
-__device__ __forceinline__ void mask_ready() {
-  static_assert(NC < 64, "vmcnt holds 6 bits");
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt((NC & 0xF) | ((NC >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
+  template <int J>
+  __device__ __forceinline__ uint32_t get() const {
+    constexpr int R = J % G;
+    const int x = (int)w[J / G];
+    if constexpr (G == 4) {
+      return (uint32_t)__builtin_amdgcn_update_dpp(0, x, R | (R << 2) | (R << 4) | (R << 6), 0xF,
+                                                   0xF, false);
+    } else {
+      static_assert(G == 8, "fp32 or bf16");
+      return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x18 | (R << 5));
+    }
+  }
+};
 
 // Bit j set iff pred(j) holds in some lane (pred is evaluated by every lane;
 // call with the whole wavefront active). Unrolled: NC compares and a few
@@ -223,41 +235,41 @@ struct RowStats {
 // per thread). That is a lower bound of the row's
 // weight sum Z, enough to settle JOINT top-p whenever the nucleus is not
 // close to the cut.
-// MASK: apply the staged allowed-token mask (stage_mask, V tokens) to each
+// MASK: apply the allowed-token mask (mk, loaded before the row) to each
 // chunk first, and count the allowed tokens (a row with few of them is
 // resolved over all its finite elements). Then, when x holds a look-back
 // window, the repetition penalty: wave 0 reads the window tokens' logits back
 // and publishes their penalised values, and the thread that holds a window
 // token puts its new value in place and refreshes its maxima (REP instances).
 // Pass A over the registers as the loads land (see reg_stats); MASKED: the
-// staged allowed-token mask is applied to each chunk first. Returns the
+// allowed-token mask words (mk) are applied to each chunk first and the
+// allowed ids counted in *nallow. Returns the
 // thread's maximum.
 // ONLINE: also the thread's weight sum relative to its own maximum, formed as
 // the chunks land (the running sum is rescaled whenever the running maximum
 // grows), in *z; c = log2(e) / T.
+template <int J, int NC, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (J < NC) {
+    f(std::integral_constant<int, J>{});
+    static_for<J + 1, NC>(f);
+  }
+}
+
 template <bool MASKED, bool ONLINE = false, int DT, int NC>
 __device__ __forceinline__ float reg_pass_a(RegRow<DT, NC>& r, const Lds& L, float c = 0.0f,
-                                            double* z = nullptr) {
+                                            double* z = nullptr,
+                                            const MaskRegs<DT, NC>* mk = nullptr,
+                                            int* nallow = nullptr) {
   float tmax = kNegInf;
   double zr = 0.0;
-  // thread t's chunk j takes bits tsh.. of mask word j * kWpr + tw; the words
-  // of the next two chunk rows are read ahead of their use
-  constexpr int kCpw = 32 / Fmt<DT>::EPC;   // chunks per mask word
-  constexpr int kWpr = kBlock / kCpw;       // mask words per chunk row
-  const int tw = (int)threadIdx.x / kCpw;
-  const uint32_t tsh = ((uint32_t)threadIdx.x % kCpw) * Fmt<DT>::EPC;
-  uint32_t mw0 = 0u, mw1 = 0u;
-  if constexpr (MASKED) {
-    mw0 = L.vmask[tw];
-    if (NC > 1) mw1 = L.vmask[kWpr + tw];
-  }
-#pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    const uint32_t mwc = mw0;
-    if constexpr (MASKED) {
-      mw0 = mw1;
-      if (j + 2 < NC) mw1 = L.vmask[(j + 2) * kWpr + tw];
-    }
+  int na = 0;
+  // thread t's chunk j takes bits tsh.. of its chunk row's mask word
+  const uint32_t tsh = ((uint32_t)threadIdx.x % (32 / Fmt<DT>::EPC)) * Fmt<DT>::EPC;
+  static_for<0, NC>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    uint32_t mwc = 0u;
+    if constexpr (MASKED) mwc = mk->template get<j>();
     uint4 t = r.get(j);
     asm volatile("" : "+v"(t.x), "+v"(t.y), "+v"(t.z), "+v"(t.w));
     t = r.settle(j, t);
@@ -267,6 +279,7 @@ __device__ __forceinline__ float reg_pass_a(RegRow<DT, NC>& r, const Lds& L, flo
       // grammar's small or near-complete sets) take one select per dword
       constexpr uint32_t kAll = (1u << Fmt<DT>::EPC) - 1u;
       const uint32_t bits = (mwc >> tsh) & kAll;
+      na += __builtin_popcount(bits);
       if (__any(bits != 0u && bits != kAll)) {
         t = apply_mask<DT>(t, bits);
       } else {
@@ -294,8 +307,9 @@ __device__ __forceinline__ float reg_pass_a(RegRow<DT, NC>& r, const Lds& L, flo
     }
     tmax = fmaxn(tmax, m);
     asm volatile("" : "+v"(tmax));
-  }
+  });
   if constexpr (ONLINE) *z = zr;
+  if constexpr (MASKED) *nallow = na;
   return tmax;
 }
 
@@ -303,17 +317,14 @@ __device__ __forceinline__ float reg_pass_a(RegRow<DT, NC>& r, const Lds& L, flo
 // pass A) instead of a lower bound.
 template <bool MASK = false, bool REP = false, bool ZEXACT = false, int DT, int NC>
 __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, float c, Lds& L,
-                                              int V = 0, const RowExtras& x = RowExtras{}) {
+                                              int V = 0, const RowExtras& x = RowExtras{},
+                                              const MaskRegs<DT, NC>* mk = nullptr) {
+  // allowed ids, counted by chunk in pass A (bits of ids past V in the last
+  // chunk may be set: an over-count)
   int nallow = 0x7FFFFFFF;
-  if constexpr (MASK) {
-    // (bits of ids past V in the last word may be set: an over-count)
-    nallow = 0;
-    for (int w = threadIdx.x; w < ((V + 31) >> 5); w += kBlock) nallow += __builtin_popcount(L.vmask[w]);
-  }
   double zown = 0.0;
-  float tmax = reg_pass_a<MASK, ZEXACT>(r, L, c, &zown);
+  float tmax = reg_pass_a<MASK, ZEXACT>(r, L, c, &zown, mk, &nallow);
   if (REP && x.hn > 0) {
-    if constexpr (MASK) __syncthreads();   // L.own shares LDS with the mask words
     if (threadIdx.x < kWave) {
       // wave 0: each window token's logit, read back from the row (one per
       // lane, in parallel) and penalised once here
