@@ -9,7 +9,7 @@ hipError_t launch_sample_dt1(const unsigned char* p, int rows, int V, long long 
   const int nc = pick_nc(chunks_per_thread(1, V), kRowNcs, 8);
   const int ext = (kp.flags & F_MASK) ? 1 : (kp.flags & F_REP) ? 2 : 0;
   // wider than the register file, or unaligned rows under a mask or a
-  // penalty: stream (other unaligned rows take the element-wise register load)
+  // penalty: stream (other unaligned rows are read in dwords into registers)
   if (nc == 0 || (!aligned && ext != 0)) {
     hipLaunchKernelGGL((sample_kernel_stream<1>), dim3(rows), dim3(kBlock), 0, s, p,
                        stride_bytes, V, aligned, kp, out, dg);

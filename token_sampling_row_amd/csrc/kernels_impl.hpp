@@ -384,10 +384,11 @@ __device__ __forceinline__ StreamRow<DT> row_stream_view(const unsigned char* p,
 // finished over the registers (reg_general, then the walk) instead of by the
 // streaming path. A separate instance, chosen on the host for filters without
 // a small top-k, so the common instance keeps its registers and code size.
-// EXT 1: an allowed-token bitmask applies (constrained decoding), staged in
-// LDS and applied in pass A, and a repetition penalty may (F_REP); EXT 2: a
-// repetition penalty applies; EXT 3: rows that do not start on a 16-byte
-// boundary (an odd row stride), read element-wise into the same registers.
+// EXT 1: an allowed-token bitmask applies (constrained decoding), its words
+// read into registers ahead of the row and applied in pass A, and a
+// repetition penalty may (F_REP); EXT 2: a repetition penalty applies; EXT 3:
+// rows that do not start on a 16-byte boundary (an odd row stride), read in
+// dwords into the same registers.
 // The bf16 instances of EXT 1-3 are WIDE.
 template <int DT, int NC, bool WIDE, int EXT>
 __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* logits,
