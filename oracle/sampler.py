@@ -35,7 +35,7 @@ __all__ = [
     "greedy_batch", "accept_probability", "residual", "spec_verify_row",
     "spec_verify_batch", "acceptance_probability", "expected_accepted_prefix",
     "values_from_stored", "allowed_from_words", "mask_logits", "log_p_tilde",
-    "round_to_element", "repetition_penalty", "HISTORY_MAX",
+    "round_to_element", "repetition_penalty", "HISTORY_MAX", "Decision",
 ]
 
 ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BADTOKEN = 0, 1, 2, 3
@@ -308,10 +308,16 @@ class RowResult:
     logprob: float = float("nan")   # log p~(token); 0 for greedy; nan for bad rows
 
     @property
-    def margin(self) -> float:
+    def margin_support(self) -> float:
+        """Nearest top-p or min-p decision of the kept set (inf without one)."""
         if self.support is None:
             return float("inf")
-        return min(self.margin_draw, self.support.margin_p, self.support.margin_m)
+        return min(self.support.margin_p, self.support.margin_m)
+
+    @property
+    def margin(self) -> float:
+        """Nearest decision of any kind: the kept set's or the draw's."""
+        return min(self.margin_draw, self.margin_support)
 
 
 def sample_row(l: np.ndarray, params, seed: int, row: int, step: int,
@@ -390,15 +396,34 @@ def expected_accepted_prefix(alphas) -> float:
 
 
 @dataclass
+class Decision:
+    """Margins of the comparisons taken at one verify position (or tree node),
+    each the distance of a quantity from the cut that decides it:
+      accept   |u0 - a| for the acceptance test(s) u0 < a (eq. 39.3), the
+               smallest over the candidates tested there; inf if none;
+      support  the nearest top-p or min-p decision of the chains that shape
+               p~ and q~ there (they move a, the residual and the draw);
+      draw     the draw's uniform from the nearer end of the drawn token's
+               CDF interval (residual, fallback or bonus draw); inf if no
+               token was drawn there."""
+    accept: float = float("inf")
+    support: float = float("inf")
+    draw: float = float("inf")
+
+    def smallest(self) -> float:
+        return min(self.accept, self.support, self.draw)
+
+
+@dataclass
 class VerifyResult:
     tokens: list                  # K + 1 entries, -1 padded
     n_accepted: int
     status: int
-    margins: list                 # per consulted position: smallest decision margin
+    margins: list                 # one Decision per consulted position, in order
 
 
 def spec_verify_row(target: np.ndarray, draft: np.ndarray, draft_tokens, params,
-                    seed: int, row: int, step: int) -> VerifyResult:
+                    seed: int, row: int, step: int, uniforms=None) -> VerifyResult:
     """Verify K drafted tokens of one sequence [P3 "The Algorithm"; P1
     "Speculative decoding"; P4 "Speculative decoding"; P2 section 39.4].
 
@@ -417,6 +442,9 @@ def spec_verify_row(target: np.ndarray, draft: np.ndarray, draft_tokens, params,
     Greedy (temperature 0): keep a draft iff it is the target's argmax, on the
     first mismatch emit the argmax, and the bonus is the argmax of row K
     (P1 "Speculative decoding"); draft rows are not read.
+
+    ``uniforms`` (tests only) replaces the Philox pair (u0[j], u1[j]) of every
+    position by the given [K+1, 2] array.
     """
     prm = Params.of(params)
     check_params(prm)
@@ -449,31 +477,34 @@ def spec_verify_row(target: np.ndarray, draft: np.ndarray, draft_tokens, params,
         out.append(greedy_token(target[K]))
         return VerifyResult(out, K, ROW_OK, margins)
 
-    words = draw_words(seed, [row] * (K + 1), np.arange(K + 1), step, DOMAIN_SPEC)
-    u0 = uniforms_from_words(words[:, 0])
-    u1 = uniforms_from_words(words[:, 1])
+    if uniforms is None:
+        words = draw_words(seed, [row] * (K + 1), np.arange(K + 1), step, DOMAIN_SPEC)
+        u0 = uniforms_from_words(words[:, 0])
+        u1 = uniforms_from_words(words[:, 1])
+    else:
+        u0, u1 = np.asarray(uniforms, dtype=np.float64).T
     for j in range(K):
         sp = support(target[j], prm)
         sq = support(draft[j], prm)
         x = xs[j]
         a = accept_probability(sp.p_tilde, sq.p_tilde, x)
-        m = min(abs(u0[j] - a), sp.margin_p, sp.margin_m, sq.margin_p, sq.margin_m)
+        d = Decision(accept=abs(u0[j] - a),
+                     support=min(sp.margin_p, sp.margin_m, sq.margin_p, sq.margin_m))
+        margins.append(d)
         if u0[j] < a:
             out.append(x)
-            margins.append(m)
             continue
         r = residual(sp.p_tilde, sq.p_tilde)
         if r.sum() > 0.0:
-            tok, md = draw_from(r, r > 0.0, u1[j])
+            tok, d.draw = draw_from(r, r > 0.0, u1[j])
         else:
-            tok, md = draw_from(sp.p_tilde, sp.keep, u1[j])
+            tok, d.draw = draw_from(sp.p_tilde, sp.keep, u1[j])
         out.append(tok)
-        margins.append(min(m, md))
         return VerifyResult(out + [-1] * (K + 1 - len(out)), j, ROW_OK, margins)
     sp = support(target[K], prm)
     tok, md = draw_from(sp.p, sp.keep, u0[K])
     out.append(tok)
-    margins.append(min(md, sp.margin_p, sp.margin_m))
+    margins.append(Decision(support=min(sp.margin_p, sp.margin_m), draw=md))
     return VerifyResult(out, K, ROW_OK, margins)
 
 

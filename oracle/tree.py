@@ -17,8 +17,8 @@ from dataclasses import dataclass
 import numpy as np
 
 from .philox import DOMAIN_TREE, draw_words, uniforms_from_words
-from .sampler import (ROW_BADTOKEN, ROW_OK, Params, check_params, draw_from, greedy_token,
-                      row_status, support)
+from .sampler import (ROW_BADTOKEN, ROW_OK, Decision, Params, check_params, draw_from,
+                      greedy_token, row_status, support)
 
 __all__ = ["TREE_MAX_NODES", "TreeResult", "tree_children", "tree_verify_row", "INVALID_TREE"]
 
@@ -31,7 +31,7 @@ class TreeResult:
     tokens: list       # emitted tokens: the accepted nodes' tokens, then one drawn token
     path: list         # the accepted nodes, root first excluded
     status: int
-    margins: list      # per decision: distance of the uniform from its cut (parity band)
+    margins: list      # one Decision per visited node (the root first), in order
 
 
 def tree_children(parent) -> list:
@@ -103,10 +103,13 @@ def tree_verify_row(target, draft, parent, tokens, params, seed: int, row: int,
             v = nxt
     while True:
         sp = support(target[v], prm)
+        d = Decision(support=min(sp.margin_p, sp.margin_m))
+        margins.append(d)
         p = sp.p_tilde.copy()
         kept = None
         if ch[v]:
             sq = support(draft[v], prm)
+            d.support = min(d.support, sq.margin_p, sq.margin_m)
             q = sq.p_tilde
             pos = [v * 32 + c for c in range(len(ch[v]))]
             u0 = uniforms_from_words(draw_words(seed, [row] * len(pos), np.array(pos), step,
@@ -114,8 +117,7 @@ def tree_verify_row(target, draft, parent, tokens, params, seed: int, row: int,
             for c, child in enumerate(ch[v]):
                 x = toks[child]
                 a = min(1.0, p[x] / max(q[x], 1e-300))
-                margins.append(min(abs(u0[c] - a), sp.margin_p, sp.margin_m, sq.margin_p,
-                                   sq.margin_m))
+                d.accept = min(d.accept, abs(u0[c] - a))
                 if u0[c] < a:
                     kept = child
                     break
@@ -129,7 +131,6 @@ def tree_verify_row(target, draft, parent, tokens, params, seed: int, row: int,
             continue
         u1 = float(uniforms_from_words(draw_words(seed, [row], v * 32, step, DOMAIN_TREE)[:, 1])[0])
         keep = p > 0.0
-        tok, md = draw_from(p, keep, u1)
-        margins.append(min(md, sp.margin_p, sp.margin_m))
+        tok, d.draw = draw_from(p, keep, u1)
         out.append(tok)
         return TreeResult(out, path, ROW_OK, margins)

@@ -1,33 +1,23 @@
 """Shared helpers for the GPU parity tests: run the HIP path through the C ABI,
 run the oracle on the same stored bits, and compare row by row.
 
-Parity rule (tolerances written here, used by every GPU test):
-  * status, greedy tokens: bit-exact.
-  * kept set (|S| and the smallest kept logit): exact, unless the oracle's
-    nearest top-p / min-p decision lies within BAND of its cut.
-  * sampled token: exact, unless the oracle's uniform lies within BAND of the
-    end of the chosen token's CDF interval (or a kept-set decision is within
-    BAND, which can move the interval).
-  * kept probabilities p~ (eq. 39.2): relative error <= PROB_RTOL where the
-    oracle's p~ is a normal float32; kept mass: relative error <= PROB_RTOL.
+Parity rule: oracle/parity.py states it (BAND, PROB_RTOL) and applies it row
+by row; the one tolerance added here:
   * log p~ of the drawn token (where token and kept set agree): absolute
     error <= LOGP_TOL * max(1, |log p~|). The kernel forms it in float64 from
     float32 weights exp2((v - M) * log2(e) / T), each within a few float32
     ulps (~3e-7 relative, so ~3e-7 absolute in the log), and rounds the result
     to float32 (2^-24 relative); 1e-5 covers both with room to spare.
-BAND = 1e-6 and PROB_RTOL = 1e-5 are the tolerances the work is held to.
 """
 from __future__ import annotations
-
-from dataclasses import dataclass, field
 
 import numpy as np
 import pytest
 
-BAND = 1e-6
-PROB_RTOL = 1e-5
+from oracle.parity import (BAND, F32_NORMAL_MIN, PROB_RTOL, Tally,  # noqa: F401
+                           compare_sample_row)
+
 LOGP_TOL = 1e-5
-F32_NORMAL_MIN = 1.1754943508222875e-38
 
 torch = pytest.importorskip("torch")
 
@@ -152,50 +142,30 @@ def compare_logprob(gpu: dict, refs: list, rows) -> int:
     return n
 
 
-@dataclass
-class Tally:
-    rows: int = 0
-    token_excused: int = 0
-    support_excused: int = 0
-    in_band: int = 0
-    notes: list = field(default_factory=list)
-
-
-def compare(gpu: dict, refs: list, rows, values: np.ndarray, greedy=False, tally=None,
-            check_probs_rows=None):
-    """Compare GPU outputs with oracle RowResults; raise on a mismatch outside the band."""
-    tally = tally or Tally()
+def compare(gpu: dict, refs: list, rows, values: np.ndarray = None, greedy=False, tally=None,
+            check_probs_rows=None) -> Tally:
+    """Compare GPU outputs with oracle RowResults row by row under the parity
+    rule of oracle.parity (raises ParityError on a mismatch no margin excuses);
+    returns the tally of rows, rows in band and excused mismatches."""
+    tally = tally if tally is not None else Tally()
     for i, b in enumerate(rows):
-        r = refs[i]
-        tally.rows += 1
-        if "status" in gpu:
-            assert gpu["status"][b] == r.status, (b, gpu["status"][b], r.status)
-        if greedy or r.status != 0:
-            assert gpu["token"][b] == r.token, (b, gpu["token"][b], r.token)
-            continue
-        s = r.support
-        sup_margin = min(s.margin_p, s.margin_m)
-        if sup_margin <= BAND or r.margin <= BAND:
-            tally.in_band += 1
-        if "kept_count" in gpu:
-            same = gpu["kept_count"][b] == s.kept_count and \
-                np.float32(gpu["threshold"][b]) == np.float32(s.threshold)
-            if not same:
-                assert sup_margin <= BAND, (b, gpu["kept_count"][b], s.kept_count,
-                                            gpu["threshold"][b], s.threshold, sup_margin)
-                tally.support_excused += 1
-                continue
-            if "kept_mass" in gpu:
-                assert abs(gpu["kept_mass"][b] - s.kept_mass) <= PROB_RTOL * s.kept_mass, \
-                    (b, gpu["kept_mass"][b], s.kept_mass)
-        if gpu["token"][b] != r.token:
-            assert r.margin <= BAND, (b, gpu["token"][b], r.token, r.margin, r.u)
-            tally.token_excused += 1
+        probs = None
         if "probs" in gpu and (check_probs_rows is None or b in check_probs_rows):
-            pg = gpu["probs"][b].astype(np.float64)
-            pr = s.p_tilde
-            assert np.all(pg[~s.keep] == 0.0), b
-            norm = pr >= F32_NORMAL_MIN
-            err = np.abs(pg - pr)[norm] / pr[norm]
-            assert err.max(initial=0.0) <= PROB_RTOL, (b, err.max())
+            probs = gpu["probs"][b]
+        compare_sample_row(
+            tally, b, refs[i], gpu["token"][b],
+            status=gpu["status"][b] if "status" in gpu else None,
+            kept_count=gpu["kept_count"][b] if "kept_count" in gpu else None,
+            threshold=gpu["threshold"][b] if "threshold" in gpu else None,
+            kept_mass=gpu["kept_mass"][b] if "kept_mass" in gpu else None,
+            probs=probs, greedy=greedy)
     return tally
+
+
+def report(name: str, t: Tally) -> None:
+    """One line per compared workload: the counts the parity rule asks for."""
+    d = t.as_dict()
+    print(f"parity {name}: rows={d['rows']} in_band={d['in_band']} "
+          f"in_1e-9={d['in_tight_band']} support_excused={d['support_excused']} "
+          f"token_excused={d['token_excused']} excused_above_1e-9={d['excused_above_1e-9']} "
+          f"out_of_band={d['out_of_band']} max_p_rel_err={d['max_prob_rel_err']:.3g}", flush=True)

@@ -2,8 +2,9 @@
 import numpy as np
 import pytest
 
-from tests.gpu_common import (BAND, Tally, compare, device, gpu_available, run_sample, to_dev,
-                              torch)
+from tests.gpu_common import (BAND, Tally, compare, device, gpu_available, report, run_sample,
+                              to_dev, torch)
+from oracle.parity import parity_sample_batch
 
 import oracle
 import token_sampling_row_amd as tsr
@@ -174,25 +175,28 @@ def test_greedy_strided_and_unaligned(sampler):
 
 # ---------------------------------------------------------------- sampler, workloads
 
-def check_workload(sampler_seed, w, params, step, rows=None, probs_rows=8):
+def check_workload(sampler_seed, w, params, step, rows=None, probs_rows=None):
+    """sample_rows on a whole workload batch, once as the benchmark calls it and
+    once with every diagnostic (kept set, kept mass, dense p~), against the
+    oracle on ``rows`` (default every row; p~ on ``probs_rows``, default every
+    row), in a pool of host processes. Prints the parity counts."""
     values = vals(w.data, w.dtype)
-    rows = list(range(w.rows)) if rows is None else rows
-    refs = [oracle.sample_row(values[b], params, sampler_seed, b, step) for b in rows]
     with make_sampler(sampler_seed) as s:
         x = to_dev(w.data, w.dtype)
         plain = run_sample(s, x, params, step)                       # as the bench runs it
         full = run_sample(s, x, params, step, diag=True, probs=True)
     assert np.array_equal(plain["token"], full["token"])
-    t = compare(full, refs, rows, values, check_probs_rows=set(rows[:probs_rows]))
-    print(f"parity {w.name} {params}: rows={t.rows} in_band={t.in_band} "
-          f"token_excused={t.token_excused} support_excused={t.support_excused}", flush=True)
+    t = parity_sample_batch(values, params, sampler_seed, step, full, rows=rows,
+                            probs_rows=probs_rows)
+    report(f"{w.name} {params}", t)
+    assert t.out_of_band == 0, t.notes[:5]
     return t
 
 
 def test_config1(sampler):
     w = wl.config(1)
     print_case("config1")
-    check_workload(wl.philox_seed(1), w, w.runs[0], 0, probs_rows=64)
+    check_workload(wl.philox_seed(1), w, w.runs[0], 0)
 
 
 @pytest.mark.parametrize("run", [1, 2])
@@ -205,16 +209,19 @@ def test_config2_runs(run):
 def test_config3_full_chain():
     w = wl.config(3)
     print_case("config3")
-    t = check_workload(wl.philox_seed(3), w, w.runs[0], 0, probs_rows=16)
-    assert t.rows == 256
+    t = check_workload(wl.philox_seed(3), w, w.runs[0], 0)
+    assert t.rows == 256 and t.probs_rows == 256
 
 
 @pytest.mark.parametrize("run", [0, 1])
-def test_config5_sampled_rows(run):
+def test_config5_all_rows(run):
+    """Every row of the 1024 x 151936 batch (p~ on every 8th row); also counts
+    mismatches a 1e-9 band would not excuse (the wide nucleus has ~9e-6 of
+    kept mass per token, so ~20% of its draws sit within 1e-6 of an end)."""
     w = wl.config(5)
     print_case("config5", run=run)
-    rows = list(range(0, 1024, 16))
-    check_workload(wl.philox_seed(5), w, w.runs[run], run, rows=rows, probs_rows=4)
+    t = check_workload(wl.philox_seed(5), w, w.runs[run], run, probs_rows=range(0, 1024, 8))
+    assert t.rows == 1024
 
 
 # ---------------------------------------------------------------- sampler, edges
@@ -262,8 +269,7 @@ def test_small_grid(dtype, V):
             refs = [oracle.sample_row(values[b], prm, seed, b, i) for b in range(len(rows))]
             got = run_sample(s, x, prm, i, diag=True, probs=True)
             compare(got, refs, list(range(len(rows))), values, tally=tally)
-    print(f"grid V={V} {dtype}: rows={tally.rows} excused token={tally.token_excused} "
-          f"support={tally.support_excused}")
+    report(f"grid V={V} {dtype}", tally)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
