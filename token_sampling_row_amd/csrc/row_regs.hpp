@@ -83,11 +83,13 @@ struct RegRow {
   }
 
   // Whole chunks of a 16-byte aligned row are 128-bit buffer loads off one
-  // resource, all issued back to back with no per-load address registers.
-  // Chunks at or past `nwhole` come back as zeros from the range check and are
-  // replaced in pass A of reg_stats (by -inf, or by `tail` for the partial
-  // chunk of a ragged row), so no wait is forced here. UNALIGNED rows are read
-  // in dwords (load_chunk_unaligned).
+  // resource whose size is the row's whole chunks, all issued back to back.
+  // The full byte offset of each load goes in its VGPR offset, the part the
+  // hardware checks against the resource size (the scalar offset is not
+  // checked), so chunks at or past `nwhole` are never read: they come back as
+  // zeros and are replaced in pass A of reg_stats (by -inf, or by `tail` for
+  // the partial chunk of a ragged row), and no wait is forced here. UNALIGNED
+  // rows are read in dwords (load_chunk_unaligned).
   template <bool UNALIGNED = false>
   __device__ __forceinline__ void load(const unsigned char* p, int V, bool ragged) {
     if constexpr (UNALIGNED) {
@@ -106,7 +108,7 @@ struct RegRow {
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         put(j, __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rs, voff, j * kBlock * 16, kLoadNonTemporal)));
+                                            rs, voff + j * kBlock * 16, 0, kLoadNonTemporal)));
         sched_fence();   // issue in chunk order: pass A waits for them in that order
       }
       tail = neg_inf_chunk<DT>();
