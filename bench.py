@@ -9,10 +9,15 @@ separate allocations are used in turn, so each call reads HBM rather than the
 256 MB last-level cache.
 
 Prints one JSON line. Also times the other workloads (greedy, pure sampling,
-min-p, the verify step, the wide-nucleus batch) and, on the host, the float64
-oracle on a bounded sample of the headline batch.
+min-p, the verify step, the wide-nucleus batch) and, in its CPU leg, runs the
+float64 oracle: on a bounded sample of the headline batch for the host
+baseline, and on every row of every workload for the parity block (the GPU's
+outputs of one untimed call per workload, with diagnostics, compared under the
+rule of oracle/parity.py: rows in band, excused and out-of-band mismatches,
+the largest relative error of p~).
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extra] [--no-cpu-baseline]
+                  [--no-parity]
 """
 from __future__ import annotations
 
@@ -108,6 +113,20 @@ def device_batch(torch, w, copies):
     return [t.clone() for _ in range(copies)]
 
 
+def median_call(torch, fn, calls=200):
+    """Median GPU time of one call: an event pair around each call on the
+    current stream (the per-call figure; the headline uses time_calls)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    return ts[len(ts) // 2]
+
+
 def time_calls(torch, fn, steps, warmup):
     """Average GPU time per call with HIP events on the current stream."""
     for i in range(warmup):
@@ -123,10 +142,26 @@ def time_calls(torch, fn, steps, warmup):
     return start.elapsed_time(end) / steps
 
 
-def cpu_baseline(w, params, seed, budget_s=12.0):
-    """The float64 oracle on the host cores over a bounded sample of the batch."""
+BOX_CPU_SHARE = 16   # host processes a one-GPU job may run (the machine's CPU share per GPU)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, params, seed, budget_s=10.0, one_core_s=4.0):
+    """The float64 oracle on the host over a bounded sample of the batch: rows/s
+    with one process per core of the job's CPU share, and rows/s on one core."""
     import multiprocessing as mp
-    cores = min(16, os.cpu_count() or 1)
+    import oracle
+    cores = min(BOX_CPU_SHARE, os.cpu_count() or 1)
     values_rows = list(range(w.rows))
     ctx = mp.get_context("fork")
     done, t0 = 0, time.perf_counter()
@@ -135,9 +170,19 @@ def cpu_baseline(w, params, seed, budget_s=12.0):
             n = sum(pool.map(_oracle_rows, [values_rows[i::cores] for i in range(cores)]))
             done += n
     dt = time.perf_counter() - t0
+    values = oracle.values_from_stored(w.data, w.dtype)
+    one, t1 = 0, time.perf_counter()
+    while time.perf_counter() - t1 < one_core_s:
+        oracle.sample_row(values[one % w.rows], params, seed, one % w.rows, 0)
+        one += 1
+    d1 = time.perf_counter() - t1
     return {"value": done / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} rows of the {w.rows}x{w.vocab} {w.dtype} batch "
-                      f"({done // w.rows} passes, {dt:.1f} s wall on {cores} processes)"}
+                      f"({done // w.rows} passes, {dt:.1f} s wall on {cores} processes); "
+                      f"one core: {one} rows in {d1:.1f} s",
+            "one_core_rows_per_s": one / d1, "os_cpu_count": os.cpu_count(),
+            "cpu_model": cpu_model(),
+            "note": f"processes capped at {BOX_CPU_SHARE}, the host CPU share of a one-GPU job"}
 
 
 _POOL = {}
@@ -164,6 +209,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the oracle comparison of every workload (CPU leg)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 256 MiB device copies (counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -199,6 +246,8 @@ def main():
 
     ms = time_calls(torch, lambda i: sampler.sample_rows(bufs[i % ROTATE], params, i, out=out),
                     args.steps, args.warmup)
+    ms_median = median_call(torch, lambda i: sampler.sample_rows(bufs[i % ROTATE], params, i,
+                                                                 out=out))
     rows_per_s = w3.rows / (ms * 1e-3)
     alg_bytes = w3.rows * w3.vocab * 2
     achieved = alg_bytes / (ms * 1e-3) / 1e9
@@ -218,6 +267,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w3, params, seed)
+    parity = None
+    if not args.no_parity:
+        del bufs
+        parity = parity_leg(torch, tsr, wl)
 
     line = {
         "metric": "sampled rows/s + achieved HBM GB/s (% peak), B=256 V=128256 full filter chain",
@@ -235,16 +288,83 @@ def main():
         "config": {"workload": "batch256_vocab128256_bf16_full_chain", "rows": w3.rows,
                    "vocab": w3.vocab, "logits": "bf16", "temperature": 0.9, "top_k": 50,
                    "top_p": 0.95, "min_p": 0.1, "tokens_per_s": rows_per_s,
-                   "input_buffers": ROTATE},
+                   "input_buffers": ROTATE, "median_ms_per_call": ms_median},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "kernel": row_kernel_label(w3.dtype, w3.vocab),
                      "algorithmic_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
+        "parity": parity,
         "extra": extra,
     }
     sampler.close()
     print(json.dumps(line))
+
+
+def parity_leg(torch, tsr, wl):
+    """One untimed call per workload run with every diagnostic, its outputs on
+    the host, and the float64 oracle on every row (draft tokens of the verify
+    workload drawn by the oracle too), compared under the rule of
+    oracle/parity.py. Returns {workload run: counts}."""
+    import numpy as np
+    import oracle
+    from oracle.parity import parity_sample_batch, parity_verify_batch
+
+    dev = torch.device("cuda:0")
+    out = {}
+    t_start = time.perf_counter()
+
+    def sample_diag(s, x, prm, step):
+        rows, V = x.shape
+        d = dict(status=torch.full((rows,), -7, dtype=torch.int32, device=dev),
+                 kept_count=torch.full((rows,), -7, dtype=torch.int32, device=dev),
+                 threshold=torch.full((rows,), float("nan"), dtype=torch.float32, device=dev),
+                 kept_mass=torch.full((rows,), float("nan"), dtype=torch.float64, device=dev),
+                 probs=torch.full((rows, V), float("nan"), dtype=torch.float32, device=dev))
+        tok = s.sample_rows(x, prm, step, diag=d)
+        torch.cuda.synchronize()
+        g = {k: t.cpu().numpy() for k, t in d.items()}
+        g["token"] = tok.cpu().numpy()
+        return g
+
+    for cfg in (1, 2, 3, 5):
+        w = wl.config(cfg)
+        seed = wl.philox_seed(cfg)
+        values = oracle.values_from_stored(w.data, w.dtype)
+        with tsr.Sampler(0, max_rows=4096, max_vocab=1 << 18, max_k=8, seed=seed) as s:
+            x = device_batch(torch, w, 1)[0]
+            for run, prm in enumerate(w.runs):
+                g = sample_diag(s, x, prm, run)
+                t = parity_sample_batch(values, prm, seed, run, g)
+                key = f"{w.name}_run{run}"
+                out[key] = dict(t.as_dict(), params=prm, **t.shape())
+                del g
+            del x
+        torch.cuda.empty_cache()
+
+    w = wl.config(4)
+    K = w.extra["K"]
+    seed = wl.philox_seed(4)
+    tv = oracle.values_from_stored(w.data, w.dtype)
+    dv = oracle.values_from_stored(w.extra["draft"], w.dtype)
+    xs = np.array([[oracle.sample_row(dv[b, j], {"temperature": 1.0}, seed, b * K + j, 1000).token
+                    for j in range(K)] for b in range(w.rows)], dtype=np.int32)
+    with tsr.Sampler(0, max_rows=4096, max_vocab=1 << 18, max_k=8, seed=seed) as s:
+        tg = torch.from_numpy(w.data).to(dev)
+        df = torch.from_numpy(w.extra["draft"]).to(dev)
+        xd = torch.from_numpy(xs).to(dev)
+        for run, prm in enumerate(w.runs):
+            st = torch.full((w.rows,), -7, dtype=torch.int32, device=dev)
+            toks, acc = s.spec_verify(tg, df, xd, prm, run, out_status=st)
+            torch.cuda.synchronize()
+            t = parity_verify_batch(tv, dv, xs, prm, seed, run, toks.cpu().numpy(),
+                                    acc.cpu().numpy(), st.cpu().numpy())
+            a = acc.float().mean().item()
+            out[f"{w.name}_run{run}"] = dict(t.as_dict(), params=prm, acceptance_rate=a / K,
+                                             tokens_per_verify=a + 1)
+    total = sum(v["out_of_band"] for v in out.values())
+    return {"out_of_band_total": total, "seconds": time.perf_counter() - t_start,
+            "workloads": out}
 
 
 def run_extra(torch, tsr, wl, steps, warmup):

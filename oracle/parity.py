@@ -62,6 +62,8 @@ class Tally:
     probs_rows: int = 0           # rows whose dense p~ was compared
     max_prob_rel_err: float = 0.0  # largest relative error of p~ / the kept mass
     notes: list = field(default_factory=list)
+    eff: list = field(default_factory=list)    # per sampled row: e^H of p (effective choices)
+    kept: list = field(default_factory=list)   # per sampled row: |S|
 
     def as_dict(self) -> dict:
         return {"rows": self.rows, "in_band": self.in_band, "in_tight_band": self.in_tight_band,
@@ -76,7 +78,20 @@ class Tally:
             setattr(self, k, getattr(self, k) + getattr(other, k))
         self.max_prob_rel_err = max(self.max_prob_rel_err, other.max_prob_rel_err)
         self.notes += other.notes
+        self.eff += other.eff
+        self.kept += other.kept
         return self
+
+    def shape(self) -> dict:
+        """The sampled rows' shape (legost.in "Temperature: one dial for
+        boldness": the entropy H of p and its effective number of choices e^H;
+        the kept-set size |S|): min / median / max over the rows."""
+        out = {}
+        for name, xs in (("effective_choices", self.eff), ("kept", self.kept)):
+            if xs:
+                a = np.asarray(xs, dtype=np.float64)
+                out[name] = [float(a.min()), float(np.median(a)), float(a.max())]
+        return out
 
 
 def _fail(t: Tally, strict: bool, msg) -> None:
@@ -247,6 +262,11 @@ def _sample_chunk(rows) -> Tally:
     g = j["gpu"]
     for b in rows:
         ref = sample_row(j["values"][b], j["params"], j["seed"], b, j["step"])
+        if ref.support is not None:
+            p = ref.support.p
+            nz = p > 0
+            t.eff.append(float(np.exp(-np.sum(p[nz] * np.log(p[nz])))))
+            t.kept.append(ref.support.kept_count)
         probs = g["probs"][b] if ("probs" in g and b in j["probs_rows"]) else None
         compare_sample_row(t, b, ref, g["token"][b],
                            status=g["status"][b] if "status" in g else None,
