@@ -100,12 +100,15 @@ typedef struct {
 
 /* Optional per-row diagnostics for sample_rows; every pointer may be NULL.
  *  status      [rows]        TSR_ROW_* per row.
- *  kept_count  [rows]        |S| (0 on greedy or bad rows).
+ *  kept_count  [rows]        |S| (0 on bad rows).
  *  threshold   [rows]        the smallest kept logit (as float32).
  *  kept_mass   [rows]        sum over S of softmax(logits / T), in (0, 1].
  *  probs       [rows][vocab] the renormalised distribution p~ (eq. 39.2),
- *                            0 outside S. Written by an extra pass: meant for
- *                            validation, not for the timed hot path. */
+ *                            0 outside S (all 0 on bad rows). Written by an
+ *                            extra pass: meant for validation, not for the
+ *                            timed hot path.
+ * A greedy row (temperature 0) reports p~ as the point mass at its token:
+ * kept_count 1, threshold the row's largest logit, kept_mass 1, probs one-hot. */
 typedef struct {
   int32_t* status;
   int32_t* kept_count;
@@ -182,7 +185,8 @@ int sample_rows_masked(tsr_handle h, const void* logits, int dtype, int rows, in
  *      rescaled once, z / r if z > 0, z * r otherwise, before anything else
  *      [P5 "The repetition penalty"]; the rescaled logit is rounded to the
  *      logits' element type (float32; bf16 to nearest even from that float32).
- *      r = 1, history NULL or history_len 0: no penalty.
+ *      r = 1 or history_len 0: no penalty. history NULL with history_len > 0
+      is TSR_EINVAL.
  *  row_params [rows] tsr_params (device memory): each row's own sampling
  *      parameters in place of the call's `params` (which may then be NULL);
  *      a row whose parameters tsr_params would reject gets

@@ -35,7 +35,8 @@ def run_rows(s, data, dtype, plist, step):
     d = dict(status=torch.full((rows,), -7, dtype=torch.int32, device=device()),
              kept_count=torch.full((rows,), -7, dtype=torch.int32, device=device()),
              threshold=torch.full((rows,), float("nan"), dtype=torch.float32, device=device()),
-             kept_mass=torch.full((rows,), float("nan"), dtype=torch.float64, device=device()))
+             kept_mass=torch.full((rows,), float("nan"), dtype=torch.float64, device=device()),
+             probs=torch.full((rows, V), float("nan"), dtype=torch.float32, device=device()))
     lp = torch.full((rows,), 123.0, dtype=torch.float32, device=device())
     out = s.sample_rows_ex(to_dev(data, dtype), None, step, logprob=lp, diag=d, row_params=rp)
     torch.cuda.synchronize()
@@ -74,6 +75,13 @@ def test_row_params_grid(dtype, V):
             for i, b in enumerate(good):
                 greedy = plist[b].get("temperature", 1.0) == 0.0
                 compare(got, [refs[i]], [b], values, greedy=greedy)
+                if greedy:   # p~ is the point mass at the token (include/tsr.h)
+                    assert got["kept_count"][b] == 1 and got["kept_mass"][b] == 1.0
+                    assert np.float32(got["threshold"][b]) == np.float32(values[b].max())
+                    if "probs" in got:
+                        onehot = np.zeros(V, dtype=np.float32)
+                        onehot[refs[i].token] = 1.0
+                        assert np.array_equal(got["probs"][b], onehot), b
             compare_logprob(got, refs, good)
 
 

@@ -4,6 +4,10 @@ Every kernel instance (element type x chunks per thread) is compiled in a
 generated translation unit of its own, in parallel; the dispatch units and the
 C-ABI host layer only declare them. Everything links into
 token_sampling_row_amd/libtsr.so, in-tree.
+
+``build(trace=True)`` (``python build.py --trace``) builds the same sources with
+TSR_TRACE=1 into libtsr_trace.so instead: per-wavefront phase stamps of the
+sampler kernels and the two calls of include/tsr_trace.h (trace.py reads them).
 """
 from __future__ import annotations
 
@@ -19,6 +23,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 GEN = os.path.join(BUILD, "gen")
 LIB = os.path.join(HERE, "libtsr.so")
+BUILD_TRACE = os.path.join(HERE, "_build_trace")
+LIB_TRACE = os.path.join(HERE, "libtsr_trace.so")
 ARCH = os.environ.get("TSR_OFFLOAD_ARCH", "gfx950")
 ROW_NCS = (1, 2, 4, 8, 16, 24, 32, 38)      # must match kRowNcs in dispatch.hpp
 VERIFY_NCS = (1, 2, 4, 8, 16)               # must match kVerifyNcs
@@ -81,10 +87,10 @@ def instance_units() -> dict[str, str]:
     return units
 
 
-def _compile(src_path: str) -> tuple[str, str]:
-    obj = os.path.join(BUILD, os.path.basename(src_path) + ".o")
-    cmd = [_hipcc(), *FLAGS, "-I", CSRC, "-Rpass-analysis=kernel-resource-usage", "-c", src_path,
-           "-o", obj]
+def _compile(src_path: str, out_dir: str = BUILD, extra: tuple = ()) -> tuple[str, str]:
+    obj = os.path.join(out_dir, os.path.basename(src_path) + ".o")
+    cmd = [_hipcc(), *FLAGS, *extra, "-I", CSRC, "-Rpass-analysis=kernel-resource-usage", "-c",
+           src_path, "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src_path}:\n{p.stderr[-4000:]}")
@@ -104,8 +110,11 @@ def spill_report(remarks: str) -> list[str]:
     return bad
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
+def build(verbose: bool = False, jobs: int | None = None, trace: bool = False) -> str:
+    out_dir, lib = (BUILD_TRACE, LIB_TRACE) if trace else (BUILD, LIB)
+    extra = ("-DTSR_TRACE=1",) if trace else ()
     os.makedirs(GEN, exist_ok=True)
+    os.makedirs(out_dir, exist_ok=True)
     srcs = [os.path.join(CSRC, s) for s in DISPATCH]
     for name, text in instance_units().items():
         path = os.path.join(GEN, name)
@@ -117,25 +126,25 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     # biggest units first so the pool drains evenly
     srcs.sort(key=lambda s: (not os.path.basename(s).startswith("i_sample"), s), reverse=False)
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        results = list(ex.map(_compile, srcs))
+        results = list(ex.map(lambda s: _compile(s, out_dir, extra), srcs))
     objs = [o for o, _ in results]
     remarks = "\n".join(r for _, r in results)
-    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
+    with open(os.path.join(out_dir, "resource_usage.txt"), "w") as f:
         f.write(remarks)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"link failed:\n{p.stderr[-4000:]}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     spills = spill_report(remarks)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} units")
+        print(f"built {lib} from {len(srcs)} units")
         for s in spills:
             print("  spill:", s)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, trace="--trace" in sys.argv[1:])
     sys.exit(0)

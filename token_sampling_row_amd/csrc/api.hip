@@ -9,6 +9,9 @@
 
 #include "tsr.h"
 #include "kernels.hpp"
+#if TSR_TRACE
+#include "tsr_trace.h"
+#endif
 
 struct tsr_ctx {
   int device;
@@ -19,6 +22,9 @@ struct tsr_ctx {
   tsr::VerifyWs ws;
   tsr::BeamWs bws;
   void* ws_block;
+#if TSR_TRACE
+  unsigned long long* trace;   // phase stamps (tracing build)
+#endif
 };
 
 namespace {
@@ -58,7 +64,7 @@ int check_params(const tsr_params* p) {
   return TSR_OK;
 }
 
-tsr::KParams make_kparams(const tsr_ctx* h, const tsr_params* p, int vocab, uint64_t step,
+tsr::KParams make_kparams(uint64_t seed, const tsr_params* p, int vocab, uint64_t step,
                           bool want_z) {
   tsr::KParams kp{};
   const double T = p->temperature;
@@ -83,8 +89,8 @@ tsr::KParams make_kparams(const tsr_ctx* h, const tsr_params* p, int vocab, uint
     if (p->filter_mode == TSR_SEQUENTIAL) kp.flags |= tsr::F_SEQ;
     if (want_z) kp.flags |= tsr::F_Z;
   }
-  kp.key0 = (uint32_t)(h->seed & 0xFFFFFFFFu);
-  kp.key1 = (uint32_t)(h->seed >> 32);
+  kp.key0 = (uint32_t)(seed & 0xFFFFFFFFu);
+  kp.key1 = (uint32_t)(seed >> 32);
   kp.step_lo = (uint32_t)(step & 0xFFFFFFFFu);
   kp.step_hi = (uint32_t)(step >> 32);
   return kp;
@@ -94,6 +100,38 @@ int esize(int dtype) { return dtype == TSR_F32 ? 4 : 2; }
 
 bool elem_aligned(const void* p, int dtype) {
   return ((uintptr_t)p % (uintptr_t)esize(dtype)) == 0;
+}
+
+// Arguments every verify entry point checks (the handle's limits aside).
+int check_verify(const void* target_logits, const void* draft_logits, int dtype,
+                 const int32_t* draft_tokens, int rows, int K, int vocab,
+                 const tsr_params* params, const int32_t* out_tokens,
+                 const int32_t* out_accepted) {
+  if (!target_logits || !draft_tokens || !out_tokens || !out_accepted) return TSR_EINVAL;
+  if (dtype != TSR_F32 && dtype != TSR_BF16) return TSR_EINVAL;
+  if (rows < 0 || vocab < 1 || K < 1 || K > kMaxDraft) return TSR_EINVAL;
+  const int prc = check_params(params);
+  if (prc != TSR_OK) return prc;
+  if (params->temperature > 0.0 && !draft_logits) return TSR_EINVAL;
+  if (!elem_aligned(target_logits, dtype) || (draft_logits && !elem_aligned(draft_logits, dtype)))
+    return TSR_EINVAL;
+  if (vocab > tsr::max_vocab_verify(dtype)) return TSR_EUNSUPPORTED;
+  return TSR_OK;
+}
+
+// The verify launch once the arguments are checked (the device is current).
+int launch_verify_checked(const void* target_logits, const void* draft_logits, int dtype,
+                          const int32_t* draft_tokens, int rows, int K, int vocab,
+                          const tsr::KParams& kp, const tsr::VerifyWs& ws, int32_t* out_tokens,
+                          int32_t* out_accepted, int32_t* out_status, void* hip_stream) {
+  const long long rb = (long long)vocab * esize(dtype);
+  const int aligned = ((uintptr_t)target_logits % 16 == 0) &&
+                      (!draft_logits || (uintptr_t)draft_logits % 16 == 0) && (rb % 16 == 0);
+  const int ragged = !aligned || (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;
+  const hipError_t e = tsr::launch_verify(target_logits, draft_logits, dtype, draft_tokens, rows,
+                                          K, vocab, aligned, ragged, kp, ws, out_tokens,
+                                          out_accepted, out_status, (hipStream_t)hip_stream);
+  return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
 }
 
 }  // namespace
@@ -148,10 +186,18 @@ int sampler_init(tsr_handle* out, int device, int max_rows, int max_vocab, int m
     h->bws.tok = (int32_t*)(bb + bslots * sizeof(double));
     h->bws.bad = (uint32_t*)(bb + bslots * (sizeof(double) + sizeof(int32_t)));
     h->bws.counter = h->bws.bad + max_rows;
+#if TSR_TRACE
+    if (hipMalloc(&h->trace, TSR_TRACE_WORDS * sizeof(uint64_t)) != hipSuccess) return TSR_ENOMEM;
+    if (hipMemset(h->trace, 0, TSR_TRACE_WORDS * sizeof(uint64_t)) != hipSuccess) return TSR_EDEVICE;
+    if (hipDeviceSynchronize() != hipSuccess) return TSR_EDEVICE;
+#endif
     return TSR_OK;
   });
   if (rc != TSR_OK) {
     if (h->ws_block) (void)hipFree(h->ws_block);
+#if TSR_TRACE
+    if (h->trace) (void)hipFree(h->trace);
+#endif
     free(h);
     return rc;
   }
@@ -164,6 +210,9 @@ int sampler_destroy(tsr_handle h) {
   const int rc = on_device(h->device, [&]() -> int {
     if (hipDeviceSynchronize() != hipSuccess) return TSR_EDEVICE;
     if (h->ws_block && hipFree(h->ws_block) != hipSuccess) return TSR_EDEVICE;
+#if TSR_TRACE
+    if (h->trace && hipFree(h->trace) != hipSuccess) return TSR_EDEVICE;
+#endif
     return TSR_OK;
   });
   free(h);
@@ -203,6 +252,7 @@ int sample_rows_ex(tsr_handle h, const void* logits, int dtype, int rows, int vo
     const int64_t words = ((int64_t)vocab + 31) / 32;
     if (cs.allowed_stride < words || ((uintptr_t)cs.allowed % 4) != 0) return TSR_EINVAL;
   }
+  if (!cs.history && cs.history_len > 0) return TSR_EINVAL;   // a window length without ids
   const bool rep_given = cs.history && cs.history_len > 0;
   if (rep_given) {
     if (cs.history_len > tsr::kHistMax || cs.history_stride < cs.history_len ||
@@ -228,7 +278,10 @@ int sample_rows_ex(tsr_handle h, const void* logits, int dtype, int rows, int vo
     dg.probs = diag->probs;
   }
   dg.logprob = out_logprob;
-  tsr::KParams kp = make_kparams(h, params, vocab, step, dg.kept_mass != nullptr);
+  tsr::KParams kp = make_kparams(h->seed, params, vocab, step, dg.kept_mass != nullptr);
+#if TSR_TRACE
+  kp.trace = h->trace;
+#endif
   if (cs.row_params) {
     kp.rowp = reinterpret_cast<const tsr::RowParams*>(cs.row_params);
     kp.flags |= tsr::F_ROWP;
@@ -278,27 +331,18 @@ int spec_verify(tsr_handle h, const void* target_logits, const void* draft_logit
                 const int32_t* draft_tokens, int rows, int K, int vocab,
                 const tsr_params* params, uint64_t step, int32_t* out_tokens,
                 int32_t* out_accepted, int32_t* out_status, void* hip_stream) {
-  if (!h || !target_logits || !draft_tokens || !out_tokens || !out_accepted) return TSR_EINVAL;
-  if (dtype != TSR_F32 && dtype != TSR_BF16) return TSR_EINVAL;
-  if (rows < 0 || rows > h->max_rows || vocab < 1 || vocab > h->max_vocab) return TSR_EINVAL;
-  if (K < 1 || K > h->max_k) return TSR_EINVAL;
-  const int prc = check_params(params);
-  if (prc != TSR_OK) return prc;
-  if (params->temperature > 0.0 && !draft_logits) return TSR_EINVAL;
-  if (!elem_aligned(target_logits, dtype) || (draft_logits && !elem_aligned(draft_logits, dtype)))
-    return TSR_EINVAL;
-  if (vocab > tsr::max_vocab_verify(dtype)) return TSR_EUNSUPPORTED;
-  if (rows == 0) return TSR_OK;
-  const tsr::KParams kp = make_kparams(h, params, vocab, step, false);
-  const long long rb = (long long)vocab * esize(dtype);
-  const int aligned = ((uintptr_t)target_logits % 16 == 0) &&
-                      (!draft_logits || (uintptr_t)draft_logits % 16 == 0) && (rb % 16 == 0);
-  const int ragged = !aligned || (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;
+  if (!h) return TSR_EINVAL;
+  if (rows > h->max_rows || vocab > h->max_vocab || K > h->max_k) return TSR_EINVAL;
+  const int rc = check_verify(target_logits, draft_logits, dtype, draft_tokens, rows, K, vocab,
+                              params, out_tokens, out_accepted);
+  if (rc != TSR_OK || rows == 0) return rc;
+  tsr::KParams kp = make_kparams(h->seed, params, vocab, step, false);
+#if TSR_TRACE
+  kp.trace = h->trace;
+#endif
   return on_device(h->device, [&]() -> int {
-    const hipError_t e = tsr::launch_verify(target_logits, draft_logits, dtype, draft_tokens,
-                                            rows, K, vocab, aligned, ragged, kp, h->ws, out_tokens,
-                                            out_accepted, out_status, (hipStream_t)hip_stream);
-    return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
+    return launch_verify_checked(target_logits, draft_logits, dtype, draft_tokens, rows, K, vocab,
+                                 kp, h->ws, out_tokens, out_accepted, out_status, hip_stream);
   });
 }
 
@@ -318,7 +362,10 @@ int tree_verify(tsr_handle h, const void* target_logits, const void* draft_logit
     return TSR_EINVAL;
   if (vocab > tsr::max_vocab_verify(dtype)) return TSR_EUNSUPPORTED;
   if (rows == 0) return TSR_OK;
-  const tsr::KParams kp = make_kparams(h, params, vocab, step, false);
+  tsr::KParams kp = make_kparams(h->seed, params, vocab, step, false);
+#if TSR_TRACE
+  kp.trace = h->trace;
+#endif
   const long long rb = (long long)vocab * esize(dtype);
   const int aligned = ((uintptr_t)target_logits % 16 == 0) &&
                       (!draft_logits || (uintptr_t)draft_logits % 16 == 0) && (rb % 16 == 0);
@@ -365,5 +412,28 @@ int sampler_philox(tsr_handle h, const uint32_t* counters, int n, uint32_t* out_
     return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
   });
 }
+
+#if TSR_TRACE
+int sampler_trace_read(tsr_handle h, uint64_t* out, int64_t n) {
+  if (!h || !out || n < 0 || n > TSR_TRACE_WORDS) return TSR_EINVAL;
+  return on_device(h->device, [&]() -> int {
+    if (hipDeviceSynchronize() != hipSuccess) return TSR_EDEVICE;
+    if (n && hipMemcpy(out, h->trace, (size_t)n * sizeof(uint64_t), hipMemcpyDeviceToHost) !=
+                 hipSuccess)
+      return TSR_EDEVICE;
+    return TSR_OK;
+  });
+}
+
+int sampler_trace_clear(tsr_handle h) {
+  if (!h) return TSR_EINVAL;
+  return on_device(h->device, [&]() -> int {
+    if (hipDeviceSynchronize() != hipSuccess) return TSR_EDEVICE;
+    if (hipMemset(h->trace, 0, TSR_TRACE_WORDS * sizeof(uint64_t)) != hipSuccess)
+      return TSR_EDEVICE;
+    return hipDeviceSynchronize() == hipSuccess ? TSR_OK : TSR_EDEVICE;
+  });
+}
+#endif
 
 }  // extern "C"

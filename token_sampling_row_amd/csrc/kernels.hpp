@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "trace.hpp"
+
 namespace tsr {
 
 // One row's sampling parameters, laid out as the C ABI's tsr_params.
@@ -33,6 +35,9 @@ struct KParams {
   int hist_len;              // ids per row (<= kHistMax)
   double rpen;               // repetition penalty r
   const RowParams* rowp;     // per-row parameters (F_ROWP), validated and derived per row
+#if TSR_TRACE
+  unsigned long long* trace; // phase stamps (tracing build only)
+#endif
 };
 enum : int {
   F_GREEDY = 1,   // temperature 0

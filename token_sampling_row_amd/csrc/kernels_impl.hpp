@@ -98,6 +98,16 @@ __device__ __forceinline__ void zero_probs(const DiagPtrs& dg, int row, int V) {
     for (int i = threadIdx.x; i < V; i += kBlock) pr[i] = 0.0f;
   }
 }
+// Diagnostics of a greedy row: p~ is the point mass at the drawn token (|S| 1,
+// the threshold its logit M, kept mass 1).
+__device__ __forceinline__ void greedy_row(int row, int tok, float M, int V, int32_t* out,
+                                           const DiagPtrs& dg) {
+  write_row(row, tok, 0, 1, M, 1.0, 1.0, 1.0, out, dg);
+  if (dg.probs) {
+    float* pr = dg.probs + (long long)row * V;
+    for (int i = threadIdx.x; i < V; i += kBlock) pr[i] = i == tok ? 1.0f : 0.0f;
+  }
+}
 
 // Kept set, draw and diagnostics of one row on the streaming path.
 template <int DT>
@@ -338,6 +348,7 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(const unsigned char* log
                                                         int aligned, int ragged, int32_t* out,
                                                         int32_t* status) {
   Lds& L = tsr_lds;
+  TSR_TRACE_INIT(nullptr);
   const int row = blockIdx.x;
   RegRow<DT, NC> r;
   r.load(logits + (long long)row * stride_bytes, V, ragged != 0);
@@ -355,6 +366,7 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel_stream(const unsigned ch
                                                                long long stride_bytes, int V,
                                                                int aligned, int32_t* out,
                                                                int32_t* status) {
+  TSR_TRACE_INIT(nullptr);
   const int row = blockIdx.x;
   const StreamRow<DT> s(logits + (long long)row * stride_bytes, V, aligned != 0);
   const StreamStats st = stream_stats(s, false, 1.0f);
@@ -401,6 +413,11 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   const unsigned char* p = logits + (long long)row * stride_bytes;
   constexpr bool MASK = EXT == 1, REP = EXT == 1 || EXT == 2, UNAL = EXT == 3;
   KParams kp = kp0;
+#if TSR_TRACE
+  TSR_STAMP_P(kp0.trace, kStEntry);
+  trace_hw_id(kp0.trace);
+  TSR_TRACE_INIT(kp0.trace);
+#endif
   if ((kp.flags & F_ROWP) && !row_kparams(kp, row, V)) {
     write_row(row, -1, kRowBadParam, 0, kNegInf, 0.0, kNaN, kNaN, out, dg);
     zero_probs(dg, row, V);
@@ -419,6 +436,9 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   r.template load<UNAL>(p, V, ragged != 0);
   const bool greedy = (kp.flags & F_GREEDY) != 0;
   const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);   // while the loads fly
+#if TSR_TRACE
+  TSR_STAMP_P(kp0.trace, kStIssued);
+#endif
   const RowStats st = reg_stats<MASK, REP>(r, !greedy && joint_top_p(kp), kp.c, L, V, x, &mk);
   if (st.status != 0) {
     write_row(row, -1, st.status, 0, kNegInf, 0.0, kNaN, kNaN, out, dg);
@@ -426,12 +446,12 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
     return;
   }
   if (greedy) {
-    const int tok = reg_argmax(r, st.M, L);
-    write_row(row, tok, 0, 0, kNegInf, 0.0, 1.0, 1.0, out, dg);
+    greedy_row(row, reg_argmax(r, st.M, L), st.M, V, out, dg);
     return;
   }
   const float M = st.M, c = kp.c;
   const Filters f = make_filters(kp, M);
+  TSR_STAMP(kStCutStart);
   float tau = -kFltMax;     // no filter: every finite logit
   int kept = -1, tok;
   double zs, wt;
@@ -454,9 +474,11 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
       // too many candidates for the LDS buffer: the search over the registers
       // (the exact value histogram of bf16 rows), then the walk
       const Cut cut = reg_general(r, M, c, kp.cR, f, L);
+      TSR_STAMP(kStGeneral);
       tau = cut.tau;
       kept = cut.kept;
       tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs, &wt);
+      TSR_STAMP(kStWalk);
     } else {
       // the streaming path finishes this row
       stream_finish(row_stream_view<DT, EXT>(p, V, kp, row), row, M, -1.0, kp, f, u, out, dg);
@@ -464,6 +486,7 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
     }
   } else {
     tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, tau, M, c}, u, L, &zs, &wt);
+    TSR_STAMP(kStWalk);
   }
   if (dg.kept_count || dg.threshold || dg.kept_mass || dg.probs) {
     diag_finish(row_stream_view<DT, EXT>(p, V, kp, row), row, tok, kept, tau, M, c, zs, wt, out,
@@ -471,6 +494,7 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
     return;
   }
   write_row(row, tok, 0, kept, tau, 0.0, wt, zs, out, dg);
+  TSR_STAMP(kStEnd);
 }
 
 // Rows wider than the register file: every pass streams the row.
@@ -482,6 +506,7 @@ __global__ __launch_bounds__(kBlock) void sample_kernel_stream(const unsigned ch
   const int row = blockIdx.x;
   const unsigned char* p = logits + (long long)row * stride_bytes;
   KParams kp = kp0;
+  TSR_TRACE_INIT(nullptr);
   if ((kp.flags & F_ROWP) && !row_kparams(kp, row, V)) {
     write_row(row, -1, kRowBadParam, 0, kNegInf, 0.0, kNaN, kNaN, out, dg);
     zero_probs(dg, row, V);
@@ -508,7 +533,7 @@ __global__ __launch_bounds__(kBlock) void sample_kernel_stream(const unsigned ch
     return;
   }
   if (greedy) {
-    write_row(row, stream_argmax(s, st.M), 0, 0, kNegInf, 0.0, 1.0, 1.0, out, dg);
+    greedy_row(row, stream_argmax(s, st.M), st.M, V, out, dg);
     return;
   }
   const Filters f = make_filters(kp, st.M);
@@ -623,6 +648,7 @@ __global__ __launch_bounds__(kBlock) void beam_kernel(const unsigned char* logit
                                                       int32_t* out_tok, double* out_score,
                                                       int32_t* out_status) {
   Lds& L = tsr_lds;
+  TSR_TRACE_INIT(nullptr);
   const int tid = threadIdx.x;
   const int row = blockIdx.x, g = row / beam;
   const unsigned char* p = logits + (long long)row * stride_bytes;
@@ -831,6 +857,7 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt
                                                         int32_t* out_acc, int32_t* out_status) {
   constexpr int EPC = Fmt<DT>::EPC;
   Lds& L = tsr_lds;
+  TSR_TRACE_INIT(nullptr);
   // the draft positions (two rows each) first, then every sequence's bonus
   // position (the target row only): when the grid exceeds the device, the
   // lighter workgroups are the ones that wait
@@ -953,6 +980,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(const unsigned char* tgt,
                                                       int32_t* out_status) {
   constexpr int EPC = Fmt<DT>::EPC;
   Lds& L = tsr_lds;
+  TSR_TRACE_INIT(nullptr);
   // node-major order: earlier nodes (the ones likely to have children, two
   // rows to read) are dispatched before the later ones (leaves, one row)
   const int nseq = (int)gridDim.x / N;

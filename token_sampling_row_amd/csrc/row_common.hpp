@@ -59,6 +59,9 @@ struct Lds {
   uint32_t su[8];
   float sf[8];
   double sd[8];
+#if TSR_TRACE
+  unsigned long long* trace;        // the launch's stamp buffer (tracing build)
+#endif
 };
 
 // Histogram bin b lives at slot (b % 16) * 64 + b / 16: the 16 consecutive
@@ -161,6 +164,18 @@ __device__ __forceinline__ uint4 penalize_chunk(uint4 t, uint32_t hit, double r)
 // One LDS instance per translation unit; every kernel of the unit uses it, as
 // do the non-inlined functions of the streaming path.
 static __shared__ Lds tsr_lds;
+
+// A phase stamp from code past the kernel's first barrier (the kernel puts
+// the stamp buffer in LDS at entry); empty outside the tracing build.
+// Every kernel that reaches a stamp sets the buffer at entry (null: none).
+#if TSR_TRACE
+#define TSR_STAMP(slot) TSR_STAMP_P(::tsr::tsr_lds.trace, (slot))
+#define TSR_TRACE_INIT(ptr) \
+  do { if (threadIdx.x % kWave == 0) ::tsr::tsr_lds.trace = (ptr); } while (0)
+#else
+#define TSR_STAMP(slot) ((void)0)
+#define TSR_TRACE_INIT(ptr) ((void)0)
+#endif
 
 // The look-back window of the repetition penalty, published by wave 0 (all
 // lanes, lane h holding id hv of the window's first n): L.hist[h] = the id if

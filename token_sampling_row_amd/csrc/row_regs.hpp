@@ -326,6 +326,9 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
   int nallow = 0x7FFFFFFF;
   double zown = 0.0;
   float tmax = reg_pass_a<MASK, ZEXACT>(r, L, c, &zown, mk, &nallow);
+#if TSR_TRACE
+  TSR_STAMP_P(L.trace, kStPassA);   // (the pointer was stored at entry by this thread's wave 0)
+#endif
   if (REP && x.hn > 0) {
     if (threadIdx.x < kWave) {
       // wave 0: each window token's logit, read back from the row (one per
@@ -372,6 +375,7 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
   __syncthreads();
   if (__lane_id() == 0) L.ws[wid] = WaveStats{wm, wt, wz, wb, wna};
   __syncthreads();
+  TSR_STAMP(kStStats);
   RowStats st;
   float M = kNegInf, tmin = kPosInf;
   int anybad = 0, na = 0;
@@ -395,6 +399,7 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
   st.zlo = Z;
   // NaN or +inf anywhere in the row shows in its (NaN-propagating) maximum
   st.status = (anybad || M != M || M == kPosInf) ? 1 : (M > kNegInf ? 0 : 2);
+  TSR_STAMP(kStStatsDone);
   return st;
 }
 
@@ -628,6 +633,7 @@ __device__ __forceinline__ void wave_compact(const RegRow<DT, NC>& r, float Lb, 
     base = kWaveCap + 1;
   } else if (holders) {
     unsigned long long m = wave_chunk_mask<NC>([&](int j) { return r.cmax(j) >= Lb; });
+    TSR_STAMP(kStMask);
     while (m && base <= kWaveCap) {
       const int j = pop_low(m);
       float v[EPC];
@@ -682,6 +688,7 @@ __device__ __forceinline__ void wave_compact(const RegRow<DT, NC>& r, float Lb, 
     }
   }
   if (__lane_id() == 0) L.wcnt[wid] = base;
+  TSR_STAMP(kStCompactEnd);
 }
 
 // Candidates the per-wavefront regions hold in all (after a barrier).
@@ -785,16 +792,19 @@ __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, floa
   if (Lb > kNegInf) {
     wave_compact(r, Lb, L);
     __syncthreads();
+    TSR_STAMP(kStCompact1);
     fits = wave_regions_total(L) <= kWaveCap;
   }
   if (!fits && f.k_on && V > kWaveCap) {
     __syncthreads();
     const float kb = topk_sketch(r, M, fmaxf(Lb, tmin), f.k, L);
+    TSR_STAMP(kStSketch);
     if (kb > Lb) {
       Lb = kb;
       all_in = false;
       wave_compact(r, Lb, L);
       __syncthreads();
+      TSR_STAMP(kStCompact2);
       fits = wave_regions_total(L) <= kWaveCap;
     }
   }
@@ -811,6 +821,7 @@ __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, floa
       zref = reg_weight_sum(r, M, c, L);
       zx = true;
     }
+    TSR_STAMP(kStResolve);
     out.drawn = 1;
     out.token = L.si[0];
     out.kept = L.si[1];
