@@ -235,6 +235,24 @@ int spec_verify(tsr_handle h, const void* target_logits, const void* draft_logit
                 const tsr_params* params, uint64_t step, int32_t* out_tokens,
                 int32_t* out_accepted, int32_t* out_status, void* hip_stream);
 
+/* spec_verify for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * No handle: the Philox key is `seed` (as sampler_init's), and the call runs
+ * on `device` (made current for the call, the caller's restored after). The
+ * verify workspace is a static device array in the library, about 1.1 MB, one
+ * copy per device, held until the process ends; the call allocates nothing
+ * and calls no allocating routine. Limits of that array: rows <= 16384 and
+ * rows * (K + 1) <= 65536 (TSR_EINVAL beyond); 1 <= K <= 32. The first call on
+ * a device also enqueues one small kernel that zeroes the array's counters.
+ * Every call on a device shares that device's array: calls that overlap on
+ * one device (on different streams, or from several threads) race and give
+ * undefined results. Arguments, outputs and results are spec_verify's. */
+int spec_verify_noalloc(int device, uint64_t seed, const void* target_logits,
+                        const void* draft_logits, int dtype, const int32_t* draft_tokens,
+                        int rows, int K, int vocab, const tsr_params* params, uint64_t step,
+                        int32_t* out_tokens, int32_t* out_accepted, int32_t* out_status,
+                        void* hip_stream);
+
 /* Tree (multi-candidate) verify [P3 "Extensions and Variants": the draft
  * proposes a tree of candidates with several branches and the target
  * verifies every path; P2 39.4 for the rule at one candidate] for `rows`

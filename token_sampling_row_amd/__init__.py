@@ -14,6 +14,7 @@ from dataclasses import dataclass
 
 __all__ = [
     "TsrError", "TsrUnavailable", "Params", "Sampler", "library_path", "load_library",
+    "spec_verify_noalloc",
     "F32", "BF16", "JOINT", "SEQUENTIAL", "ROW_OK", "ROW_NONFINITE", "ROW_EMPTY",
     "ROW_BADTOKEN", "ROW_BADPARAM", "EXPORTED_SYMBOLS", "pack_row_params",
 ]
@@ -22,8 +23,8 @@ F32, BF16 = 0, 1
 JOINT, SEQUENTIAL = 0, 1
 ROW_OK, ROW_NONFINITE, ROW_EMPTY, ROW_BADTOKEN, ROW_BADPARAM = 0, 1, 2, 3, 4
 EXPORTED_SYMBOLS = ("sampler_init", "sampler_destroy", "greedy_argmax", "sample_rows",
-                    "sample_rows_masked", "sample_rows_ex", "spec_verify", "tree_verify",
-                    "beam_step",
+                    "sample_rows_masked", "sample_rows_ex", "spec_verify", "spec_verify_noalloc",
+                    "tree_verify", "beam_step",
                     "sampler_philox", "sampler_strerror")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -88,6 +89,8 @@ def load_library():
                                    vp]
     lib.spec_verify.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, ctypes.POINTER(_Params),
                                 u64, vp, vp, vp, vp]
+    lib.spec_verify_noalloc.argtypes = [i32, u64, vp, vp, i32, vp, i32, i32, i32,
+                                        ctypes.POINTER(_Params), u64, vp, vp, vp, vp]
     lib.tree_verify.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, ctypes.POINTER(_Params),
                                 u64, vp, vp, vp, vp, vp]
     lib.beam_step.argtypes = [vp, vp, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp]
@@ -153,6 +156,25 @@ def pack_row_params(params_list):
     import numpy as np
     arr = (_Params * len(params_list))(*[Params.of(p)._c() for p in params_list])
     return np.frombuffer(bytes(arr), dtype=np.uint8).copy()
+
+
+def spec_verify_noalloc(device, seed, target, draft, draft_tokens, params, step: int,
+                        out_tokens, out_accepted, out_status=None, stream=None):
+    """spec_verify without a handle or any device allocation in the library
+    (its workspace is a static device array; overlapping calls on one device
+    race). Outputs must be preallocated: out_tokens [rows, K+1] and
+    out_accepted [rows] int32 device tensors."""
+    import torch
+    rows, k1, vocab = target.shape
+    assert target.is_contiguous() and (draft is None or draft.is_contiguous())
+    assert draft_tokens.dtype == torch.int32 and draft_tokens.is_contiguous()
+    cp = Params.of(params)._c()
+    _check(load_library().spec_verify_noalloc(
+        int(device), ctypes.c_uint64(int(seed) & (2 ** 64 - 1)), _ptr(target), _ptr(draft),
+        _dtype_code(target), _ptr(draft_tokens), rows, k1 - 1, vocab, ctypes.byref(cp),
+        ctypes.c_uint64(int(step)), _ptr(out_tokens), _ptr(out_accepted), _ptr(out_status),
+        _stream_ptr(stream)), "spec_verify_noalloc")
+    return out_tokens, out_accepted
 
 
 class Sampler:

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "tsr.h"
@@ -132,6 +134,43 @@ int launch_verify_checked(const void* target_logits, const void* draft_logits, i
                                           K, vocab, aligned, ragged, kp, ws, out_tokens,
                                           out_accepted, out_status, (hipStream_t)hip_stream);
   return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
+}
+
+// spec_verify_noalloc's workspace: the per-(sequence, position) results (four
+// int32 arrays of kStaticSlots) and the per-sequence arrival counters
+// (kStaticSeqs), in `scratch` below: one copy per device, held until the
+// process ends, shared by every call on that device.
+constexpr int kStaticSlots = 1 << 16;   // sequences x (K + 1) positions
+constexpr int kStaticSeqs = 1 << 14;    // sequences
+constexpr size_t kStaticBytes =
+    4 * (size_t)kStaticSlots * sizeof(int32_t) + (size_t)kStaticSeqs * sizeof(uint32_t);
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices];   // device address of `scratch` on each device, once looked up
+
+}  // namespace
+
+// In host code `scratch` names a host-side stand-in, not device memory: only
+// its address from hipGetSymbolAddress (static_workspace) reaches kernels.
+static __device__ __align__(256) unsigned char scratch[kStaticBytes];
+
+namespace {
+
+// The device address of `scratch` on `device` (the current device), looked up
+// once per device and kept; *fresh is set by the lookup (the counters have not
+// been cleared on this device by this process yet).
+int static_workspace(int device, void** out, bool* fresh) {
+  *fresh = false;
+  if (device >= kMaxDevices) return TSR_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[device]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TSR_EDEVICE;
+    g_static_ptr[device] = p;
+    *fresh = true;
+  }
+  *out = g_static_ptr[device];
+  return TSR_OK;
 }
 
 }  // namespace
@@ -343,6 +382,42 @@ int spec_verify(tsr_handle h, const void* target_logits, const void* draft_logit
   return on_device(h->device, [&]() -> int {
     return launch_verify_checked(target_logits, draft_logits, dtype, draft_tokens, rows, K, vocab,
                                  kp, h->ws, out_tokens, out_accepted, out_status, hip_stream);
+  });
+}
+
+int spec_verify_noalloc(int device, uint64_t seed, const void* target_logits,
+                        const void* draft_logits, int dtype, const int32_t* draft_tokens,
+                        int rows, int K, int vocab, const tsr_params* params, uint64_t step,
+                        int32_t* out_tokens, int32_t* out_accepted, int32_t* out_status,
+                        void* hip_stream) {
+  if (rows > kStaticSeqs || (int64_t)rows * (K + 1) > kStaticSlots) return TSR_EINVAL;
+  const int rc = check_verify(target_logits, draft_logits, dtype, draft_tokens, rows, K, vocab,
+                              params, out_tokens, out_accepted);
+  if (rc != TSR_OK) return rc;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess) return TSR_EDEVICE;
+  if (device < 0 || device >= ndev) return TSR_EINVAL;
+  if (rows == 0) return TSR_OK;
+  const tsr::KParams kp = make_kparams(seed, params, vocab, step, false);
+  return on_device(device, [&]() -> int {
+    void* base = nullptr;
+    bool fresh = false;
+    const int src = static_workspace(device, &base, &fresh);
+    if (src != TSR_OK) return src;
+    int32_t* b = (int32_t*)base;
+    tsr::VerifyWs ws;
+    ws.acc = b;
+    ws.tok = b + kStaticSlots;
+    ws.st_t = b + 2 * kStaticSlots;
+    ws.st_d = b + 3 * kStaticSlots;
+    ws.counter = (uint32_t*)(b + 4 * kStaticSlots);
+    ws.kmax1 = K + 1;
+    if (fresh) {   // the arrival counters start at zero (each call leaves them at zero)
+      if (tsr::launch_fill_u32(ws.counter, kStaticSeqs, 0u, (hipStream_t)hip_stream) != hipSuccess)
+        return TSR_EDEVICE;
+    }
+    return launch_verify_checked(target_logits, draft_logits, dtype, draft_tokens, rows, K, vocab,
+                                 kp, ws, out_tokens, out_accepted, out_status, hip_stream);
   });
 }
 

@@ -62,6 +62,18 @@ hipError_t launch_sample(const void* logits, int dtype, int rows, int V, long lo
                     : launch_sample_dt1(p, rows, V, stride_bytes, aligned, ragged, kp, out, dg, s);
 }
 
+static __global__ void fill_u32_kernel(uint32_t* p, int n, uint32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, int n, uint32_t v, hipStream_t s) {
+  const int threads = 256;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((n + threads - 1) / threads), dim3(threads), 0, s, p,
+                     n, v);
+  return hipGetLastError();
+}
+
 hipError_t launch_philox(const uint32_t* ctr, int n, uint32_t k0, uint32_t k1, uint32_t* out,
                          hipStream_t s) {
   const int threads = 256;

@@ -116,5 +116,7 @@ hipError_t launch_beam(const void* logits, int dtype, int groups, int beam, int 
 int max_vocab_beam(int dtype);
 hipError_t launch_philox(const uint32_t* ctr, int n, uint32_t k0, uint32_t k1, uint32_t* out,
                          hipStream_t s);
+// p[0, n) = v (a kernel, so it can be captured in a graph).
+hipError_t launch_fill_u32(uint32_t* p, int n, uint32_t v, hipStream_t s);
 
 }  // namespace tsr
