@@ -414,9 +414,8 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   constexpr bool MASK = EXT == 1, REP = EXT == 1 || EXT == 2, UNAL = EXT == 3;
   KParams kp = kp0;
 #if TSR_TRACE
-  TSR_STAMP_P(kp0.trace, kStEntry);
-  trace_hw_id(kp0.trace);
   TSR_TRACE_INIT(kp0.trace);
+  TSR_STAMP(kStEntry);
 #endif
   if ((kp.flags & F_ROWP) && !row_kparams(kp, row, V)) {
     write_row(row, -1, kRowBadParam, 0, kNegInf, 0.0, kNaN, kNaN, out, dg);
@@ -435,10 +434,9 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   if constexpr (MASK) mk.load(kp.allowed + (long long)row * kp.allowed_stride, V);
   r.template load<UNAL>(p, V, ragged != 0);
   const bool greedy = (kp.flags & F_GREEDY) != 0;
-  const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);   // while the loads fly
-#if TSR_TRACE
-  TSR_STAMP_P(kp0.trace, kStIssued);
-#endif
+  const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);
+  asm volatile("" ::"s"(u));   // the draw's uniform while the loads fly
+  TSR_STAMP(kStIssued);
   const RowStats st = reg_stats<MASK, REP>(r, !greedy && joint_top_p(kp), kp.c, L, V, x, &mk);
   if (st.status != 0) {
     write_row(row, -1, st.status, 0, kNegInf, 0.0, kNaN, kNaN, out, dg);
@@ -495,6 +493,7 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   }
   write_row(row, tok, 0, kept, tau, 0.0, wt, zs, out, dg);
   TSR_STAMP(kStEnd);
+  TSR_TRACE_FLUSH();
 }
 
 // Rows wider than the register file: every pass streams the row.

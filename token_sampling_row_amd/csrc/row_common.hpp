@@ -53,6 +53,7 @@ struct Lds {
   float hval[kHistMax];             // its penalised logits (register path)
   double tz[32];                    // tree verify: 1 / Z of each residual step
   uint32_t hbits[kWave];            // chunks holding a window token, hashed (chunk mod 2048)
+  uint32_t tk[2][kWaves][32];       // top-k bound: per-wave counts of 32 key buckets, two levels
   WaveStats ws[kWaves];
   BlockScratch bs;
   int si[8];
@@ -60,7 +61,7 @@ struct Lds {
   float sf[8];
   double sd[8];
 #if TSR_TRACE
-  unsigned long long* trace;        // the launch's stamp buffer (tracing build)
+  TraceLds trace;                   // the phase stamps (tracing build)
 #endif
 };
 
@@ -165,16 +166,17 @@ __device__ __forceinline__ uint4 penalize_chunk(uint4 t, uint32_t hit, double r)
 // do the non-inlined functions of the streaming path.
 static __shared__ Lds tsr_lds;
 
-// A phase stamp from code past the kernel's first barrier (the kernel puts
-// the stamp buffer in LDS at entry); empty outside the tracing build.
-// Every kernel that reaches a stamp sets the buffer at entry (null: none).
+// Phase stamps (tracing build; empty statements otherwise): a kernel that
+// stamps begins the record at entry (null buffer: none kept) and flushes it
+// when its row is done.
 #if TSR_TRACE
-#define TSR_STAMP(slot) TSR_STAMP_P(::tsr::tsr_lds.trace, (slot))
-#define TSR_TRACE_INIT(ptr) \
-  do { if (threadIdx.x % kWave == 0) ::tsr::tsr_lds.trace = (ptr); } while (0)
+#define TSR_STAMP(slot) ::tsr::trace_stamp(::tsr::tsr_lds.trace, (slot))
+#define TSR_TRACE_INIT(ptr) ::tsr::trace_begin(::tsr::tsr_lds.trace, (ptr))
+#define TSR_TRACE_FLUSH() ::tsr::trace_flush(::tsr::tsr_lds.trace)
 #else
 #define TSR_STAMP(slot) ((void)0)
 #define TSR_TRACE_INIT(ptr) ((void)0)
+#define TSR_TRACE_FLUSH() ((void)0)
 #endif
 
 // The look-back window of the repetition penalty, published by wave 0 (all

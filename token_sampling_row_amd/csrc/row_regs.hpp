@@ -326,9 +326,7 @@ __device__ __forceinline__ RowStats reg_stats(RegRow<DT, NC>& r, bool need_zlo, 
   int nallow = 0x7FFFFFFF;
   double zown = 0.0;
   float tmax = reg_pass_a<MASK, ZEXACT>(r, L, c, &zown, mk, &nallow);
-#if TSR_TRACE
-  TSR_STAMP_P(L.trace, kStPassA);   // (the pointer was stored at entry by this thread's wave 0)
-#endif
+  TSR_STAMP(kStPassA);
   if (REP && x.hn > 0) {
     if (threadIdx.x < kWave) {
       // wave 0: each window token's logit, read back from the row (one per

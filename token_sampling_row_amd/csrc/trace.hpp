@@ -1,9 +1,11 @@
 // Per-wavefront phase stamps, compiled only into the tracing build of the
 // library (TSR_TRACE=1, libtsr_trace.so); in the ordinary build every stamp is
-// an empty statement. Lane 0 of each wavefront writes the 100 MHz real-time
-// counter (s_memrealtime, the same clock on every compute unit) to
-// trace[(block * kWaves + wave) * kTraceSlots + slot] with an ordinary vector
-// store. The buffer belongs to the handle (sampler_trace_read).
+// an empty statement. Lane 0 of each wavefront records the 100 MHz real-time
+// counter (s_memrealtime, the same clock on every compute unit) in LDS at
+// each phase, and copies its record to the handle's buffer with ordinary
+// vector stores when the row is done (trace[(block * waves + wave) * 16 +
+// slot]): a store in flight would otherwise hold up the next barrier, which
+// waits for the wavefront's outstanding memory operations.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,6 +19,7 @@ namespace tsr {
 
 constexpr int kTraceSlots = 16;     // phase slots per wavefront
 constexpr int kTraceBlocks = 4096;  // workgroups traced per launch (the first ones)
+constexpr int kTraceWaves = 8;      // wavefronts per workgroup recorded
 
 // Slots of the sampler kernels (a slot a row does not reach stays 0).
 enum : int {
@@ -39,26 +42,35 @@ enum : int {
 };
 
 #if TSR_TRACE
-__device__ __forceinline__ void trace_stamp(unsigned long long* buf, int slot) {
-  if (buf && (threadIdx.x & 63) == 0 && blockIdx.x < (unsigned)kTraceBlocks) {
-    const unsigned long long t = __builtin_amdgcn_s_memrealtime();
-    buf[((unsigned long long)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64) * kTraceSlots +
-        slot] = t;
-  }
-}
-// Where the wavefront runs: the accelerator complex die (XCC_ID) and the
-// wave / SIMD / compute unit / shader array / engine fields of HW_ID.
-__device__ __forceinline__ void trace_hw_id(unsigned long long* buf) {
-  if (buf && (threadIdx.x & 63) == 0 && blockIdx.x < (unsigned)kTraceBlocks) {
+// The stamp record of the workgroup, in its LDS.
+struct TraceLds {
+  unsigned long long t[kTraceWaves][kTraceSlots];
+  unsigned long long* buf;   // the launch's buffer (null: not traced)
+};
+
+__device__ __forceinline__ void trace_begin(TraceLds& T, unsigned long long* buf) {
+  const int w = threadIdx.x / 64;
+  if ((threadIdx.x & 63) == 0 && w < kTraceWaves) {
+    T.buf = buf;
+#pragma unroll
+    for (int s = 0; s < kTraceSlots; ++s) T.t[w][s] = 0ull;
     const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_REG_HW_ID
     const unsigned xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // HW_REG_XCC_ID
-    buf[((unsigned long long)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64) * kTraceSlots +
-        kStHwId] = ((unsigned long long)(xcc & 0xFFFFu) << 16) | (hw & 0xFFFFu);
+    T.t[w][kStHwId] = ((unsigned long long)(xcc & 0xFFFFu) << 16) | (hw & 0xFFFFu);
   }
 }
-#define TSR_STAMP_P(buf, slot) ::tsr::trace_stamp((buf), (slot))
-#else
-#define TSR_STAMP_P(buf, slot) ((void)0)
+__device__ __forceinline__ void trace_stamp(TraceLds& T, int slot) {
+  const int w = threadIdx.x / 64;
+  if ((threadIdx.x & 63) == 0 && w < kTraceWaves) T.t[w][slot] = __builtin_amdgcn_s_memrealtime();
+}
+__device__ __forceinline__ void trace_flush(TraceLds& T) {
+  const int w = threadIdx.x / 64;
+  if ((threadIdx.x & 63) == 0 && w < kTraceWaves && T.buf && blockIdx.x < (unsigned)kTraceBlocks) {
+    unsigned long long* o = T.buf + ((unsigned long long)blockIdx.x * kTraceWaves + w) * kTraceSlots;
+#pragma unroll
+    for (int s = 0; s < kTraceSlots; ++s) o[s] = T.t[w][s];
+  }
+}
 #endif
 
 }  // namespace tsr
