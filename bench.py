@@ -414,6 +414,31 @@ def run_extra(torch, tsr, wl, steps, warmup):
             res[f"verify64_k4_32000_f32_{name}"] = r
         del tgs, dfs
 
+        # the verify step at a 128,256-id bf16 vocabulary (wider than a
+        # workgroup holds two rows of: one workgroup per row, then one per
+        # sequence), 64 sequences, K = 4, generated as the 32000 fp32 batch is
+        nseq, K, V = 64, 4, 128256
+        tgt_b, dft_b = wl.verify_batch(1040, nseq, K, V, "bf16")
+        tg = torch.from_numpy(tgt_b.view(np.int16)).to(dev).view(torch.bfloat16)
+        df = torch.from_numpy(dft_b.view(np.int16)).to(dev).view(torch.bfloat16)
+        tgs = [tg.clone() for _ in range(ROTATE)]
+        dfs = [df.clone() for _ in range(ROTATE)]
+        xs = s.sample_rows(df.view(nseq * K, V), {"temperature": 1.0}, 778)
+        xs = xs.view(nseq, K).contiguous()
+        toks = torch.empty(nseq, K + 1, dtype=torch.int32, device=dev)
+        acc = torch.empty(nseq, dtype=torch.int32, device=dev)
+        for name, prm in (("T1", {"temperature": 1.0}), ("greedy", {"temperature": 0.0})):
+            ms = time_calls(torch, lambda i: s.spec_verify(tgs[i % ROTATE], dfs[i % ROTATE], xs, prm,
+                                                           i, out_tokens=toks, out_accepted=acc),
+                            steps, warmup)
+            a = acc.float().mean().item()
+            rows_read = (2 * K + 1) if prm["temperature"] else (K + 1)
+            r = _rates(nseq, nseq * rows_read * V * 2, ms)
+            r.update(acceptance_rate=a / K, tokens_per_verify=a + 1,
+                     tokens_per_s=nseq * (a + 1) / (ms * 1e-3))
+            res[f"verify64_k4_128256_bf16_{name}"] = r
+        del tgs, dfs, tg, df
+
         # constrained decoding on the headline batch: allowed-token bitmask
         # (V/8 bytes per row more) and log p~ of each draw
         w = wl.config(3)

@@ -229,7 +229,11 @@ int sample_rows_ex(tsr_handle h, const void* logits, int dtype, int rows, int vo
  *  out_tokens   [rows][K+1]: emitted ids, -1 after the last one.
  *  out_accepted [rows]:      number of drafts kept (0..K).
  *  out_status   [rows] (nullable): TSR_ROW_*; a bad sequence gets all -1 and 0.
- * 1 <= K <= max_k (set by sampler_init) and K <= 32. */
+ * 1 <= K <= max_k (set by sampler_init) and K <= 32. vocab <= 155,648 bf16
+ * or 77,824 float32 logits (TSR_EUNSUPPORTED beyond). Up to 65,536 bf16 or
+ * 32,768 float32 logits each position's two rows are held in one workgroup's
+ * registers; wider rows take one workgroup per row, then one per sequence,
+ * which re-reads the rejecting position's rows for the residual draw. */
 int spec_verify(tsr_handle h, const void* target_logits, const void* draft_logits,
                 int dtype, const int32_t* draft_tokens, int rows, int K, int vocab,
                 const tsr_params* params, uint64_t step, int32_t* out_tokens,
@@ -242,7 +246,9 @@ int spec_verify(tsr_handle h, const void* target_logits, const void* draft_logit
  * verify workspace is a static device array in the library, about 1.1 MB, one
  * copy per device, held until the process ends; the call allocates nothing
  * and calls no allocating routine. Limits of that array: rows <= 16384 and
- * rows * (K + 1) <= 65536 (TSR_EINVAL beyond); 1 <= K <= 32. The first call on
+ * rows * (K + 1) <= 65536 (TSR_EINVAL beyond); 1 <= K <= 32; vocab <= 65,536
+ * bf16 or 32,768 float32 logits (TSR_EUNSUPPORTED beyond: the array holds no
+ * per-row records for spec_verify's wider-row path). The first call on
  * a device also enqueues one small kernel that zeroes the array's counters.
  * Every call on a device shares that device's array: calls that overlap on
  * one device (on different streams, or from several threads) race and give
@@ -279,6 +285,9 @@ int spec_verify_noalloc(int device, uint64_t seed, const void* target_logits,
  *      (nullable): TSR_ROW_* (NONFINITE/EMPTY for a bad target row or a bad
  *      draft row of a node with children, BADTOKEN for a token outside
  *      [0, vocab), 5 for a parent that is not an earlier node).
+ * vocab limits as spec_verify's (above 65,536 bf16 or 32,768 float32 logits,
+ * one workgroup per row, then one per sequence that follows the tree and
+ * streams the rows of the nodes where candidates were rejected).
  * Shares the verify workspace: not concurrent with spec_verify on the handle. */
 int tree_verify(tsr_handle h, const void* target_logits, const void* draft_logits, int dtype,
                 const int32_t* parent, const int32_t* tokens, int rows, int nodes, int vocab,

@@ -172,6 +172,10 @@ def test_spec_verify_rejects_each_invalid_argument(env):
     assert call(xs=ctypes.c_void_p(0)) == EINVAL
     assert call(tgt=vp(e["big"]), dft=vp(e["big"]), rows=0, dtype=1,
                 vocab=BIG_VOCAB) == EUNSUPPORTED
+    # one past the widest verify rows: 155,648 bf16 and 77,824 fp32 logits
+    assert call(tgt=vp(e["big"]), dft=vp(e["big"]), rows=0, dtype=1, vocab=155649) == EUNSUPPORTED
+    assert call(tgt=vp(e["big"]), dft=vp(e["big"]), rows=0, dtype=0, vocab=77825) == EUNSUPPORTED
+    assert call(tgt=vp(e["big"]), dft=vp(e["big"]), rows=0, dtype=1, vocab=155648) == 0
     assert untouched(toks, acc, st)
 
 

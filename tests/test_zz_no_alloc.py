@@ -74,5 +74,9 @@ def test_noalloc_verify_rejects_sizes_beyond_its_array():
                                    None, None) == 1                              # K > 32
     assert lib.spec_verify_noalloc(99, 1, ptr, ptr, 0, ptr, 4, 2, 8, ctypes.byref(p), 0, ptr, ptr,
                                    None, None) == 1                              # no such device
+    # rows wider than the register-pair path (65,536 bf16 / 32,768 fp32 logits)
+    for dtype, vocab in ((1, 65537), (0, 32769)):
+        assert lib.spec_verify_noalloc(0, 1, ptr, ptr, dtype, ptr, 4, 2, vocab, ctypes.byref(p), 0,
+                                       ptr, ptr, None, None) == 4
     torch.cuda.synchronize()
     assert int(buf.abs().sum()) == 0

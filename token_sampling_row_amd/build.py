@@ -28,6 +28,7 @@ LIB_TRACE = os.path.join(HERE, "libtsr_trace.so")
 ARCH = os.environ.get("TSR_OFFLOAD_ARCH", "gfx950")
 ROW_NCS = (1, 2, 4, 8, 16, 24, 32, 38)      # must match kRowNcs in dispatch.hpp
 VERIFY_NCS = (1, 2, 4, 8, 16)               # must match kVerifyNcs
+VERIFY_WIDE_NCS = (24, 32, 38)              # must match kVerifyWideNcs
 DISPATCH = ["k_greedy.hip", "k_beam.hip", "k_sample_f32.hip", "k_sample_bf16.hip", "k_verify_f32.hip",
             "k_verify_bf16.hip", "k_misc.hip", "api.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
@@ -79,6 +80,20 @@ def instance_units() -> dict[str, str]:
                     f"template __global__ void tree_kernel<{dt}, {nc}, {un}>(const unsigned char*, "
                     "const unsigned char*, const int32_t*, const int32_t*, int, int, int, KParams, "
                     "VerifyWs, int32_t*, int32_t*, int32_t*, int32_t*);\n}\n")
+        for nc in VERIFY_WIDE_NCS:
+            for un in ("false", "true"):
+                for tree in ("false", "true"):
+                    units[f"i_vrows_{dt}_{nc}_{un}_{tree}.hip"] = head + (
+                        f"template __global__ void verify_rows_kernel<{dt}, {nc}, {un}, {tree}>("
+                        "const unsigned char*, const unsigned char*, const int32_t*, int, int, int, "
+                        "KParams, VerifyWs);\n}\n")
+        units[f"i_vfinish_{dt}.hip"] = head + (
+            f"template __global__ void verify_finish_kernel<{dt}>(const unsigned char*, const "
+            "unsigned char*, const int32_t*, int, int, int, KParams, VerifyWs, int32_t*, int32_t*, "
+            "int32_t*);\n"
+            f"template __global__ void tree_finish_kernel<{dt}>(const unsigned char*, const unsigned "
+            "char*, const int32_t*, const int32_t*, int, int, int, KParams, VerifyWs, int32_t*, "
+            "int32_t*, int32_t*, int32_t*);\n}\n")
         units[f"i_stream_{dt}.hip"] = head + (
             f"template __global__ void sample_kernel_stream<{dt}>(const unsigned char*, long long, "
             "int, int, KParams, int32_t*, DiagPtrs);\n"

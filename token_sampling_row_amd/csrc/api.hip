@@ -207,8 +207,10 @@ int sampler_init(tsr_handle* out, int device, int max_rows, int max_vocab, int m
     const size_t slots = (size_t)max_rows * (size_t)(max_k + 1);
     const size_t vbytes = 4 * slots * sizeof(int32_t) + (size_t)max_rows * sizeof(uint32_t);
     const size_t bslots = (size_t)max_rows * tsr::kBeamMax;
-    const size_t bytes = ((vbytes + 7) & ~(size_t)7) + bslots * (sizeof(double) + sizeof(int32_t)) +
-                         2 * (size_t)max_rows * sizeof(uint32_t);
+    const size_t rbytes = (size_t)max_rows * 2 * (size_t)(max_k + 1) * sizeof(tsr::RowRec);
+    const size_t bbytes = bslots * (sizeof(double) + sizeof(int32_t)) +
+                          2 * (size_t)max_rows * sizeof(uint32_t);
+    const size_t bytes = ((vbytes + 7) & ~(size_t)7) + rbytes + bbytes;
     if (hipMalloc(&h->ws_block, bytes) != hipSuccess) return TSR_ENOMEM;
     if (hipMemset(h->ws_block, 0, bytes) != hipSuccess) return TSR_EDEVICE;
     if (hipDeviceSynchronize() != hipSuccess) return TSR_EDEVICE;
@@ -219,8 +221,11 @@ int sampler_init(tsr_handle* out, int device, int max_rows, int max_vocab, int m
     h->ws.st_d = base + 3 * slots;
     h->ws.counter = (uint32_t*)(base + 4 * slots);
     h->ws.kmax1 = max_k + 1;
+    // wide verify: per sequence 2 (max_k + 1) row records
+    h->ws.rec = (tsr::RowRec*)((char*)h->ws_block + ((vbytes + 7) & ~(size_t)7));
+    h->ws.recs = 2 * (max_k + 1);
     // beam step: per row kBeamMax (score, token), per group a flag and a counter
-    char* bb = (char*)h->ws_block + ((vbytes + 7) & ~(size_t)7);
+    char* bb = (char*)h->ws_block + ((vbytes + 7) & ~(size_t)7) + rbytes;
     h->bws.score = (double*)bb;
     h->bws.tok = (int32_t*)(bb + bslots * sizeof(double));
     h->bws.bad = (uint32_t*)(bb + bslots * (sizeof(double) + sizeof(int32_t)));
@@ -394,6 +399,7 @@ int spec_verify_noalloc(int device, uint64_t seed, const void* target_logits,
   const int rc = check_verify(target_logits, draft_logits, dtype, draft_tokens, rows, K, vocab,
                               params, out_tokens, out_accepted);
   if (rc != TSR_OK) return rc;
+  if (vocab > tsr::max_vocab_verify_narrow(dtype)) return TSR_EUNSUPPORTED;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess) return TSR_EDEVICE;
   if (device < 0 || device >= ndev) return TSR_EINVAL;
@@ -412,6 +418,8 @@ int spec_verify_noalloc(int device, uint64_t seed, const void* target_logits,
     ws.st_d = b + 3 * kStaticSlots;
     ws.counter = (uint32_t*)(b + 4 * kStaticSlots);
     ws.kmax1 = K + 1;
+    ws.rec = nullptr;   // the array holds no row records: register-pair rows only
+    ws.recs = 0;
     if (fresh) {   // the arrival counters start at zero (each call leaves them at zero)
       if (tsr::launch_fill_u32(ws.counter, kStaticSeqs, 0u, (hipStream_t)hip_stream) != hipSuccess)
         return TSR_EDEVICE;

@@ -2,12 +2,13 @@
 // smallest count that covers the row.
 #pragma once
 
-#include "kernels_impl.hpp"
+#include "verify_wide.hpp"
 
 namespace tsr {
 
 #define TSR_ROW_NCS(X) X(1) X(2) X(4) X(8) X(16) X(24) X(32) X(38)
 #define TSR_VERIFY_NCS(X) X(1) X(2) X(4) X(8) X(16)
+#define TSR_VERIFY_WIDE_NCS(X) X(24) X(32) X(38)
 
 inline int chunks_per_thread(int dtype, int V) {
   const int epc = dtype == 0 ? 4 : 8;
@@ -23,6 +24,7 @@ inline int pick_nc(int needed, const int* list, int n) {
 
 constexpr int kRowNcs[] = {1, 2, 4, 8, 16, 24, 32, 38};
 constexpr int kVerifyNcs[] = {1, 2, 4, 8, 16};
+constexpr int kVerifyWideNcs[] = {24, 32, 38};
 
 // Each kernel instance is compiled in a translation unit of its own (the
 // build generates them), so the units that launch them only declare them.
@@ -65,9 +67,28 @@ constexpr int kVerifyNcs[] = {1, 2, 4, 8, 16};
 #define TSR_DECLARE_VERIFY(N)                                                                \
   TSR_DECLARE_VERIFY_DT(0, N, false) TSR_DECLARE_VERIFY_DT(0, N, true)                       \
   TSR_DECLARE_VERIFY_DT(1, N, false) TSR_DECLARE_VERIFY_DT(1, N, true)
+#define TSR_DECLARE_VROWS_DT(D, N, U, T)                                                      \
+  extern template __global__ void verify_rows_kernel<D, N, U, T>(                             \
+      const unsigned char*, const unsigned char*, const int32_t*, int, int, int, KParams,      \
+      VerifyWs);
+#define TSR_DECLARE_VROWS(N)                                                                 \
+  TSR_DECLARE_VROWS_DT(0, N, false, false) TSR_DECLARE_VROWS_DT(0, N, true, false)           \
+  TSR_DECLARE_VROWS_DT(1, N, false, false) TSR_DECLARE_VROWS_DT(1, N, true, false)           \
+  TSR_DECLARE_VROWS_DT(0, N, false, true) TSR_DECLARE_VROWS_DT(0, N, true, true)             \
+  TSR_DECLARE_VROWS_DT(1, N, false, true) TSR_DECLARE_VROWS_DT(1, N, true, true)
+#define TSR_DECLARE_VFINISH(D)                                                                \
+  extern template __global__ void verify_finish_kernel<D>(                                    \
+      const unsigned char*, const unsigned char*, const int32_t*, int, int, int, KParams,      \
+      VerifyWs, int32_t*, int32_t*, int32_t*);                                                 \
+  extern template __global__ void tree_finish_kernel<D>(                                      \
+      const unsigned char*, const unsigned char*, const int32_t*, const int32_t*, int, int,    \
+      int, KParams, VerifyWs, int32_t*, int32_t*, int32_t*, int32_t*);
 #ifndef TSR_INSTANCE_UNIT
 TSR_ROW_NCS(TSR_DECLARE_ROW)
 TSR_VERIFY_NCS(TSR_DECLARE_VERIFY)
+TSR_VERIFY_WIDE_NCS(TSR_DECLARE_VROWS)
+TSR_DECLARE_VFINISH(0)
+TSR_DECLARE_VFINISH(1)
 extern template __global__ void sample_kernel_stream<0>(const unsigned char*, long long, int, int,
                                                         KParams, int32_t*, DiagPtrs);
 extern template __global__ void sample_kernel_stream<1>(const unsigned char*, long long, int, int,

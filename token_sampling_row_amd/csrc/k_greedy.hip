@@ -46,6 +46,7 @@ hipError_t launch_greedy(const void* logits, int dtype, int rows, int V, long lo
 // Rows stream when they exceed the register file; the bound keeps histogram
 // masses (2^40 fixed point, weights <= 1) inside 64 bits.
 int max_vocab_sample(int) { return 1 << 23; }
-int max_vocab_verify(int dtype) { return 16 * kBlock * (dtype == 0 ? 4 : 8); }
+int max_vocab_verify_narrow(int dtype) { return 16 * kBlock * (dtype == 0 ? 4 : 8); }
+int max_vocab_verify(int dtype) { return 38 * kBlock * (dtype == 0 ? 4 : 8); }
 
 }  // namespace tsr

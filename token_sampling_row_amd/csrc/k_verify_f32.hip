@@ -7,7 +7,32 @@ hipError_t launch_verify_dt0(const unsigned char* tp, const unsigned char* dp, c
                              int rows, int K, int V, int aligned, int ragged, const KParams& kp,
                              const VerifyWs& ws, int32_t* out_tokens, int32_t* out_acc,
                              int32_t* out_status, hipStream_t s) {
-  const int nc = pick_nc(chunks_per_thread(0, V), kVerifyNcs, 5);
+  const int need = chunks_per_thread(0, V);
+  if (need > 16) {
+    // wider rows: one row per workgroup, then one sequence per workgroup
+    const int ncw = pick_nc(need, kVerifyWideNcs, 3);
+    if (ncw == 0 || !ws.rec) return hipErrorInvalidValue;
+    const bool greedy = (kp.flags & F_GREEDY) != 0;
+    const dim3 grid_rows((unsigned)rows * (unsigned)(greedy ? K + 1 : 2 * K + 1));
+#define TSR_WCASE(N)                                                                         \
+  case N:                                                                                    \
+    if (aligned)                                                                             \
+      hipLaunchKernelGGL((verify_rows_kernel<0, N, false, false>), grid_rows, dim3(kBlock), 0, \
+                         s, tp, dp, nullptr, K, V, ragged, kp, ws);                          \
+    else                                                                                     \
+      hipLaunchKernelGGL((verify_rows_kernel<0, N, true, false>), grid_rows, dim3(kBlock), 0,  \
+                         s, tp, dp, nullptr, K, V, ragged, kp, ws);                          \
+    break;
+    switch (ncw) {
+      TSR_VERIFY_WIDE_NCS(TSR_WCASE)
+      default: return hipErrorInvalidValue;
+    }
+#undef TSR_WCASE
+    hipLaunchKernelGGL((verify_finish_kernel<0>), dim3(rows), dim3(kBlock), 0, s, tp, dp, xs, K,
+                       V, aligned, kp, ws, out_tokens, out_acc, out_status);
+    return hipGetLastError();
+  }
+  const int nc = pick_nc(need, kVerifyNcs, 5);
   const dim3 grid((unsigned)rows * (unsigned)(K + 1));
 #define TSR_CASE(N)                                                                          \
   case N:                                                                                    \
@@ -31,7 +56,31 @@ hipError_t launch_tree_dt0(const unsigned char* tp, const unsigned char* dp,
                            int aligned, int ragged, const KParams& kp, const VerifyWs& ws,
                            int32_t* out_tokens, int32_t* out_path, int32_t* out_acc,
                            int32_t* out_status, hipStream_t s) {
-  const int nc = pick_nc(chunks_per_thread(0, V), kVerifyNcs, 5);
+  const int need = chunks_per_thread(0, V);
+  if (need > 16) {
+    const int ncw = pick_nc(need, kVerifyWideNcs, 3);
+    if (ncw == 0 || !ws.rec) return hipErrorInvalidValue;
+    const bool greedy = (kp.flags & F_GREEDY) != 0;
+    const dim3 grid_rows((unsigned)rows * (unsigned)(greedy ? N : 2 * N));
+#define TSR_WCASE(N_)                                                                        \
+  case N_:                                                                                   \
+    if (aligned)                                                                             \
+      hipLaunchKernelGGL((verify_rows_kernel<0, N_, false, true>), grid_rows, dim3(kBlock), 0, \
+                         s, tp, dp, parent, N, V, ragged, kp, ws);                           \
+    else                                                                                     \
+      hipLaunchKernelGGL((verify_rows_kernel<0, N_, true, true>), grid_rows, dim3(kBlock), 0,  \
+                         s, tp, dp, parent, N, V, ragged, kp, ws);                           \
+    break;
+    switch (ncw) {
+      TSR_VERIFY_WIDE_NCS(TSR_WCASE)
+      default: return hipErrorInvalidValue;
+    }
+#undef TSR_WCASE
+    hipLaunchKernelGGL((tree_finish_kernel<0>), dim3(rows), dim3(kBlock), 0, s, tp, dp, parent,
+                       tokens, N, V, aligned, kp, ws, out_tokens, out_path, out_acc, out_status);
+    return hipGetLastError();
+  }
+  const int nc = pick_nc(need, kVerifyNcs, 5);
   const dim3 grid((unsigned)rows * (unsigned)N);
 #define TSR_CASE(N_)                                                                         \
   case N_:                                                                                   \

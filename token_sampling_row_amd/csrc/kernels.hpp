@@ -80,8 +80,21 @@ struct BeamWs {
   uint32_t* counter;
 };
 
+// What the wide verify path records of one target or draft row: the kept
+// weight sum Z_S, the row maximum M, the kept set {v >= tau}, the status, and
+// a token (greedy: the argmax; else the row's own draw where it is known).
+struct RowRec {
+  double zs;
+  float M;
+  float tau;
+  int status;
+  int tok;
+};
+
 // Per-handle workspace of the verify step: per (sequence, position) results
-// and one arrival counter per sequence (zero between calls).
+// and one arrival counter per sequence (zero between calls); for rows wider
+// than two register rows per workgroup, `recs` row records per sequence (its
+// target rows from 0, its draft rows from recs / 2).
 struct VerifyWs {
   int32_t* acc;
   int32_t* tok;
@@ -89,10 +102,13 @@ struct VerifyWs {
   int32_t* st_d;
   uint32_t* counter;
   int kmax1;      // max_k + 1: stride of the per-position arrays
+  RowRec* rec;    // null: the wide path is not available
+  int recs;       // 2 * kmax1
 };
 
 int max_vocab_sample(int dtype);
-int max_vocab_verify(int dtype);
+int max_vocab_verify(int dtype);          // with the row records (wide rows)
+int max_vocab_verify_narrow(int dtype);   // without them
 
 // aligned: every row starts on a 16-byte boundary. ragged: a row does not
 // split into whole 16-byte chunks (vocab not a multiple of 4 / 8, or unaligned).

@@ -53,7 +53,6 @@ struct Lds {
   float hval[kHistMax];             // its penalised logits (register path)
   double tz[32];                    // tree verify: 1 / Z of each residual step
   uint32_t hbits[kWave];            // chunks holding a window token, hashed (chunk mod 2048)
-  uint32_t tk[2][kWaves][32];       // top-k bound: per-wave counts of 32 key buckets, two levels
   WaveStats ws[kWaves];
   BlockScratch bs;
   int si[8];

@@ -154,6 +154,22 @@ def random_rows(seed: int, rows: int, vocab: int, a: float = 1.0, sigma: float =
     return _round_rows(out, dtype)
 
 
+def verify_batch(seed: int, rows: int, K: int, vocab: int, dtype: str = BF16, a: float = 1.0,
+                 sigma: float = 0.5, noise: float = 0.8):
+    """A speculative-verify batch of any size, generated as workload 4 is:
+    target rows [rows, K + 1, vocab] of Zipf-like logits, one per (sequence,
+    position); draft rows [rows, K, vocab] = the target's first K positions
+    plus N(0, noise^2). Returns the two as stored bits."""
+    tgt = np.empty((rows, K + 1, vocab), dtype=np.float64)
+    for b in range(rows):
+        for j in range(K + 1):
+            tgt[b, j] = zipf_row([seed, b, j], vocab, a, sigma)
+    dft = tgt[:, :K, :] + np.random.default_rng([seed, 1 << 20]).normal(0.0, noise,
+                                                                         (rows, K, vocab))
+    return (_round_rows(tgt.reshape(rows * (K + 1), vocab), dtype).reshape(rows, K + 1, vocab),
+            _round_rows(dft.reshape(rows * K, vocab), dtype).reshape(rows, K, vocab))
+
+
 def allowed_words(seed: int, rows: int, vocab: int, kind: str) -> np.ndarray:
     """Seeded allowed-token bitmasks for constrained decoding, packed as the
     sampler reads them: uint32 [rows, ceil(vocab / 32)], token i allowed iff
