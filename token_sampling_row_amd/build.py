@@ -91,6 +91,8 @@ def instance_units() -> dict[str, str]:
             f"template __global__ void verify_finish_kernel<{dt}>(const unsigned char*, const "
             "unsigned char*, const int32_t*, int, int, int, KParams, VerifyWs, int32_t*, int32_t*, "
             "int32_t*);\n"
+            f"template __global__ void verify_draw_kernel<{dt}>(const unsigned char*, const "
+            "unsigned char*, int, int, int, KParams, VerifyWs, int32_t*);\n"
             f"template __global__ void tree_finish_kernel<{dt}>(const unsigned char*, const unsigned "
             "char*, const int32_t*, const int32_t*, int, int, int, KParams, VerifyWs, int32_t*, "
             "int32_t*, int32_t*, int32_t*);\n}\n")

@@ -207,7 +207,8 @@ int sampler_init(tsr_handle* out, int device, int max_rows, int max_vocab, int m
     const size_t slots = (size_t)max_rows * (size_t)(max_k + 1);
     const size_t vbytes = 4 * slots * sizeof(int32_t) + (size_t)max_rows * sizeof(uint32_t);
     const size_t bslots = (size_t)max_rows * tsr::kBeamMax;
-    const size_t rbytes = (size_t)max_rows * 2 * (size_t)(max_k + 1) * sizeof(tsr::RowRec);
+    const size_t rbytes = (size_t)max_rows * 2 * (size_t)(max_k + 1) * sizeof(tsr::RowRec) +
+                          (size_t)max_rows * 2 * tsr::kMaxSlices * sizeof(unsigned long long);
     const size_t bbytes = bslots * (sizeof(double) + sizeof(int32_t)) +
                           2 * (size_t)max_rows * sizeof(uint32_t);
     const size_t bytes = ((vbytes + 7) & ~(size_t)7) + rbytes + bbytes;
@@ -224,6 +225,7 @@ int sampler_init(tsr_handle* out, int device, int max_rows, int max_vocab, int m
     // wide verify: per sequence 2 (max_k + 1) row records
     h->ws.rec = (tsr::RowRec*)((char*)h->ws_block + ((vbytes + 7) & ~(size_t)7));
     h->ws.recs = 2 * (max_k + 1);
+    h->ws.part = (unsigned long long*)(h->ws.rec + (size_t)max_rows * 2 * (max_k + 1));
     // beam step: per row kBeamMax (score, token), per group a flag and a counter
     char* bb = (char*)h->ws_block + ((vbytes + 7) & ~(size_t)7) + rbytes;
     h->bws.score = (double*)bb;
@@ -420,6 +422,7 @@ int spec_verify_noalloc(int device, uint64_t seed, const void* target_logits,
     ws.kmax1 = K + 1;
     ws.rec = nullptr;   // the array holds no row records: register-pair rows only
     ws.recs = 0;
+    ws.part = nullptr;
     if (fresh) {   // the arrival counters start at zero (each call leaves them at zero)
       if (tsr::launch_fill_u32(ws.counter, kStaticSeqs, 0u, (hipStream_t)hip_stream) != hipSuccess)
         return TSR_EDEVICE;

@@ -80,6 +80,8 @@ constexpr int kVerifyWideNcs[] = {24, 32, 38};
   extern template __global__ void verify_finish_kernel<D>(                                    \
       const unsigned char*, const unsigned char*, const int32_t*, int, int, int, KParams,      \
       VerifyWs, int32_t*, int32_t*, int32_t*);                                                 \
+  extern template __global__ void verify_draw_kernel<D>(                                      \
+      const unsigned char*, const unsigned char*, int, int, int, KParams, VerifyWs, int32_t*); \
   extern template __global__ void tree_finish_kernel<D>(                                      \
       const unsigned char*, const unsigned char*, const int32_t*, const int32_t*, int, int,    \
       int, KParams, VerifyWs, int32_t*, int32_t*, int32_t*, int32_t*);

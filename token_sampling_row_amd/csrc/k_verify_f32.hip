@@ -28,8 +28,15 @@ hipError_t launch_verify_dt0(const unsigned char* tp, const unsigned char* dp, c
       default: return hipErrorInvalidValue;
     }
 #undef TSR_WCASE
-    hipLaunchKernelGGL((verify_finish_kernel<0>), dim3(rows), dim3(kBlock), 0, s, tp, dp, xs, K,
-                       V, aligned, kp, ws, out_tokens, out_acc, out_status);
+    // the residual in slices of kSliceRows chunk rows (one slice when greedy)
+    VerifyWs wf = ws;
+    wf.nseq = rows;
+    const int S = greedy ? 1 : (need + kSliceRows - 1) / kSliceRows;
+    hipLaunchKernelGGL((verify_finish_kernel<0>), dim3((unsigned)rows * (unsigned)S), dim3(kBlock),
+                       0, s, tp, dp, xs, K, V, aligned, kp, wf, out_tokens, out_acc, out_status);
+    if (!greedy)
+      hipLaunchKernelGGL((verify_draw_kernel<0>), dim3(rows), dim3(kBlock), 0, s, tp, dp, K, V,
+                         aligned, kp, wf, out_tokens);
     return hipGetLastError();
   }
   const int nc = pick_nc(need, kVerifyNcs, 5);

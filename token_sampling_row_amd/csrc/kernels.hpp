@@ -104,7 +104,11 @@ struct VerifyWs {
   int kmax1;      // max_k + 1: stride of the per-position arrays
   RowRec* rec;    // null: the wide path is not available
   int recs;       // 2 * kmax1
+  unsigned long long* part;   // per sequence 2 * kMaxSlices residual sums (double bits)
+  int nseq;       // sequences of the call (set per launch)
 };
+
+constexpr int kMaxSlices = 16;   // residual slices per row on the wide verify path
 
 int max_vocab_sample(int dtype);
 int max_vocab_verify(int dtype);          // with the row records (wide rows)

@@ -731,12 +731,22 @@ __global__ __launch_bounds__(kBlock) void beam_kernel(const unsigned char* logit
 
 // Residual weights max(0, p~ - q~) of one verify position (eq. 39.4), both
 // rows resident in this workgroup with the same element layout.
+// The residual's per-element weight max(0, p~ - q~), with p~ = w_p / Z_p over
+// {a >= tp} and q~ likewise: in float, like the weights themselves (their
+// exponentials are float; double steps after them add no accuracy).
+__device__ __forceinline__ float residual_weight(float a, float b, float tp, float Mp, float tq,
+                                                 float Mq, float c, float izp, float izq) {
+  const float pe = a >= tp ? weight(a, Mp, c) * izp : 0.0f;
+  const float qe = b >= tq ? weight(b, Mq, c) * izq : 0.0f;
+  return fmaxf(pe - qe, 0.0f);
+}
+
 template <int DT, int NC>
 struct ResidualWeights {
   const RegRow<DT, NC>& rp;
   const RegRow<DT, NC>& rq;
   float tp, Mp, tq, Mq, c;
-  double inv_zp, inv_zq;
+  float izp, izq;   // 1 / Z_p, 1 / Z_q
   __device__ __forceinline__ void operator()(int j, float* w) const {
     constexpr int EPC = Fmt<DT>::EPC;
     if (rp.cmax(j) >= tp) {
@@ -744,12 +754,7 @@ struct ResidualWeights {
       rp.elems(j, a);
       rq.elems(j, b);
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        const double pe = a[e] >= tp ? (double)weight(a[e], Mp, c) * inv_zp : 0.0;
-        const double qe = b[e] >= tq ? (double)weight(b[e], Mq, c) * inv_zq : 0.0;
-        const double d = pe - qe;
-        w[e] = d > 0.0 ? (float)d : 0.0f;
-      }
+      for (int e = 0; e < EPC; ++e) w[e] = residual_weight(a[e], b[e], tp, Mp, tq, Mq, c, izp, izq);
     } else {
 #pragma unroll
       for (int e = 0; e < EPC; ++e) w[e] = 0.0f;
@@ -822,17 +827,19 @@ struct RowCut {
 };
 
 // Status, row max and kept set of a resident row, with the exact kept weight.
+// need_zs false: a row that only draws from its own p~ (the walk forms the
+// sum), so Z_S is left out where it would take a pass of its own (zs -1).
 template <int DT, int NC>
 __device__ __forceinline__ RowCut verify_row_cut(RegRow<DT, NC>& r, const unsigned char* p,
                                                  int V, bool aligned, const KParams& kp,
-                                                 Lds& L) {
+                                                 Lds& L, bool need_zs = true) {
   const RowStats st = reg_stats(r, joint_top_p(kp), kp.c, L);
   RowCut rc{st.status, st.M, kPosInf, 0.0};
   if (st.status != 0) return rc;
   const Filters f = make_filters(kp, st.M);
   if (!f.k_on && !f.p_on && !f.m_on) {
     rc.tau = -kFltMax;
-    rc.zs = reg_kept_mass(r, rc.tau, st.M, kp.c, L);
+    rc.zs = need_zs ? reg_kept_mass(r, rc.tau, st.M, kp.c, L) : -1.0;
     return rc;
   }
   const FastOut fo = fast_cut(r, V, st.M, st.tmin, st.zlo, kp.c, f, 0.0, L);
@@ -843,7 +850,7 @@ __device__ __forceinline__ RowCut verify_row_cut(RegRow<DT, NC>& r, const unsign
   }
   const Cut cut = reg_general(r, st.M, kp.c, kp.cR, f, L);
   rc.tau = cut.tau;
-  rc.zs = reg_kept_mass(r, rc.tau, st.M, kp.c, L);
+  rc.zs = need_zs ? reg_kept_mass(r, rc.tau, st.M, kp.c, L) : -1.0;
   return rc;
 }
 
@@ -884,7 +891,8 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt
       acc = (j < K && x == tok) ? 1 : 0;
     }
   } else {
-    const RowCut cp = verify_row_cut(rp, tp, V, aligned != 0, kp, L);
+    // the bonus row (j = K) only draws from p~: no separate kept-mass pass
+    const RowCut cp = verify_row_cut(rp, tp, V, aligned != 0, kp, L, j < K);
     st_t = cp.status;
     const double u0 = draw_uniform(kp, (uint32_t)b, (uint32_t)j, 1u, 0);
     const double u1 = draw_uniform(kp, (uint32_t)b, (uint32_t)j, 1u, 1);
@@ -905,7 +913,8 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt
         if (!acc) {
           double zr;
           tok = walk_regs<NC, EPC>(ResidualWeights<DT, NC>{rp, rq, cp.tau, cp.M, cq.tau, cq.M,
-                                                           kp.c, 1.0 / cp.zs, 1.0 / cq.zs},
+                                                           kp.c, (float)(1.0 / cp.zs),
+                                                           (float)(1.0 / cq.zs)},
                                    u1, L, &zr);
           if (!(zr > 0.0)) {
             double zs;
@@ -1013,7 +1022,8 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(const unsigned char* tgt,
       kept = hit ? __ffsll((long long)hit) - 1 : -1;
     }
   } else {
-    const RowCut cp = verify_row_cut(rp, tp, V, true, kp, L);
+    // a node without children only draws from p~: no separate kept-mass pass
+    const RowCut cp = verify_row_cut(rp, tp, V, true, kp, L, with_draft);
     st_t = cp.status;
     RowCut cq{0, 0.0f, kPosInf, 1.0};
     if (with_draft) {

@@ -452,7 +452,7 @@ __device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* tota
   const int tid = threadIdx.x, lane = __lane_id(), wid = tid / kWave;
   // per chunk row, each 16-lane row's total (a butterfly inside the row, no
   // cross-row step): 32 partial sums per chunk row, added in fixed order below
-#pragma nounroll
+#pragma unroll 2
   for (int j = 0; j < NC; ++j) {
     float w[EPC];
     cw(j, w);
@@ -590,6 +590,20 @@ __device__ __forceinline__ double reg_kept_mass(const RegRow<DT, NC>& r, float t
                                                 float c, Lds& L) {
   constexpr int EPC = Fmt<DT>::EPC;
   double s = 0.0;
+  if (tau == -kFltMax) {
+    // every finite element: no chunk to skip, so the chunk rows go in
+    // program order, a few at a time (independent exponentials)
+#pragma unroll 4
+    for (int j = 0; j < NC; ++j) {
+      float v[EPC];
+      r.elems(j, v);
+      float t = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) t += v[e] >= tau ? weight(v[e], M, c) : 0.0f;
+      s += (double)t;
+    }
+    return block_sum<kBlock>(s, L.bs);
+  }
   unsigned long long m = wave_chunk_mask<NC>([&](int j) { return r.cmax(j) >= tau; });
   while (m) {
     const int j = pop_low(m);

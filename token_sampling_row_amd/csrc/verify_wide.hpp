@@ -2,18 +2,26 @@
 // register rows per workgroup: 16 < chunks per thread <= 38 (up to 155,648
 // bf16 or 77,824 float32 logits per row).
 //
-// Two kernels. The row kernel takes one target or draft row per workgroup,
-// held in VGPRs, and records its status, maximum M, kept set {v >= tau} and
-// kept weight sum Z_S, the quantities every later step needs (for greedy
-// verify, the row's argmax); where the draw from the row's own p~ is already
-// known (spec_verify's bonus row, a tree node without children) it draws it.
-// A kept set the candidate bound cannot narrow is found on the streaming
-// path, as the sampler does.
-// The finish kernel takes one sequence per workgroup: the acceptance tests
-// (eq. 39.3) from the recorded quantities and the draft tokens' logits, the
-// first rejection, and there the residual draw max(0, p~ - q~) / Z_r (eq.
-// 39.4), streaming the target and draft rows of that position in batches of
-// chunk rows (tree verify: one streamed pass per rejected child for the next
+// The row kernel takes one target or draft row per workgroup, held in VGPRs,
+// and records its status, maximum M, kept set {v >= tau} and kept weight sum
+// Z_S, the quantities every later step needs (for greedy verify, the row's
+// argmax); where the draw from the row's own p~ is already known
+// (spec_verify's bonus row, a tree node without children) it draws it. A kept
+// set the candidate bound cannot narrow is found on the streaming path, as
+// the sampler does.
+//
+// spec_verify then takes two more launches. The finish kernel runs one
+// workgroup per (sequence, slice of kSliceRows chunk rows): each derives the
+// acceptance tests (eq. 39.3) and the first rejection n from the records, and
+// sums the residual max(0, p~ - q~) of position n over its slice. The draw
+// kernel (one workgroup per sequence with a rejection) adds the slices' sums
+// in order and draws from the residual (eq. 39.4) inside the slice where the
+// target falls. The launch boundaries order the steps: no workgroup waits on
+// another and no cross-workgroup fence is needed.
+//
+// tree_verify's finish takes one workgroup per sequence: it follows the kept
+// children from the root and, at a node whose candidates are rejected,
+// streams the node's two rows (one pass per rejected candidate for the next
 // residual's normaliser, then the draw).
 #pragma once
 
@@ -47,43 +55,48 @@ __device__ __forceinline__ double rec_pi(const RowRec& r, float v, float c, doub
 constexpr int kStreamBatch = 4;   // chunk rows of both rows in flight per thread
 
 // Batched stream of two rows (target p, draft q) of the same layout: calls
-// f(jrow, a[EPC], b[EPC]) for every chunk row of this thread, B chunk rows'
-// loads issued before the first is used.
+// f(jrow, a[EPC], b[EPC]) for every chunk row j0 <= jrow < j1 (< nct) of this
+// thread, B chunk rows' loads issued before the first is used.
 template <int DT, int B, class F>
-__device__ __forceinline__ void stream2(const StreamRow<DT>& sp, const StreamRow<DT>& sq, F&& f) {
+__device__ __forceinline__ void stream2(const StreamRow<DT>& sp, const StreamRow<DT>& sq, int j0,
+                                        int j1, F&& f) {
   constexpr int EPC = Fmt<DT>::EPC;
 #pragma unroll 1
-  for (int j0 = 0; j0 < sp.nct; j0 += B) {
+  for (int jb = j0; jb < j1; jb += B) {
     uint4 ta[B], tb[B];
 #pragma unroll
     for (int q = 0; q < B; ++q) {
-      const bool in = j0 + q < sp.nct;
-      ta[q] = in ? sp.chunk(j0 + q) : neg_inf_chunk<DT>();
-      tb[q] = in ? sq.chunk(j0 + q) : neg_inf_chunk<DT>();
+      const bool in = jb + q < j1;
+      ta[q] = in ? sp.chunk(jb + q) : neg_inf_chunk<DT>();
+      tb[q] = in ? sq.chunk(jb + q) : neg_inf_chunk<DT>();
     }
 #pragma unroll
     for (int q = 0; q < B; ++q) {
       float a[EPC], b[EPC];
       unpack<DT>(ta[q], a);
       unpack<DT>(tb[q], b);
-      f(j0 + q, a, b);
+      f(jb + q, a, b);
     }
   }
 }
 
 // Inverse-CDF draw in ascending token id over per-element weights of two
-// streamed rows, w(a, b) >= 0 (a float per element; a chunk's EPC weights
-// added in float, everything past that in double, in a fixed order): the
-// first element whose running total exceeds u * (total), else the last with
-// weight. Needs sp.nct <= kWalkBatch. Returns the element; *total_out the
-// total weight.
-template <int DT, class W>
+// streamed rows, w(a, b) >= 0, restricted to chunk rows [j0, j1) (a float per
+// element; a chunk's EPC weights added in float, everything past that in
+// double, in a fixed order). The target is u times the range's total
+// (ABS false) or u itself (ABS true); the draw is the first element whose
+// running total exceeds it, else the last element with weight. Needs
+// j1 - j0 <= kWalkBatch. Returns the element (-1: no weight in the range);
+// *total_out the range's total weight.
+template <int DT, bool ABS, class W>
 __device__ __forceinline__ int walk_stream2(const StreamRow<DT>& sp, const StreamRow<DT>& sq,
-                                            W&& wfn, double u, Lds& L, double* total_out) {
+                                            int j0, int j1, W&& wfn, double u, Lds& L,
+                                            double* total_out) {
   constexpr int EPC = Fmt<DT>::EPC;
   const int tid = threadIdx.x, lane = __lane_id(), wid = tid / kWave;
+  const int nj = j1 - j0;
   // per chunk row, each 16-lane row's total, in LDS (added in fixed order below)
-  stream2<DT, kStreamBatch>(sp, sq, [&](int j, const float* a, const float* b) {
+  stream2<DT, kStreamBatch>(sp, sq, j0, j1, [&](int j, const float* a, const float* b) {
     float sf = 0.0f;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) sf += wfn(a[e], b[e]);
@@ -94,17 +107,17 @@ __device__ __forceinline__ int walk_stream2(const StreamRow<DT>& sp, const Strea
       s += dpp_perm_t<kDppHalfMirror>(s);
       s += dpp_perm_t<kDppMirror>(s);
     }
-    if (j < sp.nct && (lane & 15) == 0) L.jrow[j][wid * 4 + (lane >> 4)] = s;
+    if ((lane & 15) == 0) L.jrow[j - j0][wid * 4 + (lane >> 4)] = s;
   });
   __syncthreads();
   if (tid < kWave) {
     double sj = 0.0;
-    if (lane < sp.nct)
+    if (lane < nj)
 #pragma unroll
       for (int q = 0; q < kWaves * 4; ++q) sj += L.jrow[lane][q];
     const double incl = wave_incl_scan(sj);
     const double tot = readlane_t(incl, 63);
-    const double target = u * tot;
+    const double target = ABS ? u : u * tot;
     const double excl = incl - sj;
     const unsigned long long hit = __ballot(sj > 0.0 && target < incl);
     const unsigned long long nz = __ballot(sj > 0.0);
@@ -118,7 +131,7 @@ __device__ __forceinline__ int walk_stream2(const StreamRow<DT>& sp, const Strea
     }
   }
   __syncthreads();
-  const int jstar = __builtin_amdgcn_readfirstlane(L.si[2]);
+  const int jstar = j0 + __builtin_amdgcn_readfirstlane(L.si[2]);
   const double r1 = L.sd[2];
   *total_out = L.sd[3];
   float a[EPC], b[EPC], wj[EPC];
@@ -167,7 +180,7 @@ __device__ __forceinline__ double sum_stream2(const StreamRow<DT>& sp, const Str
                                               W&& wfn, Lds& L) {
   constexpr int EPC = Fmt<DT>::EPC;
   double acc = 0.0;
-  stream2<DT, kStreamBatch>(sp, sq, [&](int, const float* a, const float* b) {
+  stream2<DT, kStreamBatch>(sp, sq, 0, sp.nct, [&](int, const float* a, const float* b) {
     float sf = 0.0f;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) sf += wfn(a[e], b[e]);
@@ -271,6 +284,19 @@ __global__ __launch_bounds__(kBlock) void verify_rows_kernel(const unsigned char
 
 // ---------------------------------------------------------------- finish: spec
 
+// Chunk rows per slice of the residual (one batch of loads).
+constexpr int kSliceRows = kStreamBatch;
+static_assert((38 + kSliceRows - 1) / kSliceRows <= kMaxSlices, "residual slices per row");
+// Per sequence, slot of ws.part that holds the rejecting position (or -1).
+constexpr int kPartPos = 2 * kMaxSlices - 1;
+
+// One workgroup per (sequence b, slice s of the rows): every workgroup
+// derives the sequence's outcome from the records (the acceptance tests of
+// eq. 39.3 at each position, the first rejection n) and slice 0 writes the
+// outputs. With a rejection at temperature > 0, slice s also sums the
+// residual max(0, p~ - q~) of position n (and p~ itself, for a residual
+// without mass) over its chunk rows into ws.part; the draw at n is left to
+// verify_draw_kernel (the next launch, which sees every slice's sums).
 template <int DT>
 __global__ __launch_bounds__(kBlock) void verify_finish_kernel(
     const unsigned char* tgt, const unsigned char* dft, const int32_t* xs, int K, int V,
@@ -278,7 +304,9 @@ __global__ __launch_bounds__(kBlock) void verify_finish_kernel(
     int32_t* out_status) {
   Lds& L = tsr_lds;
   TSR_TRACE_INIT(nullptr);
-  const int b = blockIdx.x, tid = threadIdx.x, lane = __lane_id();
+  const int S = (int)gridDim.x / ws.nseq;
+  const int b = (int)blockIdx.x / S, sl = (int)blockIdx.x - b * S;
+  const int tid = threadIdx.x, lane = __lane_id();
   const bool greedy = (kp.flags & F_GREEDY) != 0;
   const long long rowbytes = (long long)V * Fmt<DT>::ESZ;
   const RowRec* rt = ws.rec + (long long)b * ws.recs;
@@ -309,16 +337,13 @@ __global__ __launch_bounds__(kBlock) void verify_finish_kernel(
     }
     const unsigned long long rej = __ballot(dq && !acc);
     const int n = status ? 0 : (rej ? __ffsll((long long)rej) - 1 : K);
+    // greedy, or every draft kept: the emitted token is already known
+    const int known = (greedy || n == K) ? readlane_u32((uint32_t)t.tok, n) : -1;
+    const RowRec tn = readlane_rec(t, n), dn = readlane_rec(d, n);
     if (lane == 0) {
       L.si[0] = status;
       L.si[1] = n;
-    }
-    // greedy, or every draft kept: the emitted token is already known
-    const int known = (greedy || n == K) ? readlane_u32((uint32_t)t.tok, n) : -1;
-    if (lane == 0) L.si[4] = known;
-    // the rejecting position's two rows, for the residual draw
-    const RowRec tn = readlane_rec(t, n), dn = readlane_rec(d, n);
-    if (lane == 0) {
+      L.si[4] = known;
       L.sf[0] = tn.M;
       L.sf[1] = tn.tau;
       L.sd[0] = tn.zs;
@@ -328,34 +353,109 @@ __global__ __launch_bounds__(kBlock) void verify_finish_kernel(
     }
   }
   __syncthreads();
-  const int status = L.si[0], n = L.si[1];
-  int tok = L.si[4];
-  if (!status && !greedy && n < K) {
-    const RowRec tn{L.sd[0], L.sf[0], L.sf[1], 0, -1}, dn{L.sd[1], L.sf[2], L.sf[3], 0, -1};
-    __syncthreads();
-    const StreamRow<DT> sp(tgt + ((long long)b * (K + 1) + n) * rowbytes, V, aligned != 0);
-    const StreamRow<DT> sq(dft + ((long long)b * K + n) * rowbytes, V, aligned != 0);
-    const float c = kp.c;
-    const double u1 = draw_uniform(kp, (uint32_t)b, (uint32_t)n, 1u, 1);
-    const double izp = 1.0 / tn.zs, izq = 1.0 / dn.zs;
-    double zr;
-    tok = walk_stream2<DT>(sp, sq, [&](float a, float q) -> float {
-      const double d = rec_pi(tn, a, c, izp) - rec_pi(dn, q, c, izq);
-      return d > 0.0 ? (float)d : 0.0f;
-    }, u1, L, &zr);
-    if (!(zr > 0.0))   // no residual mass (p~ = q~): draw from p~
-      tok = walk_stream2<DT>(sp, sq, [&](float a, float) -> float {
-        return a >= tn.tau ? weight(a, tn.M, c) : 0.0f;
-      }, u1, L, &zr);
+  const int status = L.si[0], n = L.si[1], tok = L.si[4];
+  const bool residual = !status && !greedy && n < K;
+  unsigned long long* part = ws.part + (long long)b * (2 * kMaxSlices);
+  if (sl == 0) {
+    // every output but the residual draw's token
+    if (tid <= K) {
+      const int x = tid < K ? xs[(long long)b * K + tid] : 0;
+      if (!(residual && tid == n))
+        out_tokens[(long long)b * (K + 1) + tid] =
+            status ? -1 : (tid < n ? x : (tid == n ? tok : -1));
+    }
+    if (tid == 0) {
+      out_acc[b] = status ? 0 : n;
+      if (out_status) out_status[b] = status;
+      part[kPartPos] = residual ? (unsigned long long)n : ~0ull;
+    }
   }
-  if (tid <= K) {
-    const int x = tid < K ? xs[(long long)b * K + tid] : 0;
-    out_tokens[(long long)b * (K + 1) + tid] = status ? -1 : (tid < n ? x : (tid == n ? tok : -1));
-  }
+  if (!residual) return;
+  const RowRec tn{L.sd[0], L.sf[0], L.sf[1], 0, -1}, dn{L.sd[1], L.sf[2], L.sf[3], 0, -1};
+  const StreamRow<DT> sp(tgt + ((long long)b * (K + 1) + n) * rowbytes, V, aligned != 0);
+  const StreamRow<DT> sq(dft + ((long long)b * K + n) * rowbytes, V, aligned != 0);
+  const float c = kp.c;
+  const float izp = (float)(1.0 / tn.zs), izq = (float)(1.0 / dn.zs);
+  // this slice's two sums: the residual's and p~'s (unnormalised) weight
+  const int j0 = sl * kSliceRows, j1 = min(j0 + kSliceRows, sp.nct);
+  double pr = 0.0, pp = 0.0;
+  stream2<DT, kSliceRows>(sp, sq, j0, j1, [&](int, const float* a, const float* q) {
+    float fr = 0.0f, fp = 0.0f;
+#pragma unroll
+    for (int e = 0; e < Fmt<DT>::EPC; ++e) {
+      fr += residual_weight(a[e], q[e], tn.tau, tn.M, dn.tau, dn.M, c, izp, izq);
+      fp += a[e] >= tn.tau ? weight(a[e], tn.M, c) : 0.0f;
+    }
+    pr += (double)fr;
+    pp += (double)fp;
+  });
+  pr = block_sum<kBlock>(pr, L.bs);
+  pp = block_sum<kBlock>(pp, L.bs);
   if (tid == 0) {
-    out_acc[b] = status ? 0 : n;
-    if (out_status) out_status[b] = status;
+    part[2 * sl] = (unsigned long long)__double_as_longlong(pr);
+    part[2 * sl + 1] = (unsigned long long)__double_as_longlong(pp);
   }
+}
+
+// One workgroup per sequence with a residual draw pending (ws.part holds its
+// position n and, per slice, the residual's and p~'s sums): the slice where
+// u * Z_r falls (u from w1 of position n; p~ itself when Z_r = 0), and the
+// draw inside it, the token emitted at n (eq. 39.4).
+template <int DT>
+__global__ __launch_bounds__(kBlock) void verify_draw_kernel(
+    const unsigned char* tgt, const unsigned char* dft, int K, int V, int aligned, KParams kp,
+    VerifyWs ws, int32_t* out_tokens) {
+  Lds& L = tsr_lds;
+  TSR_TRACE_INIT(nullptr);
+  const int b = blockIdx.x, tid = threadIdx.x, lane = __lane_id();
+  const unsigned long long* part = ws.part + (long long)b * (2 * kMaxSlices);
+  const unsigned long long pos = part[kPartPos];
+  if (pos == ~0ull) return;
+  const int n = (int)pos;
+  const long long rowbytes = (long long)V * Fmt<DT>::ESZ;
+  const RowRec tn = ws.rec[(long long)b * ws.recs + n];
+  const RowRec dn = ws.rec[(long long)b * ws.recs + ws.recs / 2 + n];
+  const StreamRow<DT> sp(tgt + ((long long)b * (K + 1) + n) * rowbytes, V, aligned != 0);
+  const StreamRow<DT> sq(dft + ((long long)b * K + n) * rowbytes, V, aligned != 0);
+  const int S = (sp.nct + kSliceRows - 1) / kSliceRows;
+  if (tid < kWave) {
+    const bool in = lane < S;
+    const double r = in ? __longlong_as_double((long long)part[2 * lane]) : 0.0;
+    const double q = in ? __longlong_as_double((long long)part[2 * lane + 1]) : 0.0;
+    const double ri = wave_incl_scan(r), qi = wave_incl_scan(q);
+    const double zr = readlane_t(ri, 63), zq = readlane_t(qi, 63);
+    // no residual mass (p~ = q~): the draw is from p~ itself
+    const bool use_r = zr > 0.0;
+    const double w = use_r ? r : q, wi = use_r ? ri : qi;
+    const double target = draw_uniform(kp, (uint32_t)b, (uint32_t)n, 1u, 1) * (use_r ? zr : zq);
+    const unsigned long long hit = __ballot(w > 0.0 && target < wi);
+    const unsigned long long nz = __ballot(w > 0.0);
+    const int last = nz ? 63 - __clzll((long long)nz) : 0;
+    const int ss = hit ? __ffsll((long long)hit) - 1 : last;
+    const double r1 = hit ? target - readlane_t(wi - w, ss) : kPosInf;
+    if (lane == 0) {
+      L.si[6] = ss;
+      L.si[7] = use_r;
+      L.sd[4] = r1;
+    }
+  }
+  __syncthreads();
+  const int ss = L.si[6];
+  const int k0 = ss * kSliceRows, k1 = min(k0 + kSliceRows, sp.nct);
+  const double r1 = L.sd[4];
+  const float c = kp.c;
+  const float izp = (float)(1.0 / tn.zs), izq = (float)(1.0 / dn.zs);
+  double zt;
+  int tok;
+  if (L.si[7])
+    tok = walk_stream2<DT, true>(sp, sq, k0, k1, [&](float a, float q) -> float {
+      return residual_weight(a, q, tn.tau, tn.M, dn.tau, dn.M, c, izp, izq);
+    }, r1, L, &zt);
+  else
+    tok = walk_stream2<DT, true>(sp, sq, k0, k1, [&](float a, float) -> float {
+      return a >= tn.tau ? weight(a, tn.M, c) : 0.0f;
+    }, r1, L, &zt);
+  if (tid == 0) out_tokens[(long long)b * (K + 1) + n] = tok;
 }
 
 // ---------------------------------------------------------------- finish: tree
@@ -447,7 +547,7 @@ __global__ __launch_bounds__(kBlock) void tree_finish_kernel(
         if (kept < 0) {
           const double u1 = draw_uniform(kp, (uint32_t)b, (uint32_t)(v * 32), 2u, 1);
           double zt;
-          tok = walk_stream2<DT>(sp, sq, [&](float av, float qv) -> float {
+          tok = walk_stream2<DT, false>(sp, sq, 0, sp.nct, [&](float av, float qv) -> float {
             return (float)pk(rec_pi(t, av, c, izp), rec_pi(d, qv, c, izq));
           }, u1, L, &zt);
         }
