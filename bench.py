@@ -208,6 +208,8 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--only", default=None,
+                    help="of the other workloads, run those whose name holds this text")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true",
                     help="skip the oracle comparison of every workload (CPU leg)")
@@ -255,7 +257,8 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        extra = run_extra(torch, tsr, wl, max(50, args.steps // 4), max(5, args.warmup // 4))
+        extra = run_extra(torch, tsr, wl, max(50, args.steps // 4), max(5, args.warmup // 4),
+                          args.only)
 
     if args.copy_calibration:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda:0")
@@ -367,149 +370,163 @@ def parity_leg(torch, tsr, wl):
             "workloads": out}
 
 
-def run_extra(torch, tsr, wl, steps, warmup):
-    """Rows/s and GB/s of the other workloads (same timing method)."""
+def run_extra(torch, tsr, wl, steps, warmup, only=None):
+    """Rows/s and GB/s of the other workloads (same timing method); `only`: a
+    substring of the workload names to run (all when None)."""
     import numpy as np
     res = {}
+
+    def want(name):
+        return only is None or only in name
+
+    dev = torch.device("cuda:0")
     with tsr.Sampler(0, max_rows=4096, max_vocab=1 << 18, max_k=8, seed=wl.philox_seed(2)) as s:
-        w = wl.config(1)
-        bufs = device_batch(torch, w, ROTATE)
-        out = torch.empty(w.rows, dtype=torch.int32, device="cuda:0")
-        ms = time_calls(torch, lambda i: s.sample_rows(bufs[i % ROTATE], w.runs[0], i, out=out),
-                        steps, warmup)
-        res["tiny64_8192_f32_chain"] = _rates(w.rows, w.rows * w.vocab * 4, ms)
-
-        w = wl.config(2)
-        bufs = device_batch(torch, w, ROTATE)
-        out = torch.empty(w.rows, dtype=torch.int32, device="cuda:0")
-        ms = time_calls(torch, lambda i: s.greedy_argmax(bufs[i % ROTATE], out=out), steps, warmup)
-        res["batch256_32000_f32_greedy"] = _rates(w.rows, w.rows * w.vocab * 4, ms)
-        for name, prm in (("pure_T1", w.runs[1]), ("minp_T0.7", w.runs[2])):
-            ms = time_calls(torch, lambda i: s.sample_rows(bufs[i % ROTATE], prm, i, out=out),
+        if want("tiny64_8192_f32"):
+            w = wl.config(1)
+            bufs = device_batch(torch, w, ROTATE)
+            out = torch.empty(w.rows, dtype=torch.int32, device="cuda:0")
+            ms = time_calls(torch, lambda i: s.sample_rows(bufs[i % ROTATE], w.runs[0], i, out=out),
                             steps, warmup)
-            res[f"batch256_32000_f32_{name}"] = _rates(w.rows, w.rows * w.vocab * 4, ms)
-        del bufs
+            res["tiny64_8192_f32_chain"] = _rates(w.rows, w.rows * w.vocab * 4, ms)
 
-        w = wl.config(4)
-        K = w.extra["K"]
-        dev = torch.device("cuda:0")
-        tg = torch.from_numpy(w.data).to(dev)
-        df = torch.from_numpy(w.extra["draft"]).to(dev)
-        tgs = [tg.clone() for _ in range(ROTATE)]
-        dfs = [df.clone() for _ in range(ROTATE)]
-        # draft tokens drawn from q by the sampler itself, as a draft model would
-        xs = s.sample_rows(df.view(w.rows * K, w.vocab), {"temperature": 1.0}, 777)
-        xs = xs.view(w.rows, K).contiguous()
-        toks = torch.empty(w.rows, K + 1, dtype=torch.int32, device=dev)
-        acc = torch.empty(w.rows, dtype=torch.int32, device=dev)
-        nbytes = w.rows * (2 * K + 1) * w.vocab * 4
-        for name, prm in (("T1", w.runs[0]), ("greedy", w.runs[1])):
-            ms = time_calls(torch, lambda i: s.spec_verify(tgs[i % ROTATE], dfs[i % ROTATE], xs, prm,
-                                                           i, out_tokens=toks, out_accepted=acc),
+        if want("batch256_32000_f32"):
+            w = wl.config(2)
+            bufs = device_batch(torch, w, ROTATE)
+            out = torch.empty(w.rows, dtype=torch.int32, device="cuda:0")
+            ms = time_calls(torch, lambda i: s.greedy_argmax(bufs[i % ROTATE], out=out), steps, warmup)
+            res["batch256_32000_f32_greedy"] = _rates(w.rows, w.rows * w.vocab * 4, ms)
+            for name, prm in (("pure_T1", w.runs[1]), ("minp_T0.7", w.runs[2])):
+                ms = time_calls(torch, lambda i: s.sample_rows(bufs[i % ROTATE], prm, i, out=out),
+                                steps, warmup)
+                res[f"batch256_32000_f32_{name}"] = _rates(w.rows, w.rows * w.vocab * 4, ms)
+            del bufs
+
+        if want("verify64_k4_32000_f32"):
+            w = wl.config(4)
+            K = w.extra["K"]
+            dev = torch.device("cuda:0")
+            tg = torch.from_numpy(w.data).to(dev)
+            df = torch.from_numpy(w.extra["draft"]).to(dev)
+            tgs = [tg.clone() for _ in range(ROTATE)]
+            dfs = [df.clone() for _ in range(ROTATE)]
+            # draft tokens drawn from q by the sampler itself, as a draft model would
+            xs = s.sample_rows(df.view(w.rows * K, w.vocab), {"temperature": 1.0}, 777)
+            xs = xs.view(w.rows, K).contiguous()
+            toks = torch.empty(w.rows, K + 1, dtype=torch.int32, device=dev)
+            acc = torch.empty(w.rows, dtype=torch.int32, device=dev)
+            nbytes = w.rows * (2 * K + 1) * w.vocab * 4
+            for name, prm in (("T1", w.runs[0]), ("greedy", w.runs[1])):
+                ms = time_calls(torch, lambda i: s.spec_verify(tgs[i % ROTATE], dfs[i % ROTATE], xs, prm,
+                                                               i, out_tokens=toks, out_accepted=acc),
+                                steps, warmup)
+                a = acc.float().mean().item()
+                r = _rates(w.rows, nbytes if prm["temperature"] else w.rows * (K + 1) * w.vocab * 4, ms)
+                r.update(acceptance_rate=a / K, tokens_per_verify=a + 1,
+                         tokens_per_s=w.rows * (a + 1) / (ms * 1e-3))
+                res[f"verify64_k4_32000_f32_{name}"] = r
+            del tgs, dfs
+
+        if want("verify64_k4_128256_bf16"):
+            # the verify step at a 128,256-id bf16 vocabulary (wider than a
+            # workgroup holds two rows of: one workgroup per row, then one per
+            # sequence), 64 sequences, K = 4, generated as the 32000 fp32 batch is
+            nseq, K, V = 64, 4, 128256
+            tgt_b, dft_b = wl.verify_batch(1040, nseq, K, V, "bf16")
+            tg = torch.from_numpy(tgt_b.view(np.int16)).to(dev).view(torch.bfloat16)
+            df = torch.from_numpy(dft_b.view(np.int16)).to(dev).view(torch.bfloat16)
+            tgs = [tg.clone() for _ in range(ROTATE)]
+            dfs = [df.clone() for _ in range(ROTATE)]
+            xs = s.sample_rows(df.view(nseq * K, V), {"temperature": 1.0}, 778)
+            xs = xs.view(nseq, K).contiguous()
+            toks = torch.empty(nseq, K + 1, dtype=torch.int32, device=dev)
+            acc = torch.empty(nseq, dtype=torch.int32, device=dev)
+            for name, prm in (("T1", {"temperature": 1.0}), ("greedy", {"temperature": 0.0})):
+                ms = time_calls(torch, lambda i: s.spec_verify(tgs[i % ROTATE], dfs[i % ROTATE], xs, prm,
+                                                               i, out_tokens=toks, out_accepted=acc),
+                                steps, warmup)
+                a = acc.float().mean().item()
+                rows_read = (2 * K + 1) if prm["temperature"] else (K + 1)
+                r = _rates(nseq, nseq * rows_read * V * 2, ms)
+                r.update(acceptance_rate=a / K, tokens_per_verify=a + 1,
+                         tokens_per_s=nseq * (a + 1) / (ms * 1e-3))
+                res[f"verify64_k4_128256_bf16_{name}"] = r
+            del tgs, dfs, tg, df
+
+        if want("batch256_128256_bf16_chain"):
+            # constrained decoding on the headline batch: allowed-token bitmask
+            # (V/8 bytes per row more) and log p~ of each draw
+            w = wl.config(3)
+            bufs = device_batch(torch, w, ROTATE)
+            out = torch.empty(w.rows, dtype=torch.int32, device="cuda:0")
+            lp = torch.empty(w.rows, dtype=torch.float32, device="cuda:0")
+            ms = time_calls(torch, lambda i: s.sample_rows_masked(bufs[i % ROTATE], None, w.runs[0], i,
+                                                                  out=out, logprob=lp),
                             steps, warmup)
-            a = acc.float().mean().item()
-            r = _rates(w.rows, nbytes if prm["temperature"] else w.rows * (K + 1) * w.vocab * 4, ms)
-            r.update(acceptance_rate=a / K, tokens_per_verify=a + 1,
-                     tokens_per_s=w.rows * (a + 1) / (ms * 1e-3))
-            res[f"verify64_k4_32000_f32_{name}"] = r
-        del tgs, dfs
-
-        # the verify step at a 128,256-id bf16 vocabulary (wider than a
-        # workgroup holds two rows of: one workgroup per row, then one per
-        # sequence), 64 sequences, K = 4, generated as the 32000 fp32 batch is
-        nseq, K, V = 64, 4, 128256
-        tgt_b, dft_b = wl.verify_batch(1040, nseq, K, V, "bf16")
-        tg = torch.from_numpy(tgt_b.view(np.int16)).to(dev).view(torch.bfloat16)
-        df = torch.from_numpy(dft_b.view(np.int16)).to(dev).view(torch.bfloat16)
-        tgs = [tg.clone() for _ in range(ROTATE)]
-        dfs = [df.clone() for _ in range(ROTATE)]
-        xs = s.sample_rows(df.view(nseq * K, V), {"temperature": 1.0}, 778)
-        xs = xs.view(nseq, K).contiguous()
-        toks = torch.empty(nseq, K + 1, dtype=torch.int32, device=dev)
-        acc = torch.empty(nseq, dtype=torch.int32, device=dev)
-        for name, prm in (("T1", {"temperature": 1.0}), ("greedy", {"temperature": 0.0})):
-            ms = time_calls(torch, lambda i: s.spec_verify(tgs[i % ROTATE], dfs[i % ROTATE], xs, prm,
-                                                           i, out_tokens=toks, out_accepted=acc),
+            res["batch256_128256_bf16_chain_logprob"] = _rates(w.rows, w.rows * w.vocab * 2, ms)
+            for kind in ("p=0.5", "few=40"):
+                words = torch.from_numpy(wl.allowed_words(31, w.rows, w.vocab, kind).view("int32"))
+                words = words.to("cuda:0")
+                nbytes = w.rows * w.vocab * 2 + words.numel() * 4
+                ms = time_calls(torch, lambda i: s.sample_rows_masked(bufs[i % ROTATE], words,
+                                                                      w.runs[0], i, out=out,
+                                                                      logprob=lp),
+                                steps, warmup)
+                res[f"batch256_128256_bf16_chain_mask_{kind}"] = _rates(w.rows, nbytes, ms)
+            # repetition penalty r = 1.1 over a 64-token window per row
+            hist = torch.from_numpy(np.random.default_rng(64).integers(0, w.vocab, (w.rows, 64))
+                                    .astype(np.int32)).to("cuda:0")
+            ms = time_calls(torch, lambda i: s.sample_rows_ex(bufs[i % ROTATE], w.runs[0], i,
+                                                              history=hist, penalty=1.1, out=out,
+                                                              logprob=lp),
                             steps, warmup)
-            a = acc.float().mean().item()
-            rows_read = (2 * K + 1) if prm["temperature"] else (K + 1)
-            r = _rates(nseq, nseq * rows_read * V * 2, ms)
-            r.update(acceptance_rate=a / K, tokens_per_verify=a + 1,
-                     tokens_per_s=nseq * (a + 1) / (ms * 1e-3))
-            res[f"verify64_k4_128256_bf16_{name}"] = r
-        del tgs, dfs, tg, df
-
-        # constrained decoding on the headline batch: allowed-token bitmask
-        # (V/8 bytes per row more) and log p~ of each draw
-        w = wl.config(3)
-        bufs = device_batch(torch, w, ROTATE)
-        out = torch.empty(w.rows, dtype=torch.int32, device="cuda:0")
-        lp = torch.empty(w.rows, dtype=torch.float32, device="cuda:0")
-        ms = time_calls(torch, lambda i: s.sample_rows_masked(bufs[i % ROTATE], None, w.runs[0], i,
-                                                              out=out, logprob=lp),
-                        steps, warmup)
-        res["batch256_128256_bf16_chain_logprob"] = _rates(w.rows, w.rows * w.vocab * 2, ms)
-        for kind in ("p=0.5", "few=40"):
-            words = torch.from_numpy(wl.allowed_words(31, w.rows, w.vocab, kind).view("int32"))
-            words = words.to("cuda:0")
-            nbytes = w.rows * w.vocab * 2 + words.numel() * 4
-            ms = time_calls(torch, lambda i: s.sample_rows_masked(bufs[i % ROTATE], words,
-                                                                  w.runs[0], i, out=out,
-                                                                  logprob=lp),
+            res["batch256_128256_bf16_chain_rep64"] = _rates(
+                w.rows, w.rows * w.vocab * 2 + hist.numel() * 4, ms)
+            # the same rows one id shorter, contiguous: rows start 2 bytes apart
+            # from a 16-byte boundary (an odd vocabulary)
+            odd = [b[:, : w.vocab - 1].contiguous() for b in bufs]
+            ms = time_calls(torch, lambda i: s.sample_rows(odd[i % ROTATE], w.runs[0], i, out=out),
                             steps, warmup)
-            res[f"batch256_128256_bf16_chain_mask_{kind}"] = _rates(w.rows, nbytes, ms)
-        # repetition penalty r = 1.1 over a 64-token window per row
-        hist = torch.from_numpy(np.random.default_rng(64).integers(0, w.vocab, (w.rows, 64))
-                                .astype(np.int32)).to("cuda:0")
-        ms = time_calls(torch, lambda i: s.sample_rows_ex(bufs[i % ROTATE], w.runs[0], i,
-                                                          history=hist, penalty=1.1, out=out,
-                                                          logprob=lp),
-                        steps, warmup)
-        res["batch256_128256_bf16_chain_rep64"] = _rates(
-            w.rows, w.rows * w.vocab * 2 + hist.numel() * 4, ms)
-        # the same rows one id shorter, contiguous: rows start 2 bytes apart
-        # from a 16-byte boundary (an odd vocabulary)
-        odd = [b[:, : w.vocab - 1].contiguous() for b in bufs]
-        ms = time_calls(torch, lambda i: s.sample_rows(odd[i % ROTATE], w.runs[0], i, out=out),
-                        steps, warmup)
-        res["batch256_128255_bf16_chain_unaligned"] = _rates(w.rows, w.rows * (w.vocab - 1) * 2, ms)
-        del bufs, odd
+            res["batch256_128255_bf16_chain_unaligned"] = _rates(w.rows, w.rows * (w.vocab - 1) * 2, ms)
+            del bufs, odd
 
-        # beam-search step: 64 groups of 4 beams over the same 256 x 128256 bf16 logits
-        w = wl.config(3)
-        bufs = device_batch(torch, w, ROTATE)
-        bsc = torch.from_numpy(np.random.default_rng(4).normal(-5.0, 2.0, w.rows)).to("cuda:0")
-        ms = time_calls(torch, lambda i: s.beam_step(bufs[i % ROTATE], bsc, 4), steps, warmup)
-        res["beam64x4_128256_bf16"] = _rates(w.rows, w.rows * w.vocab * 2, ms)
-        del bufs
+        if want("beam64x4_128256_bf16"):
+            # beam-search step: 64 groups of 4 beams over the same 256 x 128256 bf16 logits
+            w = wl.config(3)
+            bufs = device_batch(torch, w, ROTATE)
+            bsc = torch.from_numpy(np.random.default_rng(4).normal(-5.0, 2.0, w.rows)).to("cuda:0")
+            ms = time_calls(torch, lambda i: s.beam_step(bufs[i % ROTATE], bsc, 4), steps, warmup)
+            res["beam64x4_128256_bf16"] = _rates(w.rows, w.rows * w.vocab * 2, ms)
+            del bufs
 
-        # tree verify: 64 sequences, 8-node trees (root with two children, each
-        # with two, one more level on node 3), 32000 fp32 logits per node
-        w = wl.config(4)
-        nseq, N, V = 64, 8, w.vocab
-        rng = np.random.default_rng(8)
-        tgt = torch.from_numpy(rng.normal(0, 1.5, (nseq, N, V)).astype(np.float32)).to(dev)
-        dft = (tgt + torch.from_numpy(rng.normal(0, 0.7, (nseq, N, V)).astype(np.float32)).to(dev))
-        parent = torch.tensor([[-1, 0, 0, 1, 1, 2, 2, 3]] * nseq, dtype=torch.int32, device=dev)
-        # each node's token drawn from the draft at its parent, as a draft model would
-        draws = s.sample_rows(dft.view(nseq * N, V), {"temperature": 1.0}, 555).view(nseq, N)
-        toks = torch.gather(draws, 1, parent.clamp(min=0).long()).to(torch.int32).contiguous()
-        tgts = [tgt.clone() for _ in range(ROTATE // 2)]
-        dfts = [dft.clone() for _ in range(ROTATE // 2)]
-        ms = time_calls(torch, lambda i: s.tree_verify(tgts[i % (ROTATE // 2)],
-                                                       dfts[i % (ROTATE // 2)], parent, toks,
-                                                       {"temperature": 1.0}, i),
-                        steps, warmup)
-        res["tree64_n8_32000_f32_T1"] = _rates(nseq, nseq * (N + 4) * V * 4, ms)
-        del tgts, dfts, tgt, dft
+        if want("tree64_n8_32000_f32"):
+            # tree verify: 64 sequences, 8-node trees (root with two children, each
+            # with two, one more level on node 3), 32000 fp32 logits per node
+            w = wl.config(4)
+            nseq, N, V = 64, 8, w.vocab
+            rng = np.random.default_rng(8)
+            tgt = torch.from_numpy(rng.normal(0, 1.5, (nseq, N, V)).astype(np.float32)).to(dev)
+            dft = (tgt + torch.from_numpy(rng.normal(0, 0.7, (nseq, N, V)).astype(np.float32)).to(dev))
+            parent = torch.tensor([[-1, 0, 0, 1, 1, 2, 2, 3]] * nseq, dtype=torch.int32, device=dev)
+            # each node's token drawn from the draft at its parent, as a draft model would
+            draws = s.sample_rows(dft.view(nseq * N, V), {"temperature": 1.0}, 555).view(nseq, N)
+            toks = torch.gather(draws, 1, parent.clamp(min=0).long()).to(torch.int32).contiguous()
+            tgts = [tgt.clone() for _ in range(ROTATE // 2)]
+            dfts = [dft.clone() for _ in range(ROTATE // 2)]
+            ms = time_calls(torch, lambda i: s.tree_verify(tgts[i % (ROTATE // 2)],
+                                                           dfts[i % (ROTATE // 2)], parent, toks,
+                                                           {"temperature": 1.0}, i),
+                            steps, warmup)
+            res["tree64_n8_32000_f32_T1"] = _rates(nseq, nseq * (N + 4) * V * 4, ms)
+            del tgts, dfts, tgt, dft
 
-        w = wl.config(5)
-        bufs = device_batch(torch, w, 2)          # 2 x 311 MB already exceeds the 256 MB cache
-        out = torch.empty(w.rows, dtype=torch.int32, device="cuda:0")
-        for name, prm in (("top_p0.9", w.runs[0]), ("top_k1024", w.runs[1])):
-            ms = time_calls(torch, lambda i: s.sample_rows(bufs[i % 2], prm, i, out=out),
-                            max(20, steps // 4), warmup)
-            res[f"batch1024_151936_bf16_{name}"] = _rates(w.rows, w.rows * w.vocab * 2, ms)
+        if want("batch1024_151936_bf16"):
+            w = wl.config(5)
+            bufs = device_batch(torch, w, 2)          # 2 x 311 MB already exceeds the 256 MB cache
+            out = torch.empty(w.rows, dtype=torch.int32, device="cuda:0")
+            for name, prm in (("top_p0.9", w.runs[0]), ("top_k1024", w.runs[1])):
+                ms = time_calls(torch, lambda i: s.sample_rows(bufs[i % 2], prm, i, out=out),
+                                max(20, steps // 4), warmup)
+                res[f"batch1024_151936_bf16_{name}"] = _rates(w.rows, w.rows * w.vocab * 2, ms)
     return res
 
 
