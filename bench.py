@@ -365,6 +365,29 @@ def parity_leg(torch, tsr, wl):
             a = acc.float().mean().item()
             out[f"{w.name}_run{run}"] = dict(t.as_dict(), params=prm, acceptance_rate=a / K,
                                              tokens_per_verify=a + 1)
+
+    # the same verify step at 128256 bf16 logits (the wide path), the batch
+    # of its bench line, at T 1 and T 0
+    nseq, K, V = 64, 4, 128256
+    tgt_b, dft_b = wl.verify_batch(1040, nseq, K, V, "bf16")
+    tv = oracle.values_from_stored(tgt_b.reshape(-1, V), "bf16").reshape(nseq, K + 1, V)
+    dv = oracle.values_from_stored(dft_b.reshape(-1, V), "bf16").reshape(nseq, K, V)
+    seed = wl.philox_seed(4)
+    xs = np.array([[oracle.sample_row(dv[b, j], {"temperature": 1.0}, seed, b * K + j, 1001).token
+                    for j in range(K)] for b in range(nseq)], dtype=np.int32)
+    with tsr.Sampler(0, max_rows=4096, max_vocab=1 << 18, max_k=8, seed=seed) as s:
+        tg = torch.from_numpy(tgt_b.view(np.int16)).to(dev).view(torch.bfloat16)
+        df = torch.from_numpy(dft_b.view(np.int16)).to(dev).view(torch.bfloat16)
+        xd = torch.from_numpy(xs).to(dev)
+        for run, prm in enumerate(({"temperature": 1.0}, {"temperature": 0.0})):
+            st = torch.full((nseq,), -7, dtype=torch.int32, device=dev)
+            toks, acc = s.spec_verify(tg, df, xd, prm, run, out_status=st)
+            torch.cuda.synchronize()
+            t = parity_verify_batch(tv, dv, xs, prm, seed, run, toks.cpu().numpy(),
+                                    acc.cpu().numpy(), st.cpu().numpy())
+            a = acc.float().mean().item()
+            out[f"verify64_k4_128256_bf16_run{run}"] = dict(
+                t.as_dict(), params=prm, acceptance_rate=a / K, tokens_per_verify=a + 1)
     total = sum(v["out_of_band"] for v in out.values())
     return {"out_of_band_total": total, "seconds": time.perf_counter() - t_start,
             "workloads": out}
