@@ -5,19 +5,20 @@
 // The row kernel takes one target or draft row per workgroup, held in VGPRs,
 // and records its status, maximum M, kept set {v >= tau} and kept weight sum
 // Z_S, the quantities every later step needs (for greedy verify, the row's
-// argmax); where the draw from the row's own p~ is already known
-// (spec_verify's bonus row, a tree node without children) it draws it. A kept
-// set the candidate bound cannot narrow is found on the streaming path, as
-// the sampler does.
+// argmax); a tree node without children, whose draw from its own p~ is
+// already known to be needed, draws it there. spec_verify's bonus rows come
+// last in the grid and record tau alone. A kept set the candidate bound
+// cannot narrow is found on the streaming path, as the sampler does.
 //
 // spec_verify then takes two more launches. The finish kernel runs one
 // workgroup per (sequence, slice of kSliceRows chunk rows): each derives the
 // acceptance tests (eq. 39.3) and the first rejection n from the records, and
-// sums the residual max(0, p~ - q~) of position n over its slice. The draw
-// kernel (one workgroup per sequence with a rejection) adds the slices' sums
-// in order and draws from the residual (eq. 39.4) inside the slice where the
-// target falls. The launch boundaries order the steps: no workgroup waits on
-// another and no cross-workgroup fence is needed.
+// sums the residual max(0, p~ - q~) of position n over its slice (every draft
+// kept: p~ of the bonus row). The draw kernel (one workgroup per sequence)
+// adds the slices' sums in order and draws from the residual (eq. 39.4), or
+// the bonus token from p~, inside the slice where the target falls. The
+// launch boundaries order the steps: no workgroup waits on another and no
+// cross-workgroup fence is needed.
 //
 // tree_verify's finish takes one workgroup per sequence: it follows the kept
 // children from the root and, at a node whose candidates are rejected,
@@ -227,7 +228,24 @@ __global__ __launch_bounds__(kBlock) void verify_rows_kernel(const unsigned char
   const int T = TREE ? K : K + 1;            // target rows per sequence (K = N for trees)
   const int D = greedy ? 0 : (TREE ? K : K); // draft rows
   const int R = T + D;
-  const int b = (int)blockIdx.x / R, s = (int)blockIdx.x - b * R;
+  int b, s;
+  if constexpr (TREE) {
+    b = (int)blockIdx.x / R;
+    s = (int)blockIdx.x - b * R;
+  } else {
+    // spec_verify: every sequence's K draft positions first, the bonus rows
+    // (target row K, the lightest: no kept mass, no draw) last
+    const int nseq = (int)gridDim.x / R;
+    const int blk = (int)blockIdx.x, nb = nseq * (R - 1);
+    if (blk < nb) {
+      b = blk / (R - 1);
+      const int q = blk - b * (R - 1);
+      s = q < K ? q : q + 1;    // targets 0..K-1, then the drafts
+    } else {
+      b = blk - nb;
+      s = K;
+    }
+  }
   const bool is_t = s < T;
   const int j = is_t ? s : s - T;
   const long long rowbytes = (long long)V * Fmt<DT>::ESZ;
@@ -251,13 +269,13 @@ __global__ __launch_bounds__(kBlock) void verify_rows_kernel(const unsigned char
     if (st.status == 0) rec.tok = reg_argmax(r, st.M, L);
   } else {
     if (st.status == 0) {
-      // spec_verify's bonus row draws with w0 of position K; a tree node
-      // without children draws from its p~ with w1 of (row, node * 32). The
-      // other rows need tau and Z_S only.
-      const bool draws = is_t && (TREE ? leaf : j == K);
-      const double u = !draws ? 0.0
-                       : TREE ? draw_uniform(kp, (uint32_t)b, (uint32_t)(j * 32), 2u, 1)
-                              : draw_uniform(kp, (uint32_t)b, (uint32_t)K, 1u, 0);
+      // a tree node without children draws from its p~ with w1 of (row,
+      // node * 32); the other rows need tau and Z_S only, and spec_verify's
+      // bonus row tau alone (its draw, when every draft is kept, is the
+      // draw kernel's)
+      const bool draws = TREE && is_t && leaf;
+      const bool need_zs = !(!TREE && j == K);
+      const double u = draws ? draw_uniform(kp, (uint32_t)b, (uint32_t)(j * 32), 2u, 1) : 0.0;
       const Filters f = make_filters(kp, st.M);
       const bool filt = f.k_on || f.p_on || f.m_on;
       rec.tau = -kFltMax;   // no filter: every finite logit
@@ -274,7 +292,7 @@ __global__ __launch_bounds__(kBlock) void verify_rows_kernel(const unsigned char
         if (draws) rec.tok = fo.token;
       } else if (draws) {
         rec.tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{r, rec.tau, st.M, kp.c}, u, L, &rec.zs);
-      } else {
+      } else if (need_zs) {
         rec.zs = reg_kept_mass(r, rec.tau, st.M, kp.c, L);
       }
     }
@@ -354,41 +372,54 @@ __global__ __launch_bounds__(kBlock) void verify_finish_kernel(
   }
   __syncthreads();
   const int status = L.si[0], n = L.si[1], tok = L.si[4];
-  const bool residual = !status && !greedy && n < K;
+  // a draw left to the draw kernel: the residual at the first rejection, or,
+  // every draft kept, the bonus draw from p~ of target row K
+  const bool pending = !status && !greedy;
+  const bool bonus = n == K;
   unsigned long long* part = ws.part + (long long)b * (2 * kMaxSlices);
   if (sl == 0) {
-    // every output but the residual draw's token
+    // every output but the pending draw's token
     if (tid <= K) {
       const int x = tid < K ? xs[(long long)b * K + tid] : 0;
-      if (!(residual && tid == n))
+      if (!(pending && tid == n))
         out_tokens[(long long)b * (K + 1) + tid] =
             status ? -1 : (tid < n ? x : (tid == n ? tok : -1));
     }
     if (tid == 0) {
       out_acc[b] = status ? 0 : n;
       if (out_status) out_status[b] = status;
-      part[kPartPos] = residual ? (unsigned long long)n : ~0ull;
+      part[kPartPos] = pending ? (unsigned long long)n : ~0ull;
     }
   }
-  if (!residual) return;
+  if (!pending) return;
   const RowRec tn{L.sd[0], L.sf[0], L.sf[1], 0, -1}, dn{L.sd[1], L.sf[2], L.sf[3], 0, -1};
   const StreamRow<DT> sp(tgt + ((long long)b * (K + 1) + n) * rowbytes, V, aligned != 0);
-  const StreamRow<DT> sq(dft + ((long long)b * K + n) * rowbytes, V, aligned != 0);
   const float c = kp.c;
-  const float izp = (float)(1.0 / tn.zs), izq = (float)(1.0 / dn.zs);
-  // this slice's two sums: the residual's and p~'s (unnormalised) weight
   const int j0 = sl * kSliceRows, j1 = min(j0 + kSliceRows, sp.nct);
   double pr = 0.0, pp = 0.0;
-  stream2<DT, kSliceRows>(sp, sq, j0, j1, [&](int, const float* a, const float* q) {
-    float fr = 0.0f, fp = 0.0f;
+  if (bonus) {
+    // p~'s weight of the bonus row only (there is no draft row K)
+    stream2<DT, kSliceRows>(sp, sp, j0, j1, [&](int, const float* a, const float*) {
+      float fp = 0.0f;
 #pragma unroll
-    for (int e = 0; e < Fmt<DT>::EPC; ++e) {
-      fr += residual_weight(a[e], q[e], tn.tau, tn.M, dn.tau, dn.M, c, izp, izq);
-      fp += a[e] >= tn.tau ? weight(a[e], tn.M, c) : 0.0f;
-    }
-    pr += (double)fr;
-    pp += (double)fp;
-  });
+      for (int e = 0; e < Fmt<DT>::EPC; ++e) fp += a[e] >= tn.tau ? weight(a[e], tn.M, c) : 0.0f;
+      pp += (double)fp;
+    });
+  } else {
+    // this slice's two sums: the residual's and p~'s (unnormalised) weight
+    const StreamRow<DT> sq(dft + ((long long)b * K + n) * rowbytes, V, aligned != 0);
+    const float izp = (float)(1.0 / tn.zs), izq = (float)(1.0 / dn.zs);
+    stream2<DT, kSliceRows>(sp, sq, j0, j1, [&](int, const float* a, const float* q) {
+      float fr = 0.0f, fp = 0.0f;
+#pragma unroll
+      for (int e = 0; e < Fmt<DT>::EPC; ++e) {
+        fr += residual_weight(a[e], q[e], tn.tau, tn.M, dn.tau, dn.M, c, izp, izq);
+        fp += a[e] >= tn.tau ? weight(a[e], tn.M, c) : 0.0f;
+      }
+      pr += (double)fr;
+      pp += (double)fp;
+    });
+  }
   pr = block_sum<kBlock>(pr, L.bs);
   pp = block_sum<kBlock>(pp, L.bs);
   if (tid == 0) {
@@ -397,10 +428,11 @@ __global__ __launch_bounds__(kBlock) void verify_finish_kernel(
   }
 }
 
-// One workgroup per sequence with a residual draw pending (ws.part holds its
-// position n and, per slice, the residual's and p~'s sums): the slice where
-// u * Z_r falls (u from w1 of position n; p~ itself when Z_r = 0), and the
-// draw inside it, the token emitted at n (eq. 39.4).
+// One workgroup per sequence with a draw pending (ws.part holds its position
+// n and, per slice, the residual's and p~'s sums): the slice where u * Z_r
+// falls (u from w1 of position n; p~ itself when Z_r = 0), and the draw inside
+// it, the token emitted at n (eq. 39.4); n = K (every draft kept): the bonus
+// draw from p~ of target row K with w0 of position K.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void verify_draw_kernel(
     const unsigned char* tgt, const unsigned char* dft, int K, int V, int aligned, KParams kp,
@@ -412,11 +444,14 @@ __global__ __launch_bounds__(kBlock) void verify_draw_kernel(
   const unsigned long long pos = part[kPartPos];
   if (pos == ~0ull) return;
   const int n = (int)pos;
+  const bool bonus = n == K;   // every draft kept: p~ of target row K, w0 of position K
   const long long rowbytes = (long long)V * Fmt<DT>::ESZ;
   const RowRec tn = ws.rec[(long long)b * ws.recs + n];
-  const RowRec dn = ws.rec[(long long)b * ws.recs + ws.recs / 2 + n];
+  const RowRec dn = bonus ? tn : ws.rec[(long long)b * ws.recs + ws.recs / 2 + n];
   const StreamRow<DT> sp(tgt + ((long long)b * (K + 1) + n) * rowbytes, V, aligned != 0);
-  const StreamRow<DT> sq(dft + ((long long)b * K + n) * rowbytes, V, aligned != 0);
+  const StreamRow<DT> sq = bonus ? sp
+                                 : StreamRow<DT>(dft + ((long long)b * K + n) * rowbytes, V,
+                                                 aligned != 0);
   const int S = (sp.nct + kSliceRows - 1) / kSliceRows;
   if (tid < kWave) {
     const bool in = lane < S;
@@ -427,7 +462,9 @@ __global__ __launch_bounds__(kBlock) void verify_draw_kernel(
     // no residual mass (p~ = q~): the draw is from p~ itself
     const bool use_r = zr > 0.0;
     const double w = use_r ? r : q, wi = use_r ? ri : qi;
-    const double target = draw_uniform(kp, (uint32_t)b, (uint32_t)n, 1u, 1) * (use_r ? zr : zq);
+    const double uu = bonus ? draw_uniform(kp, (uint32_t)b, (uint32_t)K, 1u, 0)
+                            : draw_uniform(kp, (uint32_t)b, (uint32_t)n, 1u, 1);
+    const double target = uu * (use_r ? zr : zq);
     const unsigned long long hit = __ballot(w > 0.0 && target < wi);
     const unsigned long long nz = __ballot(w > 0.0);
     const int last = nz ? 63 - __clzll((long long)nz) : 0;
