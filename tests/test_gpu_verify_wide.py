@@ -97,6 +97,23 @@ def test_verify_wide(dtype, V, B, K):
                 assert st[2] != 0                              # empty draft row
 
 
+@pytest.mark.parametrize("dtype,V,B,K", [("bf16", 128256, 1, 1), ("f32", 40000, 3, 1),
+                                         ("bf16", 70001, 2, 5)])
+def test_verify_wide_small_batches(dtype, V, B, K):
+    """One draft position, a single sequence, an odd vocabulary: the grid's
+    bonus rows last and the slice sums of one sequence."""
+    seed = 7400 + V % 991
+    tgt, dft = verify_case(B, K, V, dtype, seed, edges=False)
+    rng = np.random.default_rng(V + K)
+    tv = oracle.values_from_stored(tgt.reshape(-1, V), dtype).reshape(B, K + 1, V)
+    dv = oracle.values_from_stored(dft.reshape(-1, V), dtype).reshape(B, K, V)
+    with tsr.Sampler(0, max_rows=8, max_vocab=V, max_k=K, seed=seed) as s:
+        for step, prm in enumerate(PARAMS):
+            xs = draft_tokens(dv, tv, prm, seed, step, rng)
+            print_case("verify_wide_small", dtype=dtype, V=V, B=B, K=K, params=prm)
+            check_verify(s, tgt, dft, xs, prm, seed, step, dtype)
+
+
 def test_verify_wide_greedy_is_argmax_decoding():
     """Temperature 0 at 128,256 bf16 logits: the emitted prefix is the
     target's argmax at every position (a property at any size)."""
