@@ -61,6 +61,19 @@ def test_noalloc_verify_matches_spec_verify_twice():
                 assert (ga >= 0).all() and (ga <= K).all()
 
 
+def test_noalloc_verify_at_its_vocab_limit():
+    """The widest rows the static array serves (65,536 bf16 and 32,768 fp32
+    logits: the two-rows-per-workgroup kernel), against spec_verify."""
+    rng = np.random.default_rng(12)
+    with tsr.Sampler(0, max_rows=64, max_vocab=1 << 17, max_k=4, seed=SEED) as s:
+        for (B, K, V, dtype) in ((4, 2, 65536, "bf16"), (4, 3, 32768, "f32")):
+            t, d, x = case(rng, B, K, V, dtype)
+            for step, prm in enumerate([{"temperature": 1.0}, {"temperature": 0.0}]):
+                print(f"[case] noalloc limit B={B} K={K} V={V} {dtype} {prm}", flush=True)
+                rt, ra, rs, gt, ga, gs = both(s, t, d, x, prm, step)
+                assert np.array_equal(rt, gt) and np.array_equal(ra, ga) and np.array_equal(rs, gs)
+
+
 def test_noalloc_verify_rejects_sizes_beyond_its_array():
     lib = tsr.load_library()
     p = tsr._Params(1.0, 0, 1.0, 0.0, 0)
