@@ -445,9 +445,136 @@ __device__ __forceinline__ int reg_argmax(const RegRow<DT, NC>& r, float M, Lds&
 // element whose running total exceeds u * (total weight). cw(j, w) fills the
 // EPC weights of chunk row j (j is wavefront-uniform).
 // Returns the element index; *total_out gets the total weight.
+// The walk for rows of at most kWalkLds chunk rows per thread: every
+// thread's chunk sum goes to LDS (no lane exchange per chunk row); each chunk
+// row's total is then added over its 512 threads (eight per lane in order,
+// then a wavefront sum), wavefront 0 finds the chunk row and, from the same
+// LDS sums, the thread where the target falls, and that thread alone walks
+// its chunk. Same result as walk_regs up to the order of the additions.
+template <int NC, int EPC, class CW>
+__device__ __forceinline__ int walk_regs_lds(CW&& cw, double u, Lds& L, double* total_out,
+                                             double* wtok) {
+  static_assert(NC <= kWalkLds, "walk LDS rows");
+  const int tid = threadIdx.x, lane = __lane_id(), wid = tid / kWave;
+#pragma unroll 2
+  for (int j = 0; j < NC; ++j) {
+    float w[EPC];
+    cw(j, w);
+    float sf = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) sf += w[e];
+    L.wsum[j][tid] = sf;
+  }
+  __syncthreads();
+  // chunk row totals: wavefront w adds rows w, w + 8, ... (8 sums per lane)
+  for (int j = wid; j < NC; j += kWaves) {
+    double s = 0.0;
+#pragma unroll
+    for (int q = 0; q < kBlock / kWave; ++q) s += (double)L.wsum[j][lane * (kBlock / kWave) + q];
+    s = wave_sum(s);
+    if (lane == 0) L.jsum[j] = s;
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    const double sj = lane < NC ? L.jsum[lane] : 0.0;
+    const double incl = wave_incl_scan(sj);
+    const double tot = readlane_t(incl, 63);
+    const double target = u * tot;
+    const unsigned long long hit = __ballot(sj > 0.0 && target < incl);
+    const unsigned long long nz = __ballot(sj > 0.0);
+    const int last = nz ? 63 - __clzll((long long)nz) : 0;
+    const int jstar = hit ? __ffsll((long long)hit) - 1 : last;
+    const double r1 = hit ? target - readlane_t(incl - sj, jstar) : kPosInf;
+    // the thread of row jstar where r1 falls (lane l holds threads 8l..8l+7)
+    double ts[kBlock / kWave];
+    double ls = 0.0;
+#pragma unroll
+    for (int q = 0; q < kBlock / kWave; ++q) {
+      ts[q] = (double)L.wsum[jstar][lane * (kBlock / kWave) + q];
+      ls += ts[q];
+    }
+    const double li = wave_incl_scan(ls);
+    const double lx = li - ls;
+    const bool mine = ls > 0.0 && lx <= r1 && r1 < li;
+    const unsigned long long hl = __ballot(mine);
+    int owner = -1;
+    double r2 = 0.0;
+    if (hl) {
+      const int l0 = __ffsll((long long)hl) - 1;
+      if (lane == l0) {
+        double run = lx;
+        for (int q = 0; q < kBlock / kWave; ++q) {
+          if (ts[q] > 0.0 && r1 < run + ts[q]) {
+            owner = lane * (kBlock / kWave) + q;
+            r2 = r1 - run;
+            break;
+          }
+          run += ts[q];
+        }
+        if (owner < 0) {   // rounding inside the lane: its last thread with weight
+          for (int q = kBlock / kWave - 1; q >= 0; --q)
+            if (ts[q] > 0.0) {
+              owner = lane * (kBlock / kWave) + q;
+              break;
+            }
+          r2 = kPosInf;
+        }
+      }
+      owner = (int)readlane_u32((uint32_t)owner, l0);
+      r2 = readlane_t(r2, l0);
+    } else {
+      // the target past the row's end (rounding): its last thread with weight
+      const unsigned long long nzl = __ballot(ls > 0.0);
+      const int l1 = nzl ? 63 - __clzll((long long)nzl) : 0;
+      int o = -1;
+      for (int q = kBlock / kWave - 1; q >= 0; --q)
+        if (o < 0 && ts[q] > 0.0) o = lane * (kBlock / kWave) + q;
+      owner = (int)readlane_u32((uint32_t)o, l1);
+      r2 = kPosInf;
+    }
+    if (lane == 0) {
+      L.si[2] = jstar;
+      L.si[3] = owner;
+      L.sd[2] = r2;
+      L.sd[3] = tot;
+    }
+  }
+  __syncthreads();
+  const int jstar = __builtin_amdgcn_readfirstlane(L.si[2]);
+  const int owner = __builtin_amdgcn_readfirstlane(L.si[3]);
+  *total_out = L.sd[3];
+  if (tid == owner) {
+    const double r2 = L.sd[2];
+    float wj[EPC];
+    cw(jstar, wj);
+    double run = 0.0;
+    int pick = -1, lastpos = -1;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      if (wj[e] > 0.0f) {
+        run += (double)wj[e];
+        lastpos = e;
+        if (pick < 0 && r2 < run) pick = e;
+      }
+    }
+    if (pick < 0) pick = lastpos;
+    L.si[4] = (jstar * kBlock + tid) * EPC + pick;
+    double wp = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) wp = e == pick ? (double)wj[e] : wp;
+    L.sd[4] = wp;
+  }
+  __syncthreads();
+  const int tok = owner >= 0 ? L.si[4] : -1;
+  if (wtok) *wtok = L.sd[4];
+  __syncthreads();
+  return tok;
+}
+
 template <int NC, int EPC, class CW>
 __device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* total_out,
                                          double* wtok = nullptr) {
+  if constexpr (NC <= kWalkLds) return walk_regs_lds<NC, EPC>(cw, u, L, total_out, wtok);
   static_assert(NC <= kWalkBatch, "walk scratch too small");
   const int tid = threadIdx.x, lane = __lane_id(), wid = tid / kWave;
   // per chunk row, each 16-lane row's total (a butterfly inside the row, no
