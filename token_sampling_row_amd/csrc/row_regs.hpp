@@ -441,21 +441,35 @@ __device__ __forceinline__ int reg_argmax(const RegRow<DT, NC>& r, float M, Lds&
 }
 
 // ---------------------------------------------------------------- the walk
+// The per-(chunk row, thread) weight sums of the walk: inside the LDS union
+// up to kWalkLds chunk rows per thread, in an array of their own (one
+// workgroup per CU holds it) for the wider rows.
+template <int NC>
+__device__ __forceinline__ float (*walk_sums(Lds& L))[kBlock] {
+  if constexpr (NC <= kWalkLds) {
+    return L.wsum;
+  } else {
+    __shared__ float wide[NC][kBlock];
+    return wide;
+  }
+}
+
 // Inverse-CDF draw in ascending token id over per-element weights: the first
 // element whose running total exceeds u * (total weight). cw(j, w) fills the
-// EPC weights of chunk row j (j is wavefront-uniform).
-// Returns the element index; *total_out gets the total weight.
-// The walk for rows of at most kWalkLds chunk rows per thread: every
-// thread's chunk sum goes to LDS (no lane exchange per chunk row); each chunk
-// row's total is then added over its 512 threads (eight per lane in order,
-// then a wavefront sum), wavefront 0 finds the chunk row and, from the same
-// LDS sums, the thread where the target falls, and that thread alone walks
-// its chunk. Same result as walk_regs up to the order of the additions.
+// EPC weights of chunk row j (j is wavefront-uniform). Returns the element
+// index (-1: no weight); *total_out gets the total weight, *wtok (if given)
+// the drawn element's weight.
+// Every thread's chunk sum goes to LDS (no lane exchange per chunk row); each
+// chunk row's total is then added over its 512 threads (eight per lane in
+// order, then a wavefront sum), wavefront 0 finds the chunk row and, from the
+// same LDS sums, the thread where the target falls, and that thread alone
+// walks its chunk.
 template <int NC, int EPC, class CW>
-__device__ __forceinline__ int walk_regs_lds(CW&& cw, double u, Lds& L, double* total_out,
-                                             double* wtok) {
-  static_assert(NC <= kWalkLds, "walk LDS rows");
+__device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* total_out,
+                                         double* wtok = nullptr) {
+  static_assert(NC <= kWave, "one lane per chunk row in the search");
   const int tid = threadIdx.x, lane = __lane_id(), wid = tid / kWave;
+  float (*wsum)[kBlock] = walk_sums<NC>(L);
 #pragma unroll 2
   for (int j = 0; j < NC; ++j) {
     float w[EPC];
@@ -463,14 +477,14 @@ __device__ __forceinline__ int walk_regs_lds(CW&& cw, double u, Lds& L, double* 
     float sf = 0.0f;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) sf += w[e];
-    L.wsum[j][tid] = sf;
+    wsum[j][tid] = sf;
   }
   __syncthreads();
   // chunk row totals: wavefront w adds rows w, w + 8, ... (8 sums per lane)
   for (int j = wid; j < NC; j += kWaves) {
     double s = 0.0;
 #pragma unroll
-    for (int q = 0; q < kBlock / kWave; ++q) s += (double)L.wsum[j][lane * (kBlock / kWave) + q];
+    for (int q = 0; q < kBlock / kWave; ++q) s += (double)wsum[j][lane * (kBlock / kWave) + q];
     s = wave_sum(s);
     if (lane == 0) L.jsum[j] = s;
   }
@@ -490,7 +504,7 @@ __device__ __forceinline__ int walk_regs_lds(CW&& cw, double u, Lds& L, double* 
     double ls = 0.0;
 #pragma unroll
     for (int q = 0; q < kBlock / kWave; ++q) {
-      ts[q] = (double)L.wsum[jstar][lane * (kBlock / kWave) + q];
+      ts[q] = (double)wsum[jstar][lane * (kBlock / kWave) + q];
       ls += ts[q];
     }
     const double li = wave_incl_scan(ls);
@@ -566,99 +580,6 @@ __device__ __forceinline__ int walk_regs_lds(CW&& cw, double u, Lds& L, double* 
   }
   __syncthreads();
   const int tok = owner >= 0 ? L.si[4] : -1;
-  if (wtok) *wtok = L.sd[4];
-  __syncthreads();
-  return tok;
-}
-
-template <int NC, int EPC, class CW>
-__device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* total_out,
-                                         double* wtok = nullptr) {
-  if constexpr (NC <= kWalkLds) return walk_regs_lds<NC, EPC>(cw, u, L, total_out, wtok);
-  static_assert(NC <= kWalkBatch, "walk scratch too small");
-  const int tid = threadIdx.x, lane = __lane_id(), wid = tid / kWave;
-  // per chunk row, each 16-lane row's total (a butterfly inside the row, no
-  // cross-row step): 32 partial sums per chunk row, added in fixed order below
-#pragma unroll 2
-  for (int j = 0; j < NC; ++j) {
-    float w[EPC];
-    cw(j, w);
-    // a chunk's EPC weights add in float (within the draw's tolerance), the
-    // partial sums beyond it in double
-    float sf = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) sf += w[e];
-    double s = (double)sf;
-    if (__any(s > 0.0)) {   // skip the lane moves for empty wave chunks
-      s += dpp_perm_t<kDppXor1>(s);
-      s += dpp_perm_t<kDppXor2>(s);
-      s += dpp_perm_t<kDppHalfMirror>(s);
-      s += dpp_perm_t<kDppMirror>(s);
-    }
-    if ((lane & 15) == 0) L.jrow[j][wid * 4 + (lane >> 4)] = s;
-  }
-  __syncthreads();
-  if (tid < kWave) {
-    // lane j < NC totals chunk row j; a scan over lanes gives the running
-    // total in id order
-    double sj = 0.0;
-    if (lane < NC)
-#pragma unroll
-      for (int q = 0; q < kWaves * 4; ++q) sj += L.jrow[lane][q];
-    const double incl = wave_incl_scan(sj);
-    const double tot = readlane_t(incl, 63);
-    const double target = u * tot;
-    const double excl = incl - sj;
-    const unsigned long long hit = __ballot(sj > 0.0 && target < incl);
-    const unsigned long long nz = __ballot(sj > 0.0);
-    const int last = nz ? 63 - __clzll((long long)nz) : 0;
-    const int jstar = hit ? __ffsll((long long)hit) - 1 : last;
-    const double r1 = hit ? target - readlane_t(excl, jstar) : kPosInf;
-    if (lane == 0) {
-      L.si[2] = jstar;
-      L.sd[2] = r1;
-      L.sd[3] = tot;
-    }
-  }
-  __syncthreads();
-  const int jstar = __builtin_amdgcn_readfirstlane(L.si[2]);
-  const double r1 = L.sd[2];
-  *total_out = L.sd[3];
-  float wj[EPC];
-  cw(jstar, wj);
-  float minef = 0.0f;   // the same float sum as above
-#pragma unroll
-  for (int e = 0; e < EPC; ++e) minef += wj[e];
-  const double mine = (double)minef;
-  double tot2;
-  const double ex = block_excl_scan<kBlock>(mine, &tot2, L.bs);
-  const bool own = mine > 0.0 && ex <= r1 && r1 < ex + mine;
-  int owner = block_min<kBlock>(own ? tid : 0x7FFFFFFF, L.bs);
-  bool fallback = false;
-  if (owner == 0x7FFFFFFF) {  // rounding put the target past the end: last kept
-    owner = block_max<kBlock>(mine > 0.0 ? tid : -1, L.bs);
-    fallback = true;
-  }
-  if (tid == owner) {
-    double run = ex;
-    int pick = -1, lastpos = -1;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      if (wj[e] > 0.0f) {
-        run += (double)wj[e];
-        lastpos = e;
-        if (pick < 0 && !fallback && r1 < run) pick = e;
-      }
-    }
-    if (pick < 0) pick = lastpos;
-    L.si[3] = (jstar * kBlock + tid) * EPC + pick;
-    double wp = 0.0;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) wp = e == pick ? (double)wj[e] : wp;
-    L.sd[4] = wp;
-  }
-  __syncthreads();
-  const int tok = L.si[3];
   if (wtok) *wtok = L.sd[4];
   __syncthreads();
   return tok;
