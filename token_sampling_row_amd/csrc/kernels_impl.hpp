@@ -185,12 +185,13 @@ __device__ __forceinline__ Cut bf16_value_cut(const RegRow<1, NC>& r, float M, f
   const float M32 = M * (float)kVRes;
   uint32_t* cnt = L.vcnt + (__lane_id() & (kVCopies - 1)) * kVStride;
   __syncthreads();
-  // counts, branch-free (-inf goes to the copy's spare word past the bins);
-  // the elements of bins without a single value are weighed too, behind one
-  // test per chunk row from the chunk's lowest and highest bin (every bin in
-  // [bneg, kVBins - 2], or every bin at or below bpos, means none is there;
-  // -inf, placed in the last bin for that test, sends its chunk to the
-  // per-element test)
+  // counts, branch-free: -inf lands in the last bin with the clamp and is
+  // taken out of it again below (counted where a chunk reaches that bin). The
+  // elements of bins without a single value are weighed too, behind one test
+  // per chunk row from the chunk's lowest and highest bin (every bin in
+  // [bneg, kVBins - 2], or every bin at or below bpos, means none is there; a
+  // chunk holding -inf reaches the last bin and so takes the per-element test)
+  uint32_t ninf = 0u;
 #pragma unroll 1
   for (int j = 0; j < NC; ++j) {
     float v[EPC];
@@ -199,20 +200,22 @@ __device__ __forceinline__ Cut bf16_value_cut(const RegRow<1, NC>& r, float M, f
     int lo = kVBins, hi = 0;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
-      const int bc = (int)fminf(fmaf(v[e], -(float)kVRes, M32), (float)(kVBins - 1));
-      lo = min(lo, bc);
-      hi = max(hi, bc);
-      b[e] = v[e] > kNegInf ? bc : kVBins;
+      b[e] = (int)fminf(fmaf(v[e], -(float)kVRes, M32), (float)(kVBins - 1));
+      lo = min(lo, b[e]);
+      hi = max(hi, b[e]);
       atomicAdd(&cnt[b[e]], 1u);
     }
     const bool imp = !((hi <= kVBins - 2) & ((lo >= bneg) | (hi <= bpos)));
     if (__any(imp)) {
 #pragma unroll
-      for (int e = 0; e < EPC; ++e)
-        if ((b[e] < kVBins) & !pure(b[e]))
-          atomicAdd(&L.hmass[hslot(b[e])], to_fixed(weight(v[e], M, c)));
+      for (int e = 0; e < EPC; ++e) {
+        const bool fin = v[e] > kNegInf;
+        ninf += fin ? 0u : 1u;
+        if (fin & !pure(b[e])) atomicAdd(&L.hmass[hslot(b[e])], to_fixed(weight(v[e], M, c)));
+      }
     }
   }
+  if (ninf) atomicSub(&cnt[kVBins - 1], ninf);
   __syncthreads();
   double zt = 0.0;
   for (int b = tid; b < kVBins; b += kBlock) {

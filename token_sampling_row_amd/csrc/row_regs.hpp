@@ -175,14 +175,22 @@ struct MaskRegs {
 };
 
 // Bit j set iff pred(j) holds in some lane (pred is evaluated by every lane;
-// call with the whole wavefront active). Unrolled: NC compares and a few
-// scalar instructions.
+// call with the whole wavefront active). Each lane sets its own bits (vector
+// instructions only, no scalar test per chunk row), then one OR across the
+// wavefront.
 template <int NC, class Pred>
 __device__ __forceinline__ unsigned long long wave_chunk_mask(Pred pred) {
-  unsigned long long m = 0ull;
+  static_assert(NC <= 64, "one bit per chunk row");
+  uint32_t lo = 0u, hi = 0u;
 #pragma unroll
-  for (int j = 0; j < NC; ++j) m |= (__ballot(pred(j)) != 0ull) ? (1ull << j) : 0ull;
-  return m;
+  for (int j = 0; j < NC; ++j) {
+    if (j < 32) lo |= pred(j) ? (1u << (j & 31)) : 0u;
+    else hi |= pred(j) ? (1u << (j & 31)) : 0u;
+  }
+  auto bor = [](uint32_t a, uint32_t b) { return a | b; };
+  lo = wave_reduce(lo, bor);
+  if constexpr (NC > 32) hi = wave_reduce(hi, bor);
+  return ((unsigned long long)hi << 32) | lo;
 }
 __device__ __forceinline__ int pop_low(unsigned long long& m) {
   const int j = __builtin_amdgcn_readfirstlane(__builtin_ctzll(m));
@@ -595,10 +603,16 @@ struct KeptWeights {
     constexpr int EPC = Fmt<DT>::EPC;
     float v[EPC];
     r.elems(j, v);
-    float mx = v[0];   // the chunk maximum, where the row keeps none in registers
+    // a chunk wholly below tau is skipped on its maximum (kept in registers,
+    // else recomputed); the widest rows keep none and only reach here with
+    // wide kept sets, so they weigh every element instead
+    constexpr bool kReg = RegRow<DT, NC>::kKeepCmax, kNone = !kReg && NC > 16;
+    float mx = v[0];
+    if constexpr (!kReg && !kNone) {
 #pragma unroll
-    for (int e = 1; e < EPC; ++e) mx = fmaxf(mx, v[e]);
-    if ((RegRow<DT, NC>::kKeepCmax ? r.cmax(j) : mx) >= tau) {
+      for (int e = 1; e < EPC; ++e) mx = fmaxf(mx, v[e]);
+    }
+    if (kNone || (kReg ? r.cmax(j) : mx) >= tau) {
 #pragma unroll
       for (int e = 0; e < EPC; ++e) w[e] = v[e] >= tau ? weight(v[e], M, c) : 0.0f;
     } else {
@@ -761,11 +775,15 @@ __device__ __forceinline__ int wave_regions_total(const Lds& L) {
 
 // Top-k candidate bound: the k-th largest of the per-thread maxima (k <=
 // kBlock/4) or of the chunk maxima, which is at most the k-th largest logit.
-// Found on a linear histogram of [lo, M] and the smallest value in the bin
-// that reaches k. Returns -inf when fewer than k values are >= lo.
+// Found on a linear histogram of [lo, M]: the bound is the lower edge of the
+// bin that reaches k (two bin widths down, then checked to fall in a lower
+// bin, so it is at most every value of that bin), else, where rounding
+// defeats that check, the smallest value in the bin. Returns -inf when fewer
+// than k values are >= lo. cleared: the histogram counts are already zero
+// (and a barrier has passed since).
 template <int DT, int NC>
 __device__ __forceinline__ float topk_sketch(const RegRow<DT, NC>& r, float M, float lo,
-                                             int k, Lds& L) {
+                                             int k, Lds& L, bool cleared = false) {
   const int tid = threadIdx.x;
   const bool by_thread = k <= kBlock / 4;
   const float span = M - lo;
@@ -774,12 +792,10 @@ __device__ __forceinline__ float topk_sketch(const RegRow<DT, NC>& r, float M, f
     const float t = (M - x) * scale;
     return t < (float)(kBins - 1) ? (int)t : kBins - 1;
   };
-  for (int i = tid; i < kBins; i += kBlock) L.hcnt[i] = 0u;
-  if (tid == 0) {
-    L.si[6] = kBins;
-    L.su[0] = 0xFFFFFFFFu;
+  if (!cleared) {
+    for (int i = tid; i < kBins; i += kBlock) L.hcnt[i] = 0u;
+    __syncthreads();
   }
-  __syncthreads();
   if (by_thread) {
     if (r.tmax >= lo) atomicAdd(&L.hcnt[hslot(sbin(r.tmax))], 1u);
   } else {
@@ -792,40 +808,54 @@ __device__ __forceinline__ float topk_sketch(const RegRow<DT, NC>& r, float M, f
   __syncthreads();
   if (tid < kWave) {
     constexpr int PER = kBins / kWave;
+    int hc[PER];
     int lc = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) lc += (int)L.hcnt[hslot(tid * PER + i)];
+    for (int i = 0; i < PER; ++i) {
+      hc[i] = (int)L.hcnt[hslot(tid * PER + i)];
+      lc += hc[i];
+    }
     const int ic = wave_incl_scan(lc);
     int run = ic - lc;
     int found = kBins;
     if (run < k && ic >= k) {
+#pragma unroll
       for (int i = 0; i < PER; ++i) {
-        run += (int)L.hcnt[hslot(tid * PER + i)];
-        if (run >= k) {
-          found = tid * PER + i;
-          break;
-        }
+        run += hc[i];
+        if (found == kBins && run >= k) found = tid * PER + i;
       }
     }
     found = wave_min(found);
-    if (tid == 0) L.si[6] = found;
+    // the bin's lower edge, where it provably lies below every value of the
+    // bin (sbin is monotone: a value of a lower bin is below the whole bin)
+    float edge = kNegInf;
+    if (found < kBins) {
+      edge = fmaxf(M - (float)(found + 2) / scale, lo);
+      if (!(edge == lo || sbin(edge) > found)) edge = __builtin_nanf("");
+    }
+    if (tid == 0) {
+      L.si[6] = found;
+      L.sf[6] = edge;
+      L.su[0] = 0xFFFFFFFFu;
+    }
   }
   __syncthreads();
   const int bk = L.si[6];
-  if (bk < kBins) {
-    if (by_thread) {
-      if (r.tmax >= lo && sbin(r.tmax) == bk) atomicMin(&L.su[0], fkey(r.tmax));
-    } else {
+  const float edge = L.sf[6];
+  if (bk >= kBins) return kNegInf;
+  if (edge == edge) return edge;
+  if (by_thread) {
+    if (r.tmax >= lo && sbin(r.tmax) == bk) atomicMin(&L.su[0], fkey(r.tmax));
+  } else {
 #pragma nounroll
-      for (int j = 0; j < NC; ++j) {
-        const float x = r.cmax(j);
-        if (x >= lo && sbin(x) == bk) atomicMin(&L.su[0], fkey(x));
-      }
+    for (int j = 0; j < NC; ++j) {
+      const float x = r.cmax(j);
+      if (x >= lo && sbin(x) == bk) atomicMin(&L.su[0], fkey(x));
     }
   }
   __syncthreads();
   const uint32_t kb = L.su[0];
-  return (bk < kBins && kb != 0xFFFFFFFFu) ? key2f(kb) : kNegInf;
+  return kb != 0xFFFFFFFFu ? key2f(kb) : kNegInf;
 }
 
 // Candidate bound, compaction and exact resolution (see the file comment).
@@ -848,8 +878,12 @@ __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, floa
   // is a candidate and their sum is Z
   bool all_in = MASK && nallow <= kWaveCap;
   if (all_in || V <= kWaveCap) Lb = -kFltMax;
-  bool fits = false;
+  bool fits = false, cleared = false;
   if (Lb > kNegInf) {
+    // the sketch's histogram counts are cleared under the compaction's barrier
+    if (f.k_on)
+      for (int i = tid; i < kBins; i += kBlock) L.hcnt[i] = 0u;
+    cleared = f.k_on;
     wave_compact(r, Lb, L);
     __syncthreads();
     TSR_STAMP(kStCompact1);
@@ -857,7 +891,7 @@ __device__ __forceinline__ FastOut fast_cut(const RegRow<DT, NC>& r, int V, floa
   }
   if (!fits && f.k_on && V > kWaveCap) {
     __syncthreads();
-    const float kb = topk_sketch(r, M, fmaxf(Lb, tmin), f.k, L);
+    const float kb = topk_sketch(r, M, fmaxf(Lb, tmin), f.k, L, cleared);
     TSR_STAMP(kStSketch);
     if (kb > Lb) {
       Lb = kb;
