@@ -752,6 +752,15 @@ struct ResidualWeights {
   float izp, izq;   // 1 / Z_p, 1 / Z_q
   __device__ __forceinline__ void operator()(int j, float* w) const {
     constexpr int EPC = Fmt<DT>::EPC;
+    if (tp == -kFltMax && tq == -kFltMax) {   // both rows keep every element
+      float a[EPC], b[EPC];
+      rp.elems(j, a);
+      rq.elems(j, b);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e)
+        w[e] = fmaxf(weight(a[e], Mp, c) * izp - weight(b[e], Mq, c) * izq, 0.0f);
+      return;
+    }
     if (rp.cmax(j) >= tp) {
       float a[EPC], b[EPC];
       rp.elems(j, a);

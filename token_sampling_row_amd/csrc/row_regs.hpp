@@ -603,6 +603,11 @@ struct KeptWeights {
     constexpr int EPC = Fmt<DT>::EPC;
     float v[EPC];
     r.elems(j, v);
+    if (tau == -kFltMax) {   // every element (-inf weighs 0): no test at all
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) w[e] = weight(v[e], M, c);
+      return;
+    }
     // a chunk wholly below tau is skipped on its maximum (kept in registers,
     // else recomputed); the widest rows keep none and only reach here with
     // wide kept sets, so they weigh every element instead
@@ -661,7 +666,7 @@ __device__ __forceinline__ double reg_kept_mass(const RegRow<DT, NC>& r, float t
       r.elems(j, v);
       float t = 0.0f;
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) t += v[e] >= tau ? weight(v[e], M, c) : 0.0f;
+      for (int e = 0; e < EPC; ++e) t += weight(v[e], M, c);   // -inf weighs 0
       s += (double)t;
     }
     return block_sum<kBlock>(s, L.bs);
