@@ -336,6 +336,58 @@ __device__ __forceinline__ double wave_incl_max_scan(double x) {
   return x;
 }
 
+// The same over the first W lanes only (W = 16: one DPP row, whatever the
+// other rows hold; W = 64: the whole wavefront). Where the other rows hold
+// the operation's identity the results equal the whole-wavefront ones.
+template <int W, class T, class Op>
+__device__ __forceinline__ T reduce_w(T x, Op op) {
+  static_assert(W == 16 || W == 64, "width");
+  if constexpr (W == 64) {
+    return wave_reduce(x, op);
+  } else {
+    x = op(x, dpp_perm_t<kDppXor1>(x));
+    x = op(x, dpp_perm_t<kDppXor2>(x));
+    x = op(x, dpp_perm_t<kDppHalfMirror>(x));
+    x = op(x, dpp_perm_t<kDppMirror>(x));
+    return readlane_t(x, 0);
+  }
+}
+template <int W>
+__device__ __forceinline__ double sum_w(double x) {
+  return reduce_w<W>(x, [](double a, double b) { return a + b; });
+}
+template <int W>
+__device__ __forceinline__ uint32_t min_u32_w(uint32_t x) {
+  return reduce_w<W>(x, [](uint32_t a, uint32_t b) { return min(a, b); });
+}
+template <int W>
+__device__ __forceinline__ double incl_scan_w(double x) {
+  if constexpr (W == 64) return wave_incl_scan(x);
+  x += dpp_f64<kDppShr1>(x);
+  x += dpp_f64<kDppShr2>(x);
+  x += dpp_f64<kDppShr4>(x);
+  x += dpp_f64<kDppShr8>(x);
+  return x;
+}
+template <int W>
+__device__ __forceinline__ int incl_max_scan_w(int x) {
+  if constexpr (W == 64) return wave_incl_max_scan(x);
+  x = max(x, (int)dpp_u32<kDppShr1>((uint32_t)x));
+  x = max(x, (int)dpp_u32<kDppShr2>((uint32_t)x));
+  x = max(x, (int)dpp_u32<kDppShr4>((uint32_t)x));
+  x = max(x, (int)dpp_u32<kDppShr8>((uint32_t)x));
+  return x;
+}
+template <int W>
+__device__ __forceinline__ double incl_max_scan_w(double x) {
+  if constexpr (W == 64) return wave_incl_max_scan(x);
+  x = fmax(x, dpp_f64<kDppShr1>(x));
+  x = fmax(x, dpp_f64<kDppShr2>(x));
+  x = fmax(x, dpp_f64<kDppShr4>(x));
+  x = fmax(x, dpp_f64<kDppShr8>(x));
+  return x;
+}
+
 // ------------------------------------------------------------ wave sort
 // Value of lane (i ^ D) for D in {1, 2, 4, 8, 16, 32}: DPP inside 16-lane rows,
 // ds_swizzle across the two rows of a 32-lane half, ds_bpermute across halves.
@@ -395,13 +447,27 @@ __device__ __forceinline__ unsigned long long cx_layer(unsigned long long x) {
   const unsigned long long y = ((unsigned long long)phi << 32) | plo;
   return ((x > y) != low) ? y : x;
 }
-// Sorts one 64-bit key per lane into descending lane order inside each aligned
+template <int S, bool MIRROR>
+__device__ __forceinline__ uint32_t cx_layer(uint32_t x) {
+  uint32_t p;
+  bool low;
+  if constexpr (MIRROR) {
+    p = lane_mirror<S>(x);
+    low = (__lane_id() & (S / 2)) == 0;
+  } else {
+    p = lane_xor<S>(x);
+    low = (__lane_id() & S) == 0;
+  }
+  return ((x > p) != low) ? p : x;
+}
+// Sorts one 32- or 64-bit key per lane into descending lane order inside each aligned
 // block of W lanes (W = 16: DPP only; W = 64: the whole wavefront), with the
 // bitonic network in its mirror form: every comparator keeps the larger key
 // in the lower lane. All 64 lanes must be active.
-template <int W>
-__device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long x) {
+template <int W, class T>
+__device__ __forceinline__ T wave_sort_desc(T x) {
   static_assert(W == 16 || W == 64, "sort width");
+  static_assert(sizeof(T) == 8 || sizeof(T) == 4, "32- or 64-bit keys");
   x = cx_layer<2, true>(x);
   x = cx_layer<4, true>(x);
   x = cx_layer<1, false>(x);

@@ -478,7 +478,7 @@ __device__ __forceinline__ void wave_resolve_draw_w(Lds& L, unsigned long long k
                                                     bool z_exact, bool all_in, double u) {
   const int lane = __lane_id();
   if (all_in) {   // the candidates are every finite element: their sum is Z
-    zref = wave_sum(lane < n ? (double)weight(key2f(key_hi(key)), M, c) : 0.0);
+    zref = sum_w<W>(lane < n ? (double)weight(key2f(key_hi(key)), M, c) : 0.0);
     z_exact = true;
   }
   const uint32_t kM = fkey(M);
@@ -499,31 +499,32 @@ __device__ __forceinline__ void wave_resolve_draw_w(Lds& L, unsigned long long k
     const bool valid = lane < n;
     const uint32_t kh = key_hi(key);
     const double w = valid ? (double)weight(key2f(kh), M, c) : 0.0;
-    const double wall = wave_sum(w);
-    const uint32_t kmin = wave_min_u32(valid ? kh : 0xFFFFFFFFu);
-    const double above = wall - wave_sum(valid && kh == kmin ? w : 0.0);
+    const double wall = sum_w<W>(w);
+    const uint32_t kmin = min_u32_w<W>(valid ? kh : 0xFFFFFFFFu);
+    const double above = wall - sum_w<W>(valid && kh == kmin ? w : 0.0);
     const double thr = f.top_p * (seq_kp ? wall : (z_exact ? zref : zref * (1.0 - 1e-4)));
     sorted = !(above < thr) && kmin != kM;
   }
   if (sorted) {
+    // the value order alone decides the cut (equal values form one group),
+    // so the value keys sort without their ids
     ids = wave_sort_desc<W>(idkey);
-    key = wave_sort_desc<W>(key);
+    const uint32_t kh = wave_sort_desc<W>(key_hi(key));
     const bool valid = lane < n;
-    const uint32_t kh = key_hi(key);
     const float v = key2f(kh);
     const double w = valid ? (double)weight(v, M, c) : 0.0;
     const uint32_t prev = dpp_u32<kDppWaveShr1>(kh);
     const bool start = valid && (lane == 0 || prev != kh);
-    const int cnt_gt = wave_incl_max_scan(start ? lane : 0);
-    const double incl = wave_incl_scan(w);
-    const double mass_gt = wave_incl_max_scan(start ? incl - w : 0.0);
+    const int cnt_gt = incl_max_scan_w<W>(start ? lane : 0);
+    const double incl = incl_scan_w<W>(w);
+    const double mass_gt = incl_max_scan_w<W>(start ? incl - w : 0.0);
     const bool keep_k = !f.k_on || cnt_gt < f.k;
     const bool keep_m = v >= f.tau_m;
     bool keep_p = true;
     if (f.p_on) {
       double thr;
       if (seq_kp)
-        thr = f.top_p * wave_sum(valid && keep_k ? w : 0.0);
+        thr = f.top_p * sum_w<W>(valid && keep_k ? w : 0.0);
       else
         thr = f.top_p * (z_exact ? zref : zref * (1.0 - 1e-4));
       keep_p = mass_gt < thr || kh == kM;
@@ -541,14 +542,14 @@ __device__ __forceinline__ void wave_resolve_draw_w(Lds& L, unsigned long long k
     const uint32_t kh = key_hi(key);
     const bool keep = lane < n && key2f(kh) >= f.tau_m;
     n_in = __popcll(__ballot(keep));
-    tau = key2f(wave_min_u32(keep ? kh : 0xFFFFFFFFu));
+    tau = key2f(min_u32_w<W>(keep ? kh : 0xFFFFFFFFu));
   }
   const float vi = key2f((uint32_t)ids);
   const bool in = lane < n && vi >= tau;
   const uint32_t idx = ~key_hi(ids);
   const double w = in ? (double)weight(vi, M, c) : 0.0;
-  const double C = wave_incl_scan(w);
-  const double total = readlane_t(C, 63);
+  const double C = incl_scan_w<W>(w);
+  const double total = readlane_t(C, W - 1);
   const double target = u * total;
   const unsigned long long hit = __ballot(in && C > target);
   int pos;
