@@ -778,8 +778,10 @@ __device__ __forceinline__ int wave_regions_total(const Lds& L) {
   return t;
 }
 
-// Top-k candidate bound: the k-th largest of the per-thread maxima (k <=
-// kBlock/4) or of the chunk maxima, which is at most the k-th largest logit.
+// Top-k candidate bound: for k up to the wavefronts of a workgroup, the k-th
+// largest wavefront maximum; else the k-th largest of the per-thread maxima
+// (k <= kBlock/4) or of the chunk maxima; each is at most the k-th largest
+// logit.
 // Found on a linear histogram of [lo, M]: the bound is the lower edge of the
 // bin that reaches k (two bin widths down, then checked to fall in a lower
 // bin, so it is at most every value of that bin), else, where rounding
@@ -791,6 +793,23 @@ __device__ __forceinline__ float topk_sketch(const RegRow<DT, NC>& r, float M, f
                                              int k, Lds& L, bool cleared = false) {
   const int tid = threadIdx.x;
   const bool by_thread = k <= kBlock / 4;
+  if (k <= kWaves) {
+    // the k-th largest of the wavefront maxima (row statistics, in LDS since
+    // their barrier): k elements of the row are at least that large, so it
+    // bounds the k-th largest logit too, with no pass of its own
+    float mw[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mw[w] = L.ws[w].m;
+    float kth = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      int above = 0;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) above += (mw[v] > mw[w] || (mw[v] == mw[w] && v < w)) ? 1 : 0;
+      kth = above == k - 1 ? mw[w] : kth;
+    }
+    if (kth >= lo) return kth;
+  }
   const float span = M - lo;
   const float scale = (span > 0.0f && span <= kFltMax) ? fminf((float)kBins / span, 1e30f) : 0.0f;
   auto sbin = [&](float x) -> int {
