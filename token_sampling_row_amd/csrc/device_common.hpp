@@ -403,10 +403,15 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
   } else if constexpr (D == 8) {
     return dpp_perm_u32<kDppRor8>(x);
   } else if constexpr (D == 16) {
-    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F);  // and 31, xor 16
+    // v_permlane16_swap: result 0 holds rows 0, 0, 2, 2 and result 1 rows
+    // 1, 1, 3, 3 (16-lane rows), so each lane takes the other row of its pair
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (__lane_id() & 16) ? r[0] : r[1];
   } else {
     static_assert(D == 32, "lane distance");
-    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 32u) << 2), (int)x);
+    // v_permlane32_swap: result 0 holds the low half twice, result 1 the high
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (__lane_id() & 32) ? r[0] : r[1];
   }
 }
 // Value of lane (i ^ (S - 1)): the mirror image inside aligned blocks of S lanes.
@@ -421,10 +426,10 @@ __device__ __forceinline__ uint32_t lane_mirror(uint32_t x) {
   } else if constexpr (S == 16) {
     return dpp_perm_u32<kDppMirror>(x);
   } else if constexpr (S == 32) {
-    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x7C1F);  // and 31, xor 31
+    return lane_xor<16>(dpp_perm_u32<kDppMirror>(x));                   // i ^ 15 ^ 16
   } else {
     static_assert(S == 64, "block size");
-    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ 63u) << 2), (int)x);
+    return lane_xor<32>(lane_xor<16>(dpp_perm_u32<kDppMirror>(x)));     // i ^ 15 ^ 16 ^ 32
   }
 }
 // One comparator layer: each lane meets its partner (mirror inside blocks of
