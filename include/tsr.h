@@ -29,11 +29,11 @@
  *    of range) are reported per row through a status array, with token -1.
  *    A failed launch returns TSR_EDEVICE. No C++ exception crosses this ABI.
  *  - Logits are float32 or bfloat16, row-major; each row holds `vocab`
- *    elements. Pointers must be aligned to the element size; when the first
- *    row and the row stride are 16-byte aligned rows are read with 128-bit
- *    loads, otherwise (a contiguous batch of an odd vocab) in dwords, which
- *    may read up to 2 bytes before a bf16 row and after its last element, in
- *    the same aligned dword (never across a page).
+ *    elements. Pointers must be aligned to the element size. Rows may start
+ *    at any element boundary (a contiguous batch of an odd vocab too): they
+ *    are read in 16-byte loads at whatever alignment they have, under the
+ *    unaligned access mode the HSA runtime sets, and no byte outside a row
+ *    is read.
  *  - A handle is not thread-safe. Two calls on one handle may run on different
  *    streams only if they are not verify calls (verify uses per-handle
  *    workspace).

@@ -145,7 +145,7 @@ def test_beam_argument_errors():
 
 
 def test_beam_unaligned_rows():
-    """Rows whose start is not 16-byte aligned (element loads)."""
+    """Rows whose start is not 16-byte aligned (16-byte loads at any alignment)."""
     rng = np.random.default_rng(8)
     V, beam = 3001, 4
     base = rng.normal(0, 1.5, (16, V + 3)).astype(np.float32)

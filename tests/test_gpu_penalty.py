@@ -95,7 +95,7 @@ def test_penalty_grid(dtype, V, H):
 
 def test_penalty_with_mask_and_unaligned_rows():
     """The penalty before an allowed-token mask, in aligned rows and in rows
-    whose start is not 16-byte aligned (the streaming kernel)."""
+    whose start is not 16-byte aligned."""
     rng = np.random.default_rng(9)
     V = 5003
     base = rng.normal(0, 1.5, (12, V + 3)).astype(np.float32)

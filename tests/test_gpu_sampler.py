@@ -101,7 +101,7 @@ def test_sample_strided_and_unaligned():
     rng = np.random.default_rng(4)
     V = 3001
     base = rng.normal(0, 1.5, (24, V + 5)).astype(np.float32)
-    x = to_dev(base, "f32")[:, 3:V + 3]          # unaligned rows, element-wise register loads
+    x = to_dev(base, "f32")[:, 3:V + 3]          # rows not 16-byte aligned
     values = oracle.values_from_stored(np.ascontiguousarray(base[:, 3:V + 3]), "f32")
     seed = 5150
     with make_sampler(seed) as s:

@@ -46,61 +46,56 @@ def _hipcc() -> str:
 def instance_units() -> dict[str, str]:
     """name -> source of one translation unit per kernel instance."""
     head = '#define TSR_INSTANCE_UNIT 1\n#include "dispatch.hpp"\nnamespace tsr {\n'
+    sample_args = "(const unsigned char*, long long, int, int, KParams, int32_t*, DiagPtrs);\n}\n"
     units = {}
     for dt in (0, 1):
         for nc in ROW_NCS:
             units[f"i_sample_{dt}_{nc}.hip"] = head + (
-                f"template __global__ void sample_kernel<{dt}, {nc}, false, 0>(const unsigned "
-                "char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);\n}\n")
+                f"template __global__ void sample_kernel<{dt}, {nc}, false, 0>" + sample_args)
             if dt == 1:   # the register-resident finish for wide kept sets (bf16)
                 units[f"i_sample_wide_{dt}_{nc}.hip"] = head + (
-                    f"template __global__ void sample_kernel<{dt}, {nc}, true, 0>(const unsigned "
-                    "char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);\n}\n")
-            # an allowed-token set (1), a repetition penalty only (2), rows
-            # not 16-byte aligned (3); bf16 takes the wide finish as well
+                    f"template __global__ void sample_kernel<{dt}, {nc}, true, 0>" + sample_args)
+            # an allowed-token set (1), a repetition penalty only (2); bf16
+            # takes the wide finish as well
             wide = "true" if dt == 1 else "false"
-            for ext, tag in ((1, "mask"), (2, "rep"), (3, "unal")):
+            for ext, tag in ((1, "mask"), (2, "rep")):
                 units[f"i_sample_{tag}_{dt}_{nc}.hip"] = head + (
-                    f"template __global__ void sample_kernel<{dt}, {nc}, {wide}, {ext}>(const "
-                    "unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);\n}\n")
+                    f"template __global__ void sample_kernel<{dt}, {nc}, {wide}, {ext}>" + sample_args)
             units[f"i_beam_{dt}_{nc}.hip"] = head + (
                 f"template __global__ void beam_kernel<{dt}, {nc}>(const unsigned char*, long long, "
-                "int, int, int, int, const double*, BeamWs, int32_t*, int32_t*, double*, "
-                "int32_t*);\n}\n")
+                "int, int, int, const double*, BeamWs, int32_t*, int32_t*, double*, int32_t*);\n}\n")
             units[f"i_greedy_{dt}_{nc}.hip"] = head + (
                 f"template __global__ void greedy_kernel<{dt}, {nc}>(const unsigned char*, "
-                "long long, int, int, int, int32_t*, int32_t*);\n}\n")
+                "long long, int, int, int32_t*, int32_t*);\n}\n")
         for nc in VERIFY_NCS:
-            for un in ("false", "true"):
-                # two rows per workgroup: no chunk maxima kept in registers
-                units[f"i_verify_{dt}_{nc}_{un}.hip"] = "#define TSR_ROW_NO_CMAX 1\n" + head + (
-                    f"template __global__ void verify_kernel<{dt}, {nc}, {un}>(const unsigned char*, "
-                    "const unsigned char*, const int32_t*, int, int, int, int, KParams, VerifyWs, "
-                    "int32_t*, int32_t*, int32_t*);\n"
-                    f"template __global__ void tree_kernel<{dt}, {nc}, {un}>(const unsigned char*, "
-                    "const unsigned char*, const int32_t*, const int32_t*, int, int, int, KParams, "
-                    "VerifyWs, int32_t*, int32_t*, int32_t*, int32_t*);\n}\n")
+            # two rows per workgroup: no chunk maxima kept in registers
+            units[f"i_verify_{dt}_{nc}.hip"] = "#define TSR_ROW_NO_CMAX 1\n" + head + (
+                f"template __global__ void verify_kernel<{dt}, {nc}>(const unsigned char*, "
+                "const unsigned char*, const int32_t*, int, int, int, KParams, VerifyWs, "
+                "int32_t*, int32_t*, int32_t*);\n"
+                f"template __global__ void tree_kernel<{dt}, {nc}>(const unsigned char*, "
+                "const unsigned char*, const int32_t*, const int32_t*, int, int, int, KParams, "
+                "VerifyWs, int32_t*, int32_t*, int32_t*, int32_t*);\n}\n")
         for nc in VERIFY_WIDE_NCS:
-            for un in ("false", "true"):
-                for tree in ("false", "true"):
-                    units[f"i_vrows_{dt}_{nc}_{un}_{tree}.hip"] = head + (
-                        f"template __global__ void verify_rows_kernel<{dt}, {nc}, {un}, {tree}>("
-                        "const unsigned char*, const unsigned char*, const int32_t*, int, int, int, "
-                        "KParams, VerifyWs);\n}\n")
+            for tree in ("false", "true"):
+                units[f"i_vrows_{dt}_{nc}_{tree}.hip"] = head + (
+                    f"template __global__ void verify_rows_kernel<{dt}, {nc}, {tree}>("
+                    "const unsigned char*, const unsigned char*, const int32_t*, int, int, int, "
+                    "KParams, VerifyWs);\n}\n")
         units[f"i_vfinish_{dt}.hip"] = head + (
             f"template __global__ void verify_finish_kernel<{dt}>(const unsigned char*, const "
-            "unsigned char*, const int32_t*, int, int, int, KParams, VerifyWs, int32_t*, int32_t*, "
+            "unsigned char*, const int32_t*, int, int, KParams, VerifyWs, int32_t*, int32_t*, "
             "int32_t*);\n"
             f"template __global__ void verify_draw_kernel<{dt}>(const unsigned char*, const "
-            "unsigned char*, int, int, int, KParams, VerifyWs, int32_t*);\n"
+            "unsigned char*, int, int, KParams, VerifyWs, int32_t*);\n"
             f"template __global__ void tree_finish_kernel<{dt}>(const unsigned char*, const unsigned "
-            "char*, const int32_t*, const int32_t*, int, int, int, KParams, VerifyWs, int32_t*, "
+            "char*, const int32_t*, const int32_t*, int, int, KParams, VerifyWs, int32_t*, "
             "int32_t*, int32_t*, int32_t*);\n}\n")
         units[f"i_stream_{dt}.hip"] = head + (
             f"template __global__ void sample_kernel_stream<{dt}>(const unsigned char*, long long, "
-            "int, int, KParams, int32_t*, DiagPtrs);\n"
+            "int, KParams, int32_t*, DiagPtrs);\n"
             f"template __global__ void greedy_kernel_stream<{dt}>(const unsigned char*, long long, "
-            "int, int, int32_t*, int32_t*);\n}\n")
+            "int, int32_t*, int32_t*);\n}\n")
     return units
 
 

@@ -126,12 +126,11 @@ int launch_verify_checked(const void* target_logits, const void* draft_logits, i
                           const int32_t* draft_tokens, int rows, int K, int vocab,
                           const tsr::KParams& kp, const tsr::VerifyWs& ws, int32_t* out_tokens,
                           int32_t* out_accepted, int32_t* out_status, void* hip_stream) {
-  const long long rb = (long long)vocab * esize(dtype);
-  const int aligned = ((uintptr_t)target_logits % 16 == 0) &&
-                      (!draft_logits || (uintptr_t)draft_logits % 16 == 0) && (rb % 16 == 0);
-  const int ragged = !aligned || (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;
+  // a row of a whole number of 16-byte chunks has no partial one (rows may
+  // start at any element boundary)
+  const int ragged = (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;
   const hipError_t e = tsr::launch_verify(target_logits, draft_logits, dtype, draft_tokens, rows,
-                                          K, vocab, aligned, ragged, kp, ws, out_tokens,
+                                          K, vocab, ragged, kp, ws, out_tokens,
                                           out_accepted, out_status, (hipStream_t)hip_stream);
   return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
 }
@@ -275,10 +274,9 @@ int greedy_argmax(tsr_handle h, const void* logits, int dtype, int rows, int voc
   if (vocab > tsr::max_vocab_sample(dtype)) return TSR_EUNSUPPORTED;
   if (rows == 0) return TSR_OK;
   const long long sb = (long long)row_stride * esize(dtype);
-  const int aligned = ((uintptr_t)logits % 16 == 0) && (sb % 16 == 0);
-  const int ragged = !aligned || (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;
+  const int ragged = (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;   // a partial last chunk
   return on_device(h->device, [&]() -> int {
-    const hipError_t e = tsr::launch_greedy(logits, dtype, rows, vocab, sb, aligned, ragged,
+    const hipError_t e = tsr::launch_greedy(logits, dtype, rows, vocab, sb, ragged,
                                             out_tokens, out_status, (hipStream_t)hip_stream);
     return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
   });
@@ -346,10 +344,9 @@ int sample_rows_ex(tsr_handle h, const void* logits, int dtype, int rows, int vo
     kp.flags |= tsr::F_REP;
   }
   const long long sb = (long long)row_stride * esize(dtype);
-  const int aligned = ((uintptr_t)logits % 16 == 0) && (sb % 16 == 0);
-  const int ragged = !aligned || (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;
+  const int ragged = (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;   // a partial last chunk
   return on_device(h->device, [&]() -> int {
-    const hipError_t e = tsr::launch_sample(logits, dtype, rows, vocab, sb, aligned, ragged, kp,
+    const hipError_t e = tsr::launch_sample(logits, dtype, rows, vocab, sb, ragged, kp,
                                             out_tokens, dg, (hipStream_t)hip_stream);
     return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
   });
@@ -452,13 +449,12 @@ int tree_verify(tsr_handle h, const void* target_logits, const void* draft_logit
 #if TSR_TRACE
   kp.trace = h->trace;
 #endif
-  const long long rb = (long long)vocab * esize(dtype);
-  const int aligned = ((uintptr_t)target_logits % 16 == 0) &&
-                      (!draft_logits || (uintptr_t)draft_logits % 16 == 0) && (rb % 16 == 0);
-  const int ragged = !aligned || (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;
+  // a row of a whole number of 16-byte chunks has no partial one (rows may
+  // start at any element boundary)
+  const int ragged = (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;
   return on_device(h->device, [&]() -> int {
     const hipError_t e = tsr::launch_tree(target_logits, draft_logits, dtype, parent, tokens, rows,
-                                          nodes, vocab, aligned, ragged, kp, h->ws, out_tokens,
+                                          nodes, vocab, ragged, kp, h->ws, out_tokens,
                                           out_path, out_accepted, out_status,
                                           (hipStream_t)hip_stream);
     return e == hipSuccess ? TSR_OK : TSR_EDEVICE;
@@ -477,10 +473,9 @@ int beam_step(tsr_handle h, const void* logits, int dtype, int groups, int beam,
   if (vocab > tsr::max_vocab_beam(dtype)) return TSR_EUNSUPPORTED;
   const long long sb = (long long)row_stride * esize(dtype);
   if (groups == 0) return TSR_OK;
-  const int aligned = ((uintptr_t)logits % 16 == 0) && (sb % 16 == 0);
-  const int ragged = !aligned || (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;
+  const int ragged = (vocab % (dtype == TSR_F32 ? 4 : 8)) != 0;   // a partial last chunk
   return on_device(h->device, [&]() -> int {
-    const hipError_t e = tsr::launch_beam(logits, dtype, groups, beam, vocab, sb, aligned, ragged,
+    const hipError_t e = tsr::launch_beam(logits, dtype, groups, beam, vocab, sb, ragged,
                                           beam_scores, h->bws, out_parent, out_token, out_score,
                                           out_status, (hipStream_t)hip_stream);
     return e == hipSuccess ? TSR_OK : TSR_EDEVICE;

@@ -38,7 +38,7 @@ __device__ __forceinline__ void unpack(const uint4 r, float* v) {
 // Element-wise load of chunk c of a row (elements [c*EPC, c*EPC+EPC));
 // elements at or past V read as -inf. Branch-free: an element past the end
 // re-reads element V-1 and is replaced by -inf. Used for the ragged tail of a
-// row and for rows that are not 16-byte aligned.
+// row.
 template <int DT>
 __device__ __forceinline__ uint4 load_chunk_slow(const unsigned char* row, long long c, int V) {
   constexpr int EPC = Fmt<DT>::EPC;
@@ -59,40 +59,6 @@ __device__ __forceinline__ uint4 load_chunk_slow(const unsigned char* row, long 
     }
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-// Chunk c of a row that is not 16-byte aligned, in whole dwords: fp32 rows
-// are 4-byte aligned already (element-wise dword loads); a bf16 row read from
-// the 4-byte boundary at or below its start (in the same dword, so the same
-// page), five dwords per chunk, realigned by a 2-byte shift when the row
-// starts half-way into a dword. Dwords past the last element's re-read it;
-// elements at or past V read as -inf.
-template <int DT>
-__device__ __forceinline__ uint4 load_chunk_unaligned(const unsigned char* row, long long c,
-                                                      int V) {
-  if constexpr (DT == 0) {
-    return load_chunk_slow<0>(row, c, V);
-  } else {
-    const int sh = (int)(((uintptr_t)row >> 1) & 1u);   // element offset into the dword
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(row - 2 * sh);
-    const long long kmax = ((long long)V - 1 + sh) >> 1;   // dword of element V-1
-    uint32_t d[5];
-#pragma unroll
-    for (int w = 0; w < 5; ++w) {
-      const long long k = 4 * c + w;
-      d[w] = q[k < kmax ? k : kmax];
-    }
-    const long long e0 = c * 8;
-    uint32_t o[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t x = sh ? __builtin_amdgcn_alignbyte(d[w + 1], d[w], 2u) : d[w];
-      if (e0 + 2 * w >= V) x = (x & 0xFFFF0000u) | 0xFF80u;
-      if (e0 + 2 * w + 1 >= V) x = (x & 0x0000FFFFu) | 0xFF800000u;
-      o[w] = x;
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
-  }
 }
 
 template <int DT>

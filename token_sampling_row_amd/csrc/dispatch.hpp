@@ -28,76 +28,62 @@ constexpr int kVerifyWideNcs[] = {24, 32, 38};
 
 // Each kernel instance is compiled in a translation unit of its own (the
 // build generates them), so the units that launch them only declare them.
+#define TSR_SAMPLE_ARGS const unsigned char*, long long, int, int, KParams, int32_t*, DiagPtrs
 #define TSR_DECLARE_ROW(N)                                                                   \
-  extern template __global__ void sample_kernel<0, N, false, 0>(                             \
-      const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
-  extern template __global__ void sample_kernel<1, N, false, 0>(                             \
-      const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
-  extern template __global__ void sample_kernel<1, N, true, 0>(                              \
-      const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
-  extern template __global__ void sample_kernel<0, N, false, 1>(                             \
-      const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
-  extern template __global__ void sample_kernel<0, N, false, 2>(                             \
-      const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
-  extern template __global__ void sample_kernel<1, N, true, 2>(                              \
-      const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
-  extern template __global__ void sample_kernel<0, N, false, 3>(                             \
-      const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
-  extern template __global__ void sample_kernel<1, N, true, 3>(                              \
-      const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
+  extern template __global__ void sample_kernel<0, N, false, 0>(TSR_SAMPLE_ARGS);             \
+  extern template __global__ void sample_kernel<1, N, false, 0>(TSR_SAMPLE_ARGS);             \
+  extern template __global__ void sample_kernel<1, N, true, 0>(TSR_SAMPLE_ARGS);              \
+  extern template __global__ void sample_kernel<0, N, false, 1>(TSR_SAMPLE_ARGS);             \
+  extern template __global__ void sample_kernel<0, N, false, 2>(TSR_SAMPLE_ARGS);             \
+  extern template __global__ void sample_kernel<1, N, true, 1>(TSR_SAMPLE_ARGS);              \
+  extern template __global__ void sample_kernel<1, N, true, 2>(TSR_SAMPLE_ARGS);              \
   extern template __global__ void beam_kernel<0, N>(const unsigned char*, long long, int, int,  \
-                                                    int, int, const double*, BeamWs,          \
-                                                    int32_t*, int32_t*, double*, int32_t*);   \
+                                                    int, const double*, BeamWs, int32_t*,    \
+                                                    int32_t*, double*, int32_t*);            \
   extern template __global__ void beam_kernel<1, N>(const unsigned char*, long long, int, int,  \
-                                                    int, int, const double*, BeamWs,          \
-                                                    int32_t*, int32_t*, double*, int32_t*);   \
-  extern template __global__ void sample_kernel<1, N, true, 1>(                           \
-      const unsigned char*, long long, int, int, int, KParams, int32_t*, DiagPtrs);          \
+                                                    int, const double*, BeamWs, int32_t*,    \
+                                                    int32_t*, double*, int32_t*);            \
   extern template __global__ void greedy_kernel<0, N>(const unsigned char*, long long, int,  \
-                                                      int, int, int32_t*, int32_t*);          \
+                                                      int, int32_t*, int32_t*);               \
   extern template __global__ void greedy_kernel<1, N>(const unsigned char*, long long, int,  \
-                                                      int, int, int32_t*, int32_t*);
-#define TSR_DECLARE_VERIFY_DT(D, N, U)                                                        \
-  extern template __global__ void verify_kernel<D, N, U>(                                     \
-      const unsigned char*, const unsigned char*, const int32_t*, int, int, int, int, KParams,  \
+                                                      int, int32_t*, int32_t*);
+#define TSR_DECLARE_VERIFY_DT(D, N)                                                           \
+  extern template __global__ void verify_kernel<D, N>(                                        \
+      const unsigned char*, const unsigned char*, const int32_t*, int, int, int, KParams,      \
       VerifyWs, int32_t*, int32_t*, int32_t*);                                                 \
-  extern template __global__ void tree_kernel<D, N, U>(                                       \
+  extern template __global__ void tree_kernel<D, N>(                                          \
       const unsigned char*, const unsigned char*, const int32_t*, const int32_t*, int, int,    \
       int, KParams, VerifyWs, int32_t*, int32_t*, int32_t*, int32_t*);
-#define TSR_DECLARE_VERIFY(N)                                                                \
-  TSR_DECLARE_VERIFY_DT(0, N, false) TSR_DECLARE_VERIFY_DT(0, N, true)                       \
-  TSR_DECLARE_VERIFY_DT(1, N, false) TSR_DECLARE_VERIFY_DT(1, N, true)
-#define TSR_DECLARE_VROWS_DT(D, N, U, T)                                                      \
-  extern template __global__ void verify_rows_kernel<D, N, U, T>(                             \
+#define TSR_DECLARE_VERIFY(N) TSR_DECLARE_VERIFY_DT(0, N) TSR_DECLARE_VERIFY_DT(1, N)
+#define TSR_DECLARE_VROWS_DT(D, N, T)                                                         \
+  extern template __global__ void verify_rows_kernel<D, N, T>(                                \
       const unsigned char*, const unsigned char*, const int32_t*, int, int, int, KParams,      \
       VerifyWs);
 #define TSR_DECLARE_VROWS(N)                                                                 \
-  TSR_DECLARE_VROWS_DT(0, N, false, false) TSR_DECLARE_VROWS_DT(0, N, true, false)           \
-  TSR_DECLARE_VROWS_DT(1, N, false, false) TSR_DECLARE_VROWS_DT(1, N, true, false)           \
-  TSR_DECLARE_VROWS_DT(0, N, false, true) TSR_DECLARE_VROWS_DT(0, N, true, true)             \
-  TSR_DECLARE_VROWS_DT(1, N, false, true) TSR_DECLARE_VROWS_DT(1, N, true, true)
+  TSR_DECLARE_VROWS_DT(0, N, false) TSR_DECLARE_VROWS_DT(1, N, false)                        \
+  TSR_DECLARE_VROWS_DT(0, N, true) TSR_DECLARE_VROWS_DT(1, N, true)
 #define TSR_DECLARE_VFINISH(D)                                                                \
   extern template __global__ void verify_finish_kernel<D>(                                    \
-      const unsigned char*, const unsigned char*, const int32_t*, int, int, int, KParams,      \
-      VerifyWs, int32_t*, int32_t*, int32_t*);                                                 \
+      const unsigned char*, const unsigned char*, const int32_t*, int, int, KParams, VerifyWs, \
+      int32_t*, int32_t*, int32_t*);                                                           \
   extern template __global__ void verify_draw_kernel<D>(                                      \
-      const unsigned char*, const unsigned char*, int, int, int, KParams, VerifyWs, int32_t*); \
+      const unsigned char*, const unsigned char*, int, int, KParams, VerifyWs, int32_t*);      \
   extern template __global__ void tree_finish_kernel<D>(                                      \
       const unsigned char*, const unsigned char*, const int32_t*, const int32_t*, int, int,    \
-      int, KParams, VerifyWs, int32_t*, int32_t*, int32_t*, int32_t*);
+      KParams, VerifyWs, int32_t*, int32_t*, int32_t*, int32_t*);
 #ifndef TSR_INSTANCE_UNIT
 TSR_ROW_NCS(TSR_DECLARE_ROW)
 TSR_VERIFY_NCS(TSR_DECLARE_VERIFY)
 TSR_VERIFY_WIDE_NCS(TSR_DECLARE_VROWS)
 TSR_DECLARE_VFINISH(0)
 TSR_DECLARE_VFINISH(1)
-extern template __global__ void sample_kernel_stream<0>(const unsigned char*, long long, int, int,
+extern template __global__ void sample_kernel_stream<0>(const unsigned char*, long long, int,
                                                         KParams, int32_t*, DiagPtrs);
-extern template __global__ void sample_kernel_stream<1>(const unsigned char*, long long, int, int,
+extern template __global__ void sample_kernel_stream<1>(const unsigned char*, long long, int,
                                                         KParams, int32_t*, DiagPtrs);
-extern template __global__ void greedy_kernel_stream<0>(const unsigned char*, long long, int, int,
+extern template __global__ void greedy_kernel_stream<0>(const unsigned char*, long long, int,
                                                         int32_t*, int32_t*);
-extern template __global__ void greedy_kernel_stream<1>(const unsigned char*, long long, int, int,
+extern template __global__ void greedy_kernel_stream<1>(const unsigned char*, long long, int,
                                                         int32_t*, int32_t*);
 #endif
 

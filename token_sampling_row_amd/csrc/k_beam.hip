@@ -4,7 +4,7 @@
 namespace tsr {
 
 hipError_t launch_beam(const void* logits, int dtype, int groups, int beam, int V,
-                       long long stride_bytes, int aligned, int ragged, const double* scores, BeamWs ws,
+                       long long stride_bytes, int ragged, const double* scores, BeamWs ws,
                        int32_t* out_parent, int32_t* out_tok, double* out_score,
                        int32_t* out_status, hipStream_t s) {
   const int nc = pick_nc(chunks_per_thread(dtype, V), kRowNcs, 8);
@@ -15,11 +15,11 @@ hipError_t launch_beam(const void* logits, int dtype, int groups, int beam, int 
   case N:                                                                                    \
     if (dtype == 0)                                                                          \
       hipLaunchKernelGGL((beam_kernel<0, N>), dim3(rows), dim3(kBlock), 0, s, p,             \
-                         stride_bytes, V, aligned, ragged, beam, scores, ws, out_parent, out_tok,     \
+                         stride_bytes, V, ragged, beam, scores, ws, out_parent, out_tok,     \
                          out_score, out_status);                                             \
     else                                                                                     \
       hipLaunchKernelGGL((beam_kernel<1, N>), dim3(rows), dim3(kBlock), 0, s, p,             \
-                         stride_bytes, V, aligned, ragged, beam, scores, ws, out_parent, out_tok,     \
+                         stride_bytes, V, ragged, beam, scores, ws, out_parent, out_tok,     \
                          out_score, out_status);                                             \
     break;
   switch (nc) {

@@ -4,36 +4,26 @@
 namespace tsr {
 
 hipError_t launch_greedy(const void* logits, int dtype, int rows, int V, long long stride_bytes,
-                         int aligned, int ragged, int32_t* out, int32_t* status, hipStream_t s) {
+                         int ragged, int32_t* out, int32_t* status, hipStream_t s) {
   const int nc = pick_nc(chunks_per_thread(dtype, V), kRowNcs, 8);
   const unsigned char* p = static_cast<const unsigned char*>(logits);
-  if (nc != 0 && !aligned) {
-    // rows not on a 16-byte boundary: the sampler's unaligned register
-    // instance at temperature 0 (the same argmax, lowest id first, and status)
-    KParams kp{};
-    kp.c = 1.0f;
-    kp.flags = F_GREEDY;
-    DiagPtrs dg{};
-    dg.status = status;
-    return launch_sample(logits, dtype, rows, V, stride_bytes, aligned, ragged, kp, out, dg, s);
-  }
   if (nc == 0) {   // wider than the register file: stream
     if (dtype == 0)
       hipLaunchKernelGGL((greedy_kernel_stream<0>), dim3(rows), dim3(kBlock), 0, s, p,
-                         stride_bytes, V, aligned, out, status);
+                         stride_bytes, V, out, status);
     else
       hipLaunchKernelGGL((greedy_kernel_stream<1>), dim3(rows), dim3(kBlock), 0, s, p,
-                         stride_bytes, V, aligned, out, status);
+                         stride_bytes, V, out, status);
     return hipGetLastError();
   }
 #define TSR_CASE(N)                                                                      \
   case N:                                                                                \
     if (dtype == 0)                                                                      \
       hipLaunchKernelGGL((greedy_kernel<0, N>), dim3(rows), dim3(kBlock), 0, s, p,       \
-                         stride_bytes, V, aligned, ragged, out, status);                 \
+                         stride_bytes, V, ragged, out, status);                 \
     else                                                                                 \
       hipLaunchKernelGGL((greedy_kernel<1, N>), dim3(rows), dim3(kBlock), 0, s, p,       \
-                         stride_bytes, V, aligned, ragged, out, status);                 \
+                         stride_bytes, V, ragged, out, status);                 \
     break;
   switch (nc) {
     TSR_ROW_NCS(TSR_CASE)

@@ -4,35 +4,30 @@
 namespace tsr {
 
 hipError_t launch_sample_dt1(const unsigned char* p, int rows, int V, long long stride_bytes,
-                              int aligned, int ragged, const KParams& kp, int32_t* out,
-                              const DiagPtrs& dg, hipStream_t s) {
+                              int ragged, const KParams& kp, int32_t* out, const DiagPtrs& dg,
+                              hipStream_t s) {
   const int nc = pick_nc(chunks_per_thread(1, V), kRowNcs, 8);
   const int ext = (kp.flags & F_MASK) ? 1 : (kp.flags & F_REP) ? 2 : 0;
-  // wider than the register file, or unaligned rows under a mask or a
-  // penalty: stream (other unaligned rows are read in dwords into registers)
-  if (nc == 0 || (!aligned && ext != 0)) {
+  if (nc == 0) {   // wider than the register file: stream
     hipLaunchKernelGGL((sample_kernel_stream<1>), dim3(rows), dim3(kBlock), 0, s, p,
-                       stride_bytes, V, aligned, kp, out, dg);
+                       stride_bytes, V, kp, out, dg);
     return hipGetLastError();
   }
   const bool wide = (kp.flags & F_ROWP) != 0 || wide_filters(kp, kBlock);
 #define TSR_CASE(N)                                                                            \
   case N:                                                                                      \
-    if (!aligned)                                                                              \
-      hipLaunchKernelGGL((sample_kernel<1, N, true, 3>), dim3(rows), dim3(kBlock), 0, s, p,    \
-                         stride_bytes, V, aligned, ragged, kp, out, dg);                       \
-    else if (ext == 1)                                                                         \
+    if (ext == 1)                                                                              \
       hipLaunchKernelGGL((sample_kernel<1, N, true, 1>), dim3(rows), dim3(kBlock), 0, s, p,    \
-                         stride_bytes, V, aligned, ragged, kp, out, dg);                       \
+                         stride_bytes, V, ragged, kp, out, dg);                                \
     else if (ext == 2)                                                                         \
       hipLaunchKernelGGL((sample_kernel<1, N, true, 2>), dim3(rows), dim3(kBlock), 0, s, p,    \
-                         stride_bytes, V, aligned, ragged, kp, out, dg);                       \
+                         stride_bytes, V, ragged, kp, out, dg);                                \
     else if (wide)                                                                             \
       hipLaunchKernelGGL((sample_kernel<1, N, true, 0>), dim3(rows), dim3(kBlock), 0, s, p,    \
-                         stride_bytes, V, aligned, ragged, kp, out, dg);                       \
+                         stride_bytes, V, ragged, kp, out, dg);                                \
     else                                                                                       \
       hipLaunchKernelGGL((sample_kernel<1, N, false, 0>), dim3(rows), dim3(kBlock), 0, s, p,   \
-                         stride_bytes, V, aligned, ragged, kp, out, dg);                       \
+                         stride_bytes, V, ragged, kp, out, dg);                                \
     break;
   switch (nc) {
     TSR_ROW_NCS(TSR_CASE)

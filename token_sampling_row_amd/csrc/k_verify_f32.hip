@@ -4,7 +4,7 @@
 namespace tsr {
 
 hipError_t launch_verify_dt0(const unsigned char* tp, const unsigned char* dp, const int32_t* xs,
-                             int rows, int K, int V, int aligned, int ragged, const KParams& kp,
+                             int rows, int K, int V, int ragged, const KParams& kp,
                              const VerifyWs& ws, int32_t* out_tokens, int32_t* out_acc,
                              int32_t* out_status, hipStream_t s) {
   const int need = chunks_per_thread(0, V);
@@ -16,12 +16,8 @@ hipError_t launch_verify_dt0(const unsigned char* tp, const unsigned char* dp, c
     const dim3 grid_rows((unsigned)rows * (unsigned)(greedy ? K + 1 : 2 * K + 1));
 #define TSR_WCASE(N)                                                                         \
   case N:                                                                                    \
-    if (aligned)                                                                             \
-      hipLaunchKernelGGL((verify_rows_kernel<0, N, false, false>), grid_rows, dim3(kBlock), 0, \
-                         s, tp, dp, nullptr, K, V, ragged, kp, ws);                          \
-    else                                                                                     \
-      hipLaunchKernelGGL((verify_rows_kernel<0, N, true, false>), grid_rows, dim3(kBlock), 0,  \
-                         s, tp, dp, nullptr, K, V, ragged, kp, ws);                          \
+    hipLaunchKernelGGL((verify_rows_kernel<0, N, false>), grid_rows, dim3(kBlock), 0, s, tp, dp, \
+                       nullptr, K, V, ragged, kp, ws);                                       \
     break;
     switch (ncw) {
       TSR_VERIFY_WIDE_NCS(TSR_WCASE)
@@ -33,22 +29,18 @@ hipError_t launch_verify_dt0(const unsigned char* tp, const unsigned char* dp, c
     wf.nseq = rows;
     const int S = greedy ? 1 : (need + kSliceRows - 1) / kSliceRows;
     hipLaunchKernelGGL((verify_finish_kernel<0>), dim3((unsigned)rows * (unsigned)S), dim3(kBlock),
-                       0, s, tp, dp, xs, K, V, aligned, kp, wf, out_tokens, out_acc, out_status);
+                       0, s, tp, dp, xs, K, V, kp, wf, out_tokens, out_acc, out_status);
     if (!greedy)
-      hipLaunchKernelGGL((verify_draw_kernel<0>), dim3(rows), dim3(kBlock), 0, s, tp, dp, K, V,
-                         aligned, kp, wf, out_tokens);
+      hipLaunchKernelGGL((verify_draw_kernel<0>), dim3(rows), dim3(kBlock), 0, s, tp, dp, K, V, kp,
+                         wf, out_tokens);
     return hipGetLastError();
   }
   const int nc = pick_nc(need, kVerifyNcs, 5);
   const dim3 grid((unsigned)rows * (unsigned)(K + 1));
 #define TSR_CASE(N)                                                                          \
   case N:                                                                                    \
-    if (aligned)                                                                             \
-      hipLaunchKernelGGL((verify_kernel<0, N, false>), grid, dim3(kBlock), 0, s, tp, dp, xs,  \
-                         K, V, aligned, ragged, kp, ws, out_tokens, out_acc, out_status);    \
-    else                                                                                     \
-      hipLaunchKernelGGL((verify_kernel<0, N, true>), grid, dim3(kBlock), 0, s, tp, dp, xs,   \
-                         K, V, aligned, ragged, kp, ws, out_tokens, out_acc, out_status);    \
+    hipLaunchKernelGGL((verify_kernel<0, N>), grid, dim3(kBlock), 0, s, tp, dp, xs, K, V, ragged, \
+                       kp, ws, out_tokens, out_acc, out_status);                             \
     break;
   switch (nc) {
     TSR_VERIFY_NCS(TSR_CASE)
@@ -60,7 +52,7 @@ hipError_t launch_verify_dt0(const unsigned char* tp, const unsigned char* dp, c
 
 hipError_t launch_tree_dt0(const unsigned char* tp, const unsigned char* dp,
                            const int32_t* parent, const int32_t* tokens, int rows, int N, int V,
-                           int aligned, int ragged, const KParams& kp, const VerifyWs& ws,
+                           int ragged, const KParams& kp, const VerifyWs& ws,
                            int32_t* out_tokens, int32_t* out_path, int32_t* out_acc,
                            int32_t* out_status, hipStream_t s) {
   const int need = chunks_per_thread(0, V);
@@ -71,12 +63,8 @@ hipError_t launch_tree_dt0(const unsigned char* tp, const unsigned char* dp,
     const dim3 grid_rows((unsigned)rows * (unsigned)(greedy ? N : 2 * N));
 #define TSR_WCASE(N_)                                                                        \
   case N_:                                                                                   \
-    if (aligned)                                                                             \
-      hipLaunchKernelGGL((verify_rows_kernel<0, N_, false, true>), grid_rows, dim3(kBlock), 0, \
-                         s, tp, dp, parent, N, V, ragged, kp, ws);                           \
-    else                                                                                     \
-      hipLaunchKernelGGL((verify_rows_kernel<0, N_, true, true>), grid_rows, dim3(kBlock), 0,  \
-                         s, tp, dp, parent, N, V, ragged, kp, ws);                           \
+    hipLaunchKernelGGL((verify_rows_kernel<0, N_, true>), grid_rows, dim3(kBlock), 0, s, tp, dp, \
+                       parent, N, V, ragged, kp, ws);                                        \
     break;
     switch (ncw) {
       TSR_VERIFY_WIDE_NCS(TSR_WCASE)
@@ -84,21 +72,15 @@ hipError_t launch_tree_dt0(const unsigned char* tp, const unsigned char* dp,
     }
 #undef TSR_WCASE
     hipLaunchKernelGGL((tree_finish_kernel<0>), dim3(rows), dim3(kBlock), 0, s, tp, dp, parent,
-                       tokens, N, V, aligned, kp, ws, out_tokens, out_path, out_acc, out_status);
+                       tokens, N, V, kp, ws, out_tokens, out_path, out_acc, out_status);
     return hipGetLastError();
   }
   const int nc = pick_nc(need, kVerifyNcs, 5);
   const dim3 grid((unsigned)rows * (unsigned)N);
 #define TSR_CASE(N_)                                                                         \
   case N_:                                                                                   \
-    if (aligned)                                                                             \
-      hipLaunchKernelGGL((tree_kernel<0, N_, false>), grid, dim3(kBlock), 0, s, tp, dp,     \
-                         parent, tokens, N, V, ragged, kp, ws, out_tokens, out_path, out_acc, \
-                         out_status);                                                        \
-    else                                                                                     \
-      hipLaunchKernelGGL((tree_kernel<0, N_, true>), grid, dim3(kBlock), 0, s, tp, dp,      \
-                         parent, tokens, N, V, ragged, kp, ws, out_tokens, out_path, out_acc, \
-                         out_status);                                                        \
+    hipLaunchKernelGGL((tree_kernel<0, N_>), grid, dim3(kBlock), 0, s, tp, dp, parent, tokens, N, \
+                       V, ragged, kp, ws, out_tokens, out_path, out_acc, out_status);        \
     break;
   switch (nc) {
     TSR_VERIFY_NCS(TSR_CASE)

@@ -114,23 +114,23 @@ int max_vocab_sample(int dtype);
 int max_vocab_verify(int dtype);          // with the row records (wide rows)
 int max_vocab_verify_narrow(int dtype);   // without them
 
-// aligned: every row starts on a 16-byte boundary. ragged: a row does not
-// split into whole 16-byte chunks (vocab not a multiple of 4 / 8, or unaligned).
+// ragged: a row does not split into whole 16-byte chunks (vocab not a
+// multiple of 4 / 8). Rows may start at any element boundary.
 hipError_t launch_greedy(const void* logits, int dtype, int rows, int V, long long stride_bytes,
-                         int aligned, int ragged, int32_t* out, int32_t* status, hipStream_t s);
+                         int ragged, int32_t* out, int32_t* status, hipStream_t s);
 hipError_t launch_sample(const void* logits, int dtype, int rows, int V, long long stride_bytes,
-                         int aligned, int ragged, const KParams& kp, int32_t* out,
+                         int ragged, const KParams& kp, int32_t* out,
                          const DiagPtrs& dg, hipStream_t s);
 hipError_t launch_verify(const void* tgt, const void* dft, int dtype, const int32_t* xs,
-                         int rows, int K, int V, int aligned, int ragged, const KParams& kp,
+                         int rows, int K, int V, int ragged, const KParams& kp,
                          const VerifyWs& ws, int32_t* out_tokens, int32_t* out_acc,
                          int32_t* out_status, hipStream_t s);
 hipError_t launch_tree(const void* tgt, const void* dft, int dtype, const int32_t* parent,
-                       const int32_t* tokens, int rows, int N, int V, int aligned, int ragged,
+                       const int32_t* tokens, int rows, int N, int V, int ragged,
                        const KParams& kp, const VerifyWs& ws, int32_t* out_tokens,
                        int32_t* out_path, int32_t* out_acc, int32_t* out_status, hipStream_t s);
 hipError_t launch_beam(const void* logits, int dtype, int groups, int beam, int V,
-                       long long stride_bytes, int aligned, int ragged, const double* scores, BeamWs ws,
+                       long long stride_bytes, int ragged, const double* scores, BeamWs ws,
                        int32_t* out_parent, int32_t* out_tok, double* out_score,
                        int32_t* out_status, hipStream_t s);
 int max_vocab_beam(int dtype);

@@ -348,7 +348,7 @@ __device__ __forceinline__ Cut reg_general(const RegRow<DT, NC>& r, float M, flo
 template <int DT, int NC>
 __global__ __launch_bounds__(kBlock) void greedy_kernel(const unsigned char* logits,
                                                         long long stride_bytes, int V,
-                                                        int aligned, int ragged, int32_t* out,
+                                                        int ragged, int32_t* out,
                                                         int32_t* status) {
   Lds& L = tsr_lds;
   TSR_TRACE_INIT(nullptr);
@@ -367,11 +367,10 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel(const unsigned char* log
 template <int DT>
 __global__ __launch_bounds__(kBlock) void greedy_kernel_stream(const unsigned char* logits,
                                                                long long stride_bytes, int V,
-                                                               int aligned, int32_t* out,
-                                                               int32_t* status) {
+                                                               int32_t* out, int32_t* status) {
   TSR_TRACE_INIT(nullptr);
   const int row = blockIdx.x;
-  const StreamRow<DT> s(logits + (long long)row * stride_bytes, V, aligned != 0);
+  const StreamRow<DT> s(logits + (long long)row * stride_bytes, V);
   const StreamStats st = stream_stats(s, false, 1.0f);
   int tok = -1;
   if (st.status == 0) tok = stream_argmax(s, st.M);
@@ -385,11 +384,11 @@ __global__ __launch_bounds__(kBlock) void greedy_kernel_stream(const unsigned ch
 
 // The streaming view of row `row` (for the streaming finish and the
 // diagnostics), with the allowed-token mask (EXT 1) and the repetition
-// penalty (EXT 1 or 2, when asked for); EXT 3 rows are not 16-byte aligned.
+// penalty (EXT 1 or 2, when asked for).
 template <int DT, int EXT>
 __device__ __forceinline__ StreamRow<DT> row_stream_view(const unsigned char* p, int V,
                                                          const KParams& kp, int row) {
-  return StreamRow<DT>(p, V, EXT != 3,
+  return StreamRow<DT>(p, V,
                        EXT == 1 ? kp.allowed + (long long)row * kp.allowed_stride : nullptr,
                        ((EXT == 1 || EXT == 2) && (kp.flags & F_REP)) ? kp.hist_len : 0,
                        kp.rpen);
@@ -401,20 +400,18 @@ __device__ __forceinline__ StreamRow<DT> row_stream_view(const unsigned char* p,
 // a small top-k, so the common instance keeps its registers and code size.
 // EXT 1: an allowed-token bitmask applies (constrained decoding), its words
 // read into registers ahead of the row and applied in pass A, and a
-// repetition penalty may (F_REP); EXT 2: a repetition penalty applies; EXT 3:
-// rows that do not start on a 16-byte boundary (an odd row stride), read in
-// dwords into the same registers.
-// The bf16 instances of EXT 1-3 are WIDE.
+// repetition penalty may (F_REP); EXT 2: a repetition penalty applies.
+// The bf16 instances of EXT 1-2 are WIDE.
 template <int DT, int NC, bool WIDE, int EXT>
 __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* logits,
                                                         long long stride_bytes, int V,
-                                                        int aligned, int ragged, KParams kp0,
+                                                        int ragged, KParams kp0,
                                                         int32_t* out, DiagPtrs dg) {
   constexpr int EPC = Fmt<DT>::EPC;
   Lds& L = tsr_lds;
   const int row = blockIdx.x;
   const unsigned char* p = logits + (long long)row * stride_bytes;
-  constexpr bool MASK = EXT == 1, REP = EXT == 1 || EXT == 2, UNAL = EXT == 3;
+  constexpr bool MASK = EXT == 1, REP = EXT == 1 || EXT == 2;
   KParams kp = kp0;
 #if TSR_TRACE
   TSR_TRACE_INIT(kp0.trace);
@@ -435,7 +432,7 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
   }
   MaskRegs<DT, NC> mk;
   if constexpr (MASK) mk.load(kp.allowed + (long long)row * kp.allowed_stride, V);
-  r.template load<UNAL>(p, V, ragged != 0);
+  r.load(p, V, ragged != 0);
   const bool greedy = (kp.flags & F_GREEDY) != 0;
   const double u = draw_uniform(kp, (uint32_t)row, 0u, 0u, 0);
   asm volatile("" ::"s"(u));   // the draw's uniform while the loads fly
@@ -503,8 +500,8 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const unsigned char* log
 template <int DT>
 __global__ __launch_bounds__(kBlock) void sample_kernel_stream(const unsigned char* logits,
                                                                long long stride_bytes, int V,
-                                                               int aligned, KParams kp0,
-                                                               int32_t* out, DiagPtrs dg) {
+                                                               KParams kp0, int32_t* out,
+                                                               DiagPtrs dg) {
   const int row = blockIdx.x;
   const unsigned char* p = logits + (long long)row * stride_bytes;
   KParams kp = kp0;
@@ -523,7 +520,7 @@ __global__ __launch_bounds__(kBlock) void sample_kernel_stream(const unsigned ch
                        hn, V, tsr_lds);
     __syncthreads();
   }
-  const StreamRow<DT> s(p, V, aligned != 0,
+  const StreamRow<DT> s(p, V,
                         (kp.flags & F_MASK) ? kp.allowed + (long long)row * kp.allowed_stride
                                             : nullptr,
                         hn, kp.rpen);
@@ -644,7 +641,7 @@ __device__ __forceinline__ int reg_top_keys(const RegRow<DT, NC>& r, float M, fl
 // lower b first) and writes the group's output.
 template <int DT, int NC>
 __global__ __launch_bounds__(kBlock) void beam_kernel(const unsigned char* logits,
-                                                      long long stride_bytes, int V, int aligned,
+                                                      long long stride_bytes, int V,
                                                       int ragged, int beam, const double* scores,
                                                       BeamWs ws, int32_t* out_parent,
                                                       int32_t* out_tok, double* out_score,
@@ -655,10 +652,7 @@ __global__ __launch_bounds__(kBlock) void beam_kernel(const unsigned char* logit
   const int row = blockIdx.x, g = row / beam;
   const unsigned char* p = logits + (long long)row * stride_bytes;
   RegRow<DT, NC> r;
-  if (aligned)
-    r.load(p, V, ragged != 0);
-  else
-    r.template load<true>(p, V, true);
+  r.load(p, V, ragged != 0);
   const double sb = scores[row];
   // the row's weight sum Z is formed as the chunks land (log p = v - M - ln Z)
   const RowStats st = reg_stats<false, false, true>(r, true, kLog2e, L);
@@ -842,8 +836,7 @@ struct RowCut {
 // need_zs false: a row that only draws from its own p~ (the walk forms the
 // sum), so Z_S is left out where it would take a pass of its own (zs -1).
 template <int DT, int NC>
-__device__ __forceinline__ RowCut verify_row_cut(RegRow<DT, NC>& r, const unsigned char* p,
-                                                 int V, bool aligned, const KParams& kp,
+__device__ __forceinline__ RowCut verify_row_cut(RegRow<DT, NC>& r, int V, const KParams& kp,
                                                  Lds& L, bool need_zs = true) {
   const RowStats st = reg_stats(r, joint_top_p(kp), kp.c, L);
   RowCut rc{st.status, st.M, kPosInf, 0.0};
@@ -866,11 +859,11 @@ __device__ __forceinline__ RowCut verify_row_cut(RegRow<DT, NC>& r, const unsign
   return rc;
 }
 
-template <int DT, int NC, bool UNALIGNED>
+template <int DT, int NC>
 __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt,
                                                         const unsigned char* dft,
                                                         const int32_t* xs, int K, int V,
-                                                        int aligned, int ragged, KParams kp,
+                                                        int ragged, KParams kp,
                                                         VerifyWs ws, int32_t* out_tokens,
                                                         int32_t* out_acc, int32_t* out_status) {
   constexpr int EPC = Fmt<DT>::EPC;
@@ -889,8 +882,8 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt
   const bool greedy = (kp.flags & F_GREEDY) != 0;
   const bool with_draft = !greedy && j < K;
   RegRow<DT, NC> rp, rq;
-  rp.template load<UNALIGNED>(tp, V, ragged != 0);
-  if (with_draft) rq.template load<UNALIGNED>(dp, V, ragged != 0);
+  rp.load(tp, V, ragged != 0);
+  if (with_draft) rq.load(dp, V, ragged != 0);
   asm volatile("" ::: "memory");   // both rows' loads in flight before any use
   int st_t = 0, st_d = 0, acc = 0, tok = -1;
   const int x = j < K ? xs[(long long)b * K + j] : 0;
@@ -904,7 +897,7 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt
     }
   } else {
     // the bonus row (j = K) only draws from p~: no separate kept-mass pass
-    const RowCut cp = verify_row_cut(rp, tp, V, aligned != 0, kp, L, j < K);
+    const RowCut cp = verify_row_cut(rp, V, kp, L, j < K);
     st_t = cp.status;
     const double u0 = draw_uniform(kp, (uint32_t)b, (uint32_t)j, 1u, 0);
     const double u1 = draw_uniform(kp, (uint32_t)b, (uint32_t)j, 1u, 1);
@@ -914,7 +907,7 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt
         tok = walk_regs<NC, EPC>(KeptWeights<DT, NC>{rp, cp.tau, cp.M, kp.c}, u0, L, &zs);
       }
     } else {
-      const RowCut cq = verify_row_cut(rq, dp, V, aligned != 0, kp, L);
+      const RowCut cq = verify_row_cut(rq, V, kp, L);
       st_d = cq.status;
       if (st_t == 0 && st_d == 0 && x_ok) {
         const float lp = load_elem<DT>(tp, x), lq = load_elem<DT>(dp, x);
@@ -990,7 +983,7 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt
 // sequence's last workgroup follows kept children from the root and writes
 // the emitted tokens and the accepted path. The tree (parent ids, tokens) is
 // read by every workgroup; N <= 32.
-template <int DT, int NC, bool UNALIGNED>
+template <int DT, int NC>
 __global__ __launch_bounds__(kBlock) void tree_kernel(const unsigned char* tgt,
                                                       const unsigned char* dft,
                                                       const int32_t* parent, const int32_t* tokens,
@@ -1021,8 +1014,8 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(const unsigned char* tgt,
   const unsigned long long chm = __ballot(ln && lane > 0 && pa == v);
   const bool with_draft = !greedy && chm != 0ull;
   RegRow<DT, NC> rp, rq;
-  rp.template load<UNALIGNED>(tp, V, ragged != 0);
-  if (with_draft) rq.template load<UNALIGNED>(dp, V, ragged != 0);
+  rp.load(tp, V, ragged != 0);
+  if (with_draft) rq.load(dp, V, ragged != 0);
   asm volatile("" ::: "memory");
   int st_t = 0, st_d = 0, kept = -1, tok = -1;
   if (greedy) {
@@ -1035,11 +1028,11 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(const unsigned char* tgt,
     }
   } else {
     // a node without children only draws from p~: no separate kept-mass pass
-    const RowCut cp = verify_row_cut(rp, tp, V, true, kp, L, with_draft);
+    const RowCut cp = verify_row_cut(rp, V, kp, L, with_draft);
     st_t = cp.status;
     RowCut cq{0, 0.0f, kPosInf, 1.0};
     if (with_draft) {
-      cq = verify_row_cut(rq, dp, V, true, kp, L);
+      cq = verify_row_cut(rq, V, kp, L);
       st_d = cq.status;
     }
     if (st_t == 0 && st_d == 0 && !bad_tree && !bad_tok) {

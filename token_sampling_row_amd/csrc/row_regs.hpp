@@ -82,39 +82,31 @@ struct RegRow {
     }
   }
 
-  // Whole chunks of a 16-byte aligned row are 128-bit buffer loads off one
-  // resource whose size is the row's whole chunks, all issued back to back.
-  // The full byte offset of each load goes in its VGPR offset, the part the
-  // hardware checks against the resource size (the scalar offset is not
-  // checked), so chunks at or past `nwhole` are never read: they come back as
-  // zeros and are replaced in pass A of reg_stats (by -inf, or by `tail` for
-  // the partial chunk of a ragged row), and no wait is forced here. UNALIGNED
-  // rows are read in dwords (load_chunk_unaligned).
-  template <bool UNALIGNED = false>
+  // Whole chunks of a row are 128-bit buffer loads off one resource whose
+  // size is the row's whole chunks, all issued back to back. The full byte
+  // offset of each load goes in its VGPR offset, the part the hardware checks
+  // against the resource size (the scalar offset is not checked), so chunks
+  // at or past `nwhole` are never read: they come back as zeros and are
+  // replaced in pass A of reg_stats (by -inf, or by `tail` for the partial
+  // chunk of a ragged row), and no wait is forced here. A row need not start
+  // on a 16-byte boundary (an odd row stride): the HSA runtime runs the GPU in
+  // unaligned access mode, which the compiler assumes for every global access
+  // too, and a 128-bit load at any byte address returns those 16 bytes.
   __device__ __forceinline__ void load(const unsigned char* p, int V, bool ragged) {
-    if constexpr (UNALIGNED) {
-      nwhole = 0x7FFFFFFF;
-      jfull = NC;
-      tail = neg_inf_chunk<DT>();
+    nwhole = V / EPC;
+    jfull = nwhole / kBlock;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(p), (short)0, nwhole * 16, 0x00020000);
+    const int voff = (int)threadIdx.x * 16;
 #pragma unroll
-      for (int j = 0; j < NC; ++j)
-        put(j, load_chunk_unaligned<DT>(p, (long long)j * kBlock + threadIdx.x, V));
-    } else {
-      nwhole = V / EPC;
-      jfull = nwhole / kBlock;
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<unsigned char*>(p), (short)0, nwhole * 16, 0x00020000);
-      const int voff = (int)threadIdx.x * 16;
-#pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        put(j, __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rs, voff + j * kBlock * 16, 0, kLoadNonTemporal)));
-        sched_fence();   // issue in chunk order: pass A waits for them in that order
-      }
-      tail = neg_inf_chunk<DT>();
-      if (ragged && nwhole * EPC < V && (nwhole % kBlock) == (int)threadIdx.x)
-        tail = load_chunk_slow<DT>(p, nwhole, V);
+    for (int j = 0; j < NC; ++j) {
+      put(j, __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rs, voff + j * kBlock * 16, 0, kLoadNonTemporal)));
+      sched_fence();   // issue in chunk order: pass A waits for them in that order
     }
+    tail = neg_inf_chunk<DT>();
+    if (ragged && nwhole * EPC < V && (nwhole % kBlock) == (int)threadIdx.x)
+      tail = load_chunk_slow<DT>(p, nwhole, V);
   }
   // Pass-A fix-up of chunk j (see load): only chunk rows at or past jfull
   // (a uniform test) can hold chunks past the end; the fix is branch-free.

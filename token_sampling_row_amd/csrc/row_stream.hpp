@@ -20,15 +20,14 @@ struct StreamRow {
   const unsigned char* p;
   int V;
   int nct;        // chunks per thread
-  bool aligned;
   const uint32_t* mask;   // the row's allowed-token words, or null
   int hn;                 // look-back window entries published in LDS (0: no penalty)
   double rpen;            // repetition penalty
 
-  __device__ __forceinline__ StreamRow(const unsigned char* p_, int V_, bool aligned_,
+  __device__ __forceinline__ StreamRow(const unsigned char* p_, int V_,
                                        const uint32_t* mask_ = nullptr, int hn_ = 0,
                                        double rpen_ = 1.0)
-      : p(p_), V(V_), aligned(aligned_), mask(mask_), hn(hn_), rpen(rpen_) {
+      : p(p_), V(V_), mask(mask_), hn(hn_), rpen(rpen_) {
     const long long chunks = ((long long)V + EPC - 1) / EPC;
     nct = (int)((chunks + kBlock - 1) / kBlock);
   }
@@ -39,9 +38,13 @@ struct StreamRow {
   __device__ __forceinline__ uint4 chunk(int j) const {
     const long long c = chunk_id(j);
     if (c * EPC >= V) return neg_inf_chunk<DT>();
-    const uint4 t = !aligned                ? load_chunk_unaligned<DT>(p, c, V)
-                    : ((c + 1) * EPC <= V) ? *reinterpret_cast<const uint4*>(p + c * EPC * Fmt<DT>::ESZ)
-                                           : load_chunk_slow<DT>(p, c, V);
+    // a whole chunk is one 16-byte load at whatever alignment the row has
+    // (the unaligned access mode); the partial one is read element-wise
+    uint4 t;
+    if ((c + 1) * EPC <= V)
+      __builtin_memcpy(&t, p + c * EPC * Fmt<DT>::ESZ, sizeof(t));
+    else
+      t = load_chunk_slow<DT>(p, c, V);
     uint4 m = mask ? apply_mask<DT>(t, chunk_mask_bits<DT>(mask, c)) : t;
     if (hn > 0) {   // window tokens in this chunk (the hashed flag first)
       const Lds& L = tsr_lds;

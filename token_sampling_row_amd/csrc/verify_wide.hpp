@@ -215,7 +215,7 @@ __device__ __noinline__ void stream_row_rest(const StreamRow<DT> s, float M, con
 // of sequence b are its N target rows then its N draft rows (a draft row of a
 // node without children, and every draft row at temperature 0, is skipped);
 // else its K + 1 target rows then its K draft rows.
-template <int DT, int NC, bool UNALIGNED, bool TREE>
+template <int DT, int NC, bool TREE>
 __global__ __launch_bounds__(kBlock) void verify_rows_kernel(const unsigned char* tgt,
                                                              const unsigned char* dft,
                                                              const int32_t* parent, int K, int V,
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kBlock) void verify_rows_kernel(const unsigned char
   }
   RowRec* const slot = ws.rec + (long long)b * ws.recs + (is_t ? j : ws.recs / 2 + j);
   RegRow<DT, NC> r;
-  r.template load<UNALIGNED>(p, V, ragged != 0);
+  r.load(p, V, ragged != 0);
   RowRec rec{0.0, 0.0f, kPosInf, 0, -1};
   const RowStats st = reg_stats(r, !greedy && joint_top_p(kp), kp.c, L);
   rec.status = st.status;
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kBlock) void verify_rows_kernel(const unsigned char
         // dead afterwards)
         const FastOut fo = fast_cut(r, V, st.M, st.tmin, st.zlo, kp.c, f, u, L);
         if (!fo.ok) {
-          stream_row_rest<DT>(StreamRow<DT>(p, V, !UNALIGNED), st.M, kp, f, draws, u, slot);
+          stream_row_rest<DT>(StreamRow<DT>(p, V), st.M, kp, f, draws, u, slot);
           return;
         }
         rec.tau = fo.tau;
@@ -318,7 +318,7 @@ constexpr int kPartPos = 2 * kMaxSlices - 1;
 template <int DT>
 __global__ __launch_bounds__(kBlock) void verify_finish_kernel(
     const unsigned char* tgt, const unsigned char* dft, const int32_t* xs, int K, int V,
-    int aligned, KParams kp, VerifyWs ws, int32_t* out_tokens, int32_t* out_acc,
+    KParams kp, VerifyWs ws, int32_t* out_tokens, int32_t* out_acc,
     int32_t* out_status) {
   Lds& L = tsr_lds;
   TSR_TRACE_INIT(nullptr);
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(kBlock) void verify_finish_kernel(
   }
   if (!pending) return;
   const RowRec tn{L.sd[0], L.sf[0], L.sf[1], 0, -1}, dn{L.sd[1], L.sf[2], L.sf[3], 0, -1};
-  const StreamRow<DT> sp(tgt + ((long long)b * (K + 1) + n) * rowbytes, V, aligned != 0);
+  const StreamRow<DT> sp(tgt + ((long long)b * (K + 1) + n) * rowbytes, V);
   const float c = kp.c;
   const int j0 = sl * kSliceRows, j1 = min(j0 + kSliceRows, sp.nct);
   double pr = 0.0, pp = 0.0;
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(kBlock) void verify_finish_kernel(
     });
   } else {
     // this slice's two sums: the residual's and p~'s (unnormalised) weight
-    const StreamRow<DT> sq(dft + ((long long)b * K + n) * rowbytes, V, aligned != 0);
+    const StreamRow<DT> sq(dft + ((long long)b * K + n) * rowbytes, V);
     const float izp = (float)(1.0 / tn.zs), izq = (float)(1.0 / dn.zs);
     stream2<DT, kSliceRows>(sp, sq, j0, j1, [&](int, const float* a, const float* q) {
       float fr = 0.0f, fp = 0.0f;
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(kBlock) void verify_finish_kernel(
 // draw from p~ of target row K with w0 of position K.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void verify_draw_kernel(
-    const unsigned char* tgt, const unsigned char* dft, int K, int V, int aligned, KParams kp,
+    const unsigned char* tgt, const unsigned char* dft, int K, int V, KParams kp,
     VerifyWs ws, int32_t* out_tokens) {
   Lds& L = tsr_lds;
   TSR_TRACE_INIT(nullptr);
@@ -448,10 +448,9 @@ __global__ __launch_bounds__(kBlock) void verify_draw_kernel(
   const long long rowbytes = (long long)V * Fmt<DT>::ESZ;
   const RowRec tn = ws.rec[(long long)b * ws.recs + n];
   const RowRec dn = bonus ? tn : ws.rec[(long long)b * ws.recs + ws.recs / 2 + n];
-  const StreamRow<DT> sp(tgt + ((long long)b * (K + 1) + n) * rowbytes, V, aligned != 0);
+  const StreamRow<DT> sp(tgt + ((long long)b * (K + 1) + n) * rowbytes, V);
   const StreamRow<DT> sq = bonus ? sp
-                                 : StreamRow<DT>(dft + ((long long)b * K + n) * rowbytes, V,
-                                                 aligned != 0);
+                                 : StreamRow<DT>(dft + ((long long)b * K + n) * rowbytes, V);
   const int S = (sp.nct + kSliceRows - 1) / kSliceRows;
   if (tid < kWave) {
     const bool in = lane < S;
@@ -500,7 +499,7 @@ __global__ __launch_bounds__(kBlock) void verify_draw_kernel(
 template <int DT>
 __global__ __launch_bounds__(kBlock) void tree_finish_kernel(
     const unsigned char* tgt, const unsigned char* dft, const int32_t* parent,
-    const int32_t* tokens, int N, int V, int aligned, KParams kp, VerifyWs ws,
+    const int32_t* tokens, int N, int V, KParams kp, VerifyWs ws,
     int32_t* out_tokens, int32_t* out_path, int32_t* out_acc, int32_t* out_status) {
   Lds& L = tsr_lds;
   TSR_TRACE_INIT(nullptr);
@@ -551,7 +550,7 @@ __global__ __launch_bounds__(kBlock) void tree_finish_kernel(
         const RowRec d = rd[v];
         const unsigned char* tp = tgt + ((long long)b * N + v) * rowbytes;
         const unsigned char* dp = dft + ((long long)b * N + v) * rowbytes;
-        const StreamRow<DT> sp(tp, V, aligned != 0), sq(dp, V, aligned != 0);
+        const StreamRow<DT> sp(tp, V), sq(dp, V);
         const double izp = 1.0 / t.zs, izq = 1.0 / d.zs;
         // p_1 = p~_v; after k rejections p_{k+1} = max(0, p_k - q~) / Z_k (L.tz)
         int k = 0;
