@@ -17,7 +17,7 @@ constexpr int kWaveCap = 64;  // candidates resolved by one wavefront without ba
 constexpr int kBins = 1024;   // bins of every histogram level
 constexpr int kLogRes = 16;   // log-probability bins per unit of log2(p / p_max)
 constexpr int kWalkBatch = 40;  // chunk rows per step of the inverse-CDF walk
-constexpr int kWalkLds = 16;    // up to this many chunk rows per thread the walk keeps every thread's sums in LDS
+constexpr int kWalkLds = 16;    // up to this many chunk rows per thread the walk's per-thread sums share the LDS union
 constexpr int kWaves = kBlock / kWave;
 constexpr int kVRes = 32;        // bf16 value histogram: bins per logit below the max
 constexpr int kVBins = 1024;     //   bins (32 logits)
@@ -41,7 +41,7 @@ struct Lds {
     uint32_t vcnt[kVCopies * kVStride];   // bf16 value histogram: per-copy counts
     unsigned long long own[kBlock];       // per thread: window entries in its chunks (after pass A)
     double jrow[kWalkBatch][kWaves * 4];  // walk: per (chunk row, 16-lane row) sums
-    float wsum[kWalkLds][kBlock];         // walk (rows of <= kWalkLds chunk rows): per (chunk row, thread) sums
+    float wsum[kWalkLds][kBlock];         // walk: per (chunk row, thread) sums (wider rows: walk_sums)
   };
   uint32_t hcnt[kBins];             // histogram counts
   unsigned long long hmass[kBins];  // histogram masses, fixed point 2^-40
