@@ -117,9 +117,10 @@ def test_sample_strided_and_unaligned():
                                      ("bf16", 128255), ("bf16", 151935), ("bf16", 160001)])
 def test_sample_unaligned_contiguous(dtype, V):
     """A contiguous batch of an odd vocabulary: rows start on every 2- or
-    4-byte offset, so they are read element-wise into the register rows (the
-    last case is wider than the register file and streams); narrow and wide
-    kept sets, no filter and greedy, against the oracle on every row."""
+    4-byte offset and are read with 16-byte loads at that alignment into the
+    register rows (the last case is wider than the register file and
+    streams); narrow and wide kept sets, no filter and greedy, against the
+    oracle on every row."""
     rng = np.random.default_rng(V + (7 if dtype == "bf16" else 0))
     rows = [-a * np.log(rng.permutation(V) + 1.0) + rng.normal(0, 0.5, V)
             for a in np.linspace(0.2, 1.4, 11)]
