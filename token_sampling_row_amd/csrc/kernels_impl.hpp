@@ -217,27 +217,101 @@ __device__ __forceinline__ Cut bf16_value_cut(const RegRow<1, NC>& r, float M, f
   }
   if (ninf) atomicSub(&cnt[kVBins - 1], ninf);
   __syncthreads();
-  double zt = 0.0;
-  for (int b = tid; b < kVBins; b += kBlock) {
+  // the bin totals and the boundary in one block pass: thread t owns bins 2t
+  // and 2t + 1, and a block scan of (count, fixed-point mass) in bin order
+  // gives Z exactly and each bin what lies above it; the boundary rule is
+  // find_boundary's (nothing above the bins, the row max among them)
+  static_assert(kVBins == 2 * kBlock, "two bins per thread");
+  const int lane = __lane_id(), wid = tid / kWave;
+  uint32_t nb[2];
+  unsigned long long mb[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int b = 2 * tid + q;
     uint32_t n = 0u;
 #pragma unroll
-    for (int q = 0; q < kVCopies; ++q) n += L.vcnt[q * kVStride + b];
+    for (int k = 0; k < kVCopies; ++k) n += L.vcnt[k * kVStride + b];
     L.hcnt[hslot(b)] = n;
+    unsigned long long mm = L.hmass[hslot(b)];
     if (n && pure(b)) {
       // the bin's one value: M - b/32 (exact) rounded down to the bf16 grid
       const uint32_t x = __float_as_uint(M - (float)b * (1.0f / kVRes));
       const uint32_t xv = (x & 0xFFFFu) == 0u ? x
                           : ((x >> 31) ? (x & 0xFFFF0000u) + 0x10000u : (x & 0xFFFF0000u));
       const double m = (double)n * (double)weight(__uint_as_float(xv), M, c);
-      L.hmass[hslot(b)] = (unsigned long long)(m * kFix + 0.5);
+      mm = (unsigned long long)(m * kFix + 0.5);
+      L.hmass[hslot(b)] = mm;
     }
-    zt += (double)L.hmass[hslot(b)] * kInvFix;
+    nb[q] = n;
+    mb[q] = mm;
   }
-  const double Z = block_sum<kBlock>(zt, L.bs);
+  const int tc = (int)(nb[0] + nb[1]);
+  const unsigned long long tm = mb[0] + mb[1];
+  const int ic = wave_incl_scan(tc);
+  const unsigned long long im = wave_incl_scan(tm);
+  if (lane == kWave - 1) {
+    L.bs.i[wid] = ic;
+    L.bs.q[wid] = im;
+  }
+  __syncthreads();
+  int cbefore = 0, call = 0;
+  unsigned long long mbefore = 0ull, mall = 0ull;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int tcw = L.bs.i[w];
+    const unsigned long long tmw = L.bs.q[w];
+    cbefore += w < wid ? tcw : 0;
+    mbefore += w < wid ? tmw : 0ull;
+    call += tcw;
+    mall += tmw;
+  }
+  const double Z = (double)mall * kInvFix;
   const double thr = f.p_on ? f.top_p * Z : 0.0;
-  int add_c = 0;
-  double add_m = 0.0;
-  const int d = find_boundary(L, 0, 0.0, f, thr, true, &add_c, &add_m);
+  const int ex_c = cbefore + ic - tc;
+  const unsigned long long ex_m = mbefore + im - tm;
+  int first = kBins, dk = kBins, dp = -1;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int b = 2 * tid + q;
+    const int rc = ex_c + (q ? (int)nb[0] : 0);
+    const unsigned long long rm = ex_m + (q ? mb[0] : 0ull);
+    if (nb[q]) {
+      first = min(first, b);
+      if (f.k_on && dk == kBins && rc + (int)nb[q] >= f.k) dk = b;
+      if (f.p_on && (double)rm * kInvFix < thr) dp = b;
+    }
+  }
+  first = wave_min(first);
+  dk = wave_min(dk);
+  dp = wave_max(dp);
+  if (lane == 0) {
+    L.bs.u[wid] = (uint32_t)first;
+    L.bs.f[wid] = (float)dk;
+    L.bs.d[wid] = (double)dp;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    first = min(first, (int)L.bs.u[w]);
+    dk = min(dk, (int)L.bs.f[w]);
+    dp = max(dp, (int)L.bs.d[w]);
+  }
+  if (f.p_on) dp = max(dp, first);
+  int d = kBins;
+  if (f.k_on) d = min(d, dk);
+  if (f.p_on) d = min(d, dp < 0 ? kBins : dp);
+  int add_c = call;
+  double add_m = (double)mall * kInvFix;
+  if (d < kBins) {   // what lies above bin d, from its owner's prefix
+    if (tid == (d >> 1)) {
+      L.si[5] = ex_c + ((d & 1) ? (int)nb[0] : 0);
+      L.sd[5] = (double)(ex_m + ((d & 1) ? mb[0] : 0ull)) * kInvFix;
+    }
+    __syncthreads();
+    add_c = L.si[5];
+    add_m = L.sd[5];
+  }
+  __syncthreads();
   *ok = true;
   Cut cut;
   const float floor_m = f.tau_m > kNegInf ? f.tau_m : -kFltMax;
