@@ -83,7 +83,9 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, kernel_prefix: 
         kern = [i for i, r in enumerate(rows) if r["Kernel_Name"].removeprefix("void ").startswith(kernel_prefix)]
         if not kern:
             raise SystemExit(f"no {kernel_prefix} dispatch in {path}")
-        calib = [float(r["Counter_Value"]) for r in rows[kern[-1] + 1:] if "copyBuffer" in r["Kernel_Name"]]
+        # the 256 MiB copies only (a small copy of a result may follow the kernel)
+        calib = [float(r["Counter_Value"]) for r in rows[kern[-1] + 1:]
+                 if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) > CALIB_BYTES / 1024.0 / 100]
         if not calib:
             raise SystemExit(f"no calibration copies after the sampler dispatches in {path}")
         factor = (CALIB_BYTES / 1024.0) / (sum(calib) / len(calib))
