@@ -314,6 +314,44 @@ def test_general_path_wide_supports(V, dtype):
             compare(got, refs, list(range(len(rows))), values)
 
 
+@pytest.mark.parametrize("V", [70001, 151936])
+def test_topk_chunk_max_bound_bf16(V):
+    """Top-k alone on bf16 rows held in registers with k above the candidate
+    sketch (the value histogram counts only bins at or above the k-th largest
+    chunk maximum): flat rows, heavy ties at the boundary, -inf holes, rows
+    of one or two tie groups, and k at and past the bound's limit (eight
+    chunk maxima per thread)."""
+    rng = np.random.default_rng(V + 11)
+    rows = [rng.normal(0, 0.3, V),
+            np.round(rng.normal(0, 0.3, V), 1),                           # large tie groups
+            -np.log(rng.permutation(V) + 1.0) + rng.normal(0, 0.5, V),
+            rng.normal(-12.0, 1.5, V),
+            np.concatenate([np.zeros(V // 2), np.full(V - V // 2, -0.001)]),
+            np.zeros(V)]
+    holes = -np.log(rng.permutation(V) + 1.0) + rng.normal(-6.0, 0.5, V)
+    holes[rng.random(V) < 0.3] = -np.inf
+    rows.append(holes)
+    sparse = np.full(V, -np.inf)
+    sparse[rng.choice(V, 1500, replace=False)] = rng.normal(0, 1, 1500)   # fewer finite than k
+    rows.append(sparse)
+    data = wl.f32_to_bf16_bits(np.stack(rows).astype(np.float32))
+    values = vals(data, "bf16")
+    seed = 404
+    nc = -(-V // (8 * 512))
+    grid = [dict(temperature=1.0, top_k=129), dict(temperature=1.5, top_k=1024),
+            dict(temperature=0.7, top_k=nc * 64), dict(temperature=1.0, top_k=nc * 64 + 1),
+            dict(temperature=1.0, top_k=700, min_p=0.01)]
+    tally = Tally()
+    with make_sampler(seed) as s:
+        x = to_dev(data, "bf16")
+        for i, prm in enumerate(grid):
+            print_case("topk_bound", V=V, params=prm)
+            refs = [oracle.sample_row(values[b], prm, seed, b, i) for b in range(len(rows))]
+            got = run_sample(s, x, prm, i, diag=True, probs=True)
+            compare(got, refs, list(range(len(rows))), values, tally=tally)
+    report(f"top-k bound V={V}", tally)
+
+
 def test_bad_rows_and_status(sampler):
     V = 5000
     rng = np.random.default_rng(2)
