@@ -192,8 +192,7 @@ __device__ __forceinline__ Cut bf16_value_cut(const RegRow<1, NC>& r, float M, f
   // [bneg, kVBins - 2], or every bin at or below bpos, means none is there; a
   // chunk holding -inf reaches the last bin and so takes the per-element test)
   uint32_t ninf = 0u;
-#pragma unroll 1
-  for (int j = 0; j < NC; ++j) {
+  auto count = [&](int j) {
     float v[EPC];
     r.elems(j, v);
     int b[EPC];
@@ -214,7 +213,12 @@ __device__ __forceinline__ Cut bf16_value_cut(const RegRow<1, NC>& r, float M, f
         if (fin & !pure(b[e])) atomicAdd(&L.hmass[hslot(b[e])], to_fixed(weight(v[e], M, c)));
       }
     }
-  }
+  };
+  // chunk rows past the 32nd at fixed register indices
+  constexpr int kDyn = NC > 32 ? 32 : NC;
+#pragma unroll 1
+  for (int j = 0; j < kDyn; ++j) count(j);
+  static_for<kDyn, NC>([&](auto jc) { count(decltype(jc)::value); });
   if (ninf) atomicSub(&cnt[kVBins - 1], ninf);
   __syncthreads();
   // the bin totals and the boundary in one block pass: thread t owns bins 2t

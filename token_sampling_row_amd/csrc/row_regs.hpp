@@ -470,15 +470,20 @@ __device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* tota
   static_assert(NC <= kWave, "one lane per chunk row in the search");
   const int tid = threadIdx.x, lane = __lane_id(), wid = tid / kWave;
   float (*wsum)[kBlock] = walk_sums<NC>(L);
-#pragma unroll 2
-  for (int j = 0; j < NC; ++j) {
+  auto weigh = [&](int j) {
     float w[EPC];
     cw(j, w);
     float sf = 0.0f;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) sf += w[e];
     wsum[j][tid] = sf;
-  }
+  };
+  // chunk rows past the 32nd at fixed register indices (a run-time index
+  // there takes a select chain per chunk)
+  constexpr int kDyn = NC > 32 ? 32 : NC;
+#pragma unroll 2
+  for (int j = 0; j < kDyn; ++j) weigh(j);
+  static_for<kDyn, NC>([&](auto jc) { weigh(decltype(jc)::value); });
   __syncthreads();
   // chunk row totals: wavefront w adds rows w, w + 8, ... (8 sums per lane)
   for (int j = wid; j < NC; j += kWaves) {
