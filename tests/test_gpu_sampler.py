@@ -352,6 +352,43 @@ def test_topk_chunk_max_bound_bf16(V):
     report(f"top-k bound V={V}", tally)
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 151937), ("bf16", 155647), ("f32", 77823),
+                                     ("f32", 65537)])
+def test_widest_register_rows_ragged(dtype, V):
+    """Rows of 33 to 38 chunk rows per thread whose vocabulary ends inside a
+    16-byte chunk: the chunk rows past the 32nd sit at fixed register indices
+    and the last chunk is partial; every filter family and the unfiltered
+    walk."""
+    rng = np.random.default_rng(V * 3 + (1 if dtype == "bf16" else 0))
+    rows = [-np.log(rng.permutation(V) + 1.0) + rng.normal(0, 0.5, V),
+            rng.normal(0, 0.3, V),
+            np.round(rng.normal(-6, 1.0, V), 1)]
+    tail = rng.normal(-20, 1, V)
+    tail[-3:] = 5.0                                   # the maximum in the partial last chunk
+    rows.append(tail)
+    holes = rng.normal(0, 1, V)
+    holes[rng.random(V) < 0.4] = -np.inf
+    rows.append(holes)
+    data = np.stack(rows).astype(np.float32)
+    if dtype == "bf16":
+        data = wl.f32_to_bf16_bits(data)
+    values = vals(data, dtype)
+    seed = 515
+    grid = [dict(temperature=1.0), dict(temperature=1.5, top_p=0.9),
+            dict(temperature=1.5, top_k=1024), dict(temperature=0.9, top_k=50, top_p=0.95, min_p=0.1),
+            dict(temperature=0.0)]
+    tally = Tally()
+    with make_sampler(seed) as s:
+        x = to_dev(data, dtype)
+        for i, prm in enumerate(grid):
+            print_case("widest_ragged", dtype=dtype, V=V, params=prm)
+            refs = [oracle.sample_row(values[b], prm, seed, b, i) for b in range(len(rows))]
+            got = run_sample(s, x, prm, i, diag=True, probs=True)
+            compare(got, refs, list(range(len(rows))), values, greedy=prm["temperature"] == 0.0,
+                    tally=tally)
+    report(f"widest ragged V={V} {dtype}", tally)
+
+
 def test_bad_rows_and_status(sampler):
     V = 5000
     rng = np.random.default_rng(2)
