@@ -485,13 +485,37 @@ __device__ __forceinline__ int walk_regs(CW&& cw, double u, Lds& L, double* tota
   for (int j = 0; j < kDyn; ++j) weigh(j);
   static_for<kDyn, NC>([&](auto jc) { weigh(decltype(jc)::value); });
   __syncthreads();
-  // chunk row totals: wavefront w adds rows w, w + 8, ... (8 sums per lane)
-  for (int j = wid; j < NC; j += kWaves) {
-    double s = 0.0;
+  // chunk row totals: wavefront w adds rows w, w + 8, ... (8 sums per lane),
+  // its rows' chains side by side up to 32 chunk rows (in the 38-chunk-row
+  // instances that costs registers the walk needs: one row at a time there)
+  if constexpr (NC > 32) {
+    for (int j = wid; j < NC; j += kWaves) {
+      double s = 0.0;
 #pragma unroll
-    for (int q = 0; q < kBlock / kWave; ++q) s += (double)wsum[j][lane * (kBlock / kWave) + q];
-    s = wave_sum(s);
-    if (lane == 0) L.jsum[j] = s;
+      for (int q = 0; q < kBlock / kWave; ++q) s += (double)wsum[j][lane * (kBlock / kWave) + q];
+      s = wave_sum(s);
+      if (lane == 0) L.jsum[j] = s;
+    }
+  } else {
+    constexpr int kPer = (NC + kWaves - 1) / kWaves;
+    double s[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int j = wid + i * kWaves;
+      s[i] = 0.0;
+      if (j < NC) {
+#pragma unroll
+        for (int q = 0; q < kBlock / kWave; ++q)
+          s[i] += (double)wsum[j][lane * (kBlock / kWave) + q];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) s[i] = wave_sum(s[i]);
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (wid + i * kWaves < NC) L.jsum[wid + i * kWaves] = s[i];
+    }
   }
   __syncthreads();
   if (tid < kWave) {
