@@ -113,8 +113,9 @@ def test_beam_ties_and_degenerate_rows():
 
 
 def test_beam_repeated_calls_reset_workspace():
-    """The per-group counters and flags are left at zero: a second call (with
-    a NaN group the first time) gives the same answers as a fresh handle."""
+    """Nothing of an earlier call reaches a later one's merge: after a call
+    with a NaN group, two calls on clean logits give the same answers and
+    every group status 0."""
     rng = np.random.default_rng(7)
     V, beam, groups = 5000, 8, 32
     data = beam_rows(groups, beam, V, "f32", rng)

@@ -63,7 +63,7 @@ def instance_units() -> dict[str, str]:
                     f"template __global__ void sample_kernel<{dt}, {nc}, {wide}, {ext}>" + sample_args)
             units[f"i_beam_{dt}_{nc}.hip"] = head + (
                 f"template __global__ void beam_kernel<{dt}, {nc}>(const unsigned char*, long long, "
-                "int, int, int, const double*, BeamWs, int32_t*, int32_t*, double*, int32_t*);\n}\n")
+                "int, int, int, const double*, BeamWs);\n}\n")
             units[f"i_greedy_{dt}_{nc}.hip"] = head + (
                 f"template __global__ void greedy_kernel<{dt}, {nc}>(const unsigned char*, "
                 "long long, int, int, int32_t*, int32_t*);\n}\n")

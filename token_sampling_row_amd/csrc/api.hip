@@ -208,8 +208,7 @@ int sampler_init(tsr_handle* out, int device, int max_rows, int max_vocab, int m
     const size_t bslots = (size_t)max_rows * tsr::kBeamMax;
     const size_t rbytes = (size_t)max_rows * 2 * (size_t)(max_k + 1) * sizeof(tsr::RowRec) +
                           (size_t)max_rows * 2 * tsr::kMaxSlices * sizeof(unsigned long long);
-    const size_t bbytes = bslots * (sizeof(double) + sizeof(int32_t)) +
-                          2 * (size_t)max_rows * sizeof(uint32_t);
+    const size_t bbytes = bslots * (sizeof(double) + sizeof(int32_t));
     const size_t bytes = ((vbytes + 7) & ~(size_t)7) + rbytes + bbytes;
     if (hipMalloc(&h->ws_block, bytes) != hipSuccess) return TSR_ENOMEM;
     if (hipMemset(h->ws_block, 0, bytes) != hipSuccess) return TSR_EDEVICE;
@@ -225,12 +224,10 @@ int sampler_init(tsr_handle* out, int device, int max_rows, int max_vocab, int m
     h->ws.rec = (tsr::RowRec*)((char*)h->ws_block + ((vbytes + 7) & ~(size_t)7));
     h->ws.recs = 2 * (max_k + 1);
     h->ws.part = (unsigned long long*)(h->ws.rec + (size_t)max_rows * 2 * (max_k + 1));
-    // beam step: per row kBeamMax (score, token), per group a flag and a counter
+    // beam step: per row kBeamMax (score, token)
     char* bb = (char*)h->ws_block + ((vbytes + 7) & ~(size_t)7) + rbytes;
     h->bws.score = (double*)bb;
     h->bws.tok = (int32_t*)(bb + bslots * sizeof(double));
-    h->bws.bad = (uint32_t*)(bb + bslots * (sizeof(double) + sizeof(int32_t)));
-    h->bws.counter = h->bws.bad + max_rows;
 #if TSR_TRACE
     if (hipMalloc(&h->trace, TSR_TRACE_WORDS * sizeof(uint64_t)) != hipSuccess) return TSR_ENOMEM;
     if (hipMemset(h->trace, 0, TSR_TRACE_WORDS * sizeof(uint64_t)) != hipSuccess) return TSR_EDEVICE;

@@ -38,11 +38,9 @@ constexpr int kVerifyWideNcs[] = {24, 32, 38};
   extern template __global__ void sample_kernel<1, N, true, 1>(TSR_SAMPLE_ARGS);              \
   extern template __global__ void sample_kernel<1, N, true, 2>(TSR_SAMPLE_ARGS);              \
   extern template __global__ void beam_kernel<0, N>(const unsigned char*, long long, int, int,  \
-                                                    int, const double*, BeamWs, int32_t*,    \
-                                                    int32_t*, double*, int32_t*);            \
+                                                    int, const double*, BeamWs);              \
   extern template __global__ void beam_kernel<1, N>(const unsigned char*, long long, int, int,  \
-                                                    int, const double*, BeamWs, int32_t*,    \
-                                                    int32_t*, double*, int32_t*);            \
+                                                    int, const double*, BeamWs);              \
   extern template __global__ void greedy_kernel<0, N>(const unsigned char*, long long, int,  \
                                                       int, int32_t*, int32_t*);               \
   extern template __global__ void greedy_kernel<1, N>(const unsigned char*, long long, int,  \

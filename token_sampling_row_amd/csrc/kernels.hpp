@@ -70,14 +70,12 @@ struct DiagPtrs {
 };
 
 // Per-handle workspace of the beam step: each beam row's best candidates,
-// best first (score, token), kBeamMax per row; per group a bad-input flag and
-// an arrival counter (both zero between calls).
+// best first (score, token), kBeamMax per row, written by the row kernel and
+// merged per group by the kernel that follows it in the stream.
 constexpr int kBeamMax = 16;
 struct BeamWs {
   double* score;
   int32_t* tok;
-  uint32_t* bad;
-  uint32_t* counter;
 };
 
 // What the wide verify path records of one target or draft row: the kept

@@ -714,20 +714,19 @@ __device__ __forceinline__ int reg_top_keys(const RegRow<DT, NC>& r, float M, fl
 
 // One beam-search step [P2 39.1, eq. 39.1 and Listing 39.1]: workgroup row =
 // g * beam + b holds beam b of group g. It writes its best candidates
-// (score s_b + log p_b(i), token), best first, to the workspace; the last of
-// the group's workgroups to arrive merges the beam sorted lists (equal scores:
-// lower b first) and writes the group's output.
+// (score s_b + log p_b(i), token), best first, to the workspace; a
+// one-wavefront kernel per group that follows in the stream (launch_beam)
+// merges the beams' sorted lists (equal scores: lower b first) and writes the
+// group's output.
 template <int DT, int NC>
 __global__ __launch_bounds__(kBlock) void beam_kernel(const unsigned char* logits,
                                                       long long stride_bytes, int V,
                                                       int ragged, int beam, const double* scores,
-                                                      BeamWs ws, int32_t* out_parent,
-                                                      int32_t* out_tok, double* out_score,
-                                                      int32_t* out_status) {
+                                                      BeamWs ws) {
   Lds& L = tsr_lds;
   TSR_TRACE_INIT(nullptr);
   const int tid = threadIdx.x;
-  const int row = blockIdx.x, g = row / beam;
+  const int row = blockIdx.x;
   const unsigned char* p = logits + (long long)row * stride_bytes;
   RegRow<DT, NC> r;
   r.load(p, V, ragged != 0);
@@ -742,8 +741,8 @@ __global__ __launch_bounds__(kBlock) void beam_kernel(const unsigned char* logit
     n = reg_top_keys(r, st.M, st.tmin, beam, L);
   }
   if (tid == 0) {
-    // the row's list, then the arrival (its release orders this thread's
-    // stores before the counter)
+    // the row's list for the group merge that follows in the stream (a bad
+    // row marks its first score NaN, which no other row's list holds)
     for (int q = 0; q < beam; ++q) {
       double sc = (double)kNegInf;
       int tk = -1;
@@ -752,53 +751,11 @@ __global__ __launch_bounds__(kBlock) void beam_kernel(const unsigned char* logit
         sc = sb + ((double)key2f(key_hi(key)) - (double)st.M) - lnz;
         tk = (int)~(uint32_t)key;
       }
+      if (bad && q == 0) sc = __builtin_nan("");
       const long long slot = (long long)row * kBeamMax + q;
-      __hip_atomic_store(&ws.score[slot], sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&ws.tok[slot], tk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ws.score[slot] = sc;
+      ws.tok[slot] = tk;
     }
-    if (bad) __hip_atomic_fetch_or(&ws.bad[g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t prev = __hip_atomic_fetch_add(&ws.counter[g], 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    L.si[0] = prev == (uint32_t)(beam - 1);
-  }
-  __syncthreads();
-  if (!L.si[0] || tid >= kWave) return;
-  // the group's last workgroup, wave 0: the beam lists into LDS at once (one
-  // round trip), then lane b < beam walks beam b's list
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int lane = tid;
-  const long long base = (long long)g * beam * kBeamMax;
-  for (int q = lane; q < beam * kBeamMax; q += kWave) {
-    L.pref[q] = __hip_atomic_load(&ws.score[base + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    L.hcnt[q] = (uint32_t)__hip_atomic_load(&ws.tok[base + q], __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-  }
-  int ptr = 0;
-  auto head = [&](int q) -> double {
-    return (lane < beam && q < beam) ? L.pref[lane * kBeamMax + q] : (double)kNegInf;
-  };
-  double hs = head(0);
-  const bool gbad = __hip_atomic_load(&ws.bad[g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-  int any_finite = 0;
-  for (int q = 0; q < beam; ++q) {
-    const double best = wave_reduce(hs, [](double a, double b) { return a > b ? a : b; });
-    const int w = __ffsll((long long)__ballot(lane < beam && hs == best)) - 1;
-    const long long o = (long long)g * beam + q;
-    if (lane == w) {
-      const bool fin = best > (double)kNegInf;
-      const int tk = fin ? (int)L.hcnt[w * kBeamMax + ptr] : -1;
-      out_parent[o] = gbad ? -1 : (fin ? w : -1);
-      out_tok[o] = gbad ? -1 : tk;
-      out_score[o] = gbad ? __builtin_nan("") : best;
-      ++ptr;
-      hs = head(ptr);
-    }
-    any_finite |= best > (double)kNegInf;
-  }
-  if (lane == 0) {
-    if (out_status) out_status[g] = gbad ? 1 : (any_finite ? 0 : 2);
-    __hip_atomic_store(&ws.bad[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&ws.counter[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
