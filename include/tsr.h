@@ -243,14 +243,12 @@ int spec_verify(tsr_handle h, const void* target_logits, const void* draft_logit
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * No handle: the Philox key is `seed` (as sampler_init's), and the call runs
  * on `device` (made current for the call, the caller's restored after). The
- * verify workspace is a static device array in the library, about 1.1 MB, one
+ * verify workspace is a static device array in the library, 1 MiB, one
  * copy per device, held until the process ends; the call allocates nothing
  * and calls no allocating routine. Limits of that array: rows <= 16384 and
  * rows * (K + 1) <= 65536 (TSR_EINVAL beyond); 1 <= K <= 32; vocab <= 65,536
  * bf16 or 32,768 float32 logits (TSR_EUNSUPPORTED beyond: the array holds no
- * per-row records for spec_verify's wider-row path). The first call on
- * a device also enqueues one small kernel that zeroes the array's counters.
- * Every call on a device shares that device's array: calls that overlap on
+ * per-row records for spec_verify's wider-row path). Every call on a device shares that device's array: calls that overlap on
  * one device (on different streams, or from several threads) race and give
  * undefined results. Arguments, outputs and results are spec_verify's. */
 int spec_verify_noalloc(int device, uint64_t seed, const void* target_logits,

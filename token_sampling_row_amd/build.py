@@ -71,8 +71,7 @@ def instance_units() -> dict[str, str]:
             # two rows per workgroup: no chunk maxima kept in registers
             units[f"i_verify_{dt}_{nc}.hip"] = "#define TSR_ROW_NO_CMAX 1\n" + head + (
                 f"template __global__ void verify_kernel<{dt}, {nc}>(const unsigned char*, "
-                "const unsigned char*, const int32_t*, int, int, int, KParams, VerifyWs, "
-                "int32_t*, int32_t*, int32_t*);\n"
+                "const unsigned char*, const int32_t*, int, int, int, KParams, VerifyWs);\n"
                 f"template __global__ void tree_kernel<{dt}, {nc}>(const unsigned char*, "
                 "const unsigned char*, const int32_t*, const int32_t*, int, int, int, KParams, "
                 "VerifyWs, int32_t*, int32_t*, int32_t*, int32_t*);\n}\n")

@@ -136,13 +136,12 @@ int launch_verify_checked(const void* target_logits, const void* draft_logits, i
 }
 
 // spec_verify_noalloc's workspace: the per-(sequence, position) results (four
-// int32 arrays of kStaticSlots) and the per-sequence arrival counters
-// (kStaticSeqs), in `scratch` below: one copy per device, held until the
-// process ends, shared by every call on that device.
+// int32 arrays of kStaticSlots), in `scratch` below: one copy per device,
+// held until the process ends, shared by every call on that device. Every
+// call writes each slot it reads, so nothing needs clearing.
 constexpr int kStaticSlots = 1 << 16;   // sequences x (K + 1) positions
-constexpr int kStaticSeqs = 1 << 14;    // sequences
-constexpr size_t kStaticBytes =
-    4 * (size_t)kStaticSlots * sizeof(int32_t) + (size_t)kStaticSeqs * sizeof(uint32_t);
+constexpr int kStaticSeqs = 1 << 14;    // sequences per call
+constexpr size_t kStaticBytes = 4 * (size_t)kStaticSlots * sizeof(int32_t);
 constexpr int kMaxDevices = 64;
 std::mutex g_static_mu;
 void* g_static_ptr[kMaxDevices];   // device address of `scratch` on each device, once looked up
@@ -156,17 +155,14 @@ static __device__ __align__(256) unsigned char scratch[kStaticBytes];
 namespace {
 
 // The device address of `scratch` on `device` (the current device), looked up
-// once per device and kept; *fresh is set by the lookup (the counters have not
-// been cleared on this device by this process yet).
-int static_workspace(int device, void** out, bool* fresh) {
-  *fresh = false;
+// once per device and kept.
+int static_workspace(int device, void** out) {
   if (device >= kMaxDevices) return TSR_EUNSUPPORTED;
   std::lock_guard<std::mutex> lock(g_static_mu);
   if (!g_static_ptr[device]) {
     void* p = nullptr;
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TSR_EDEVICE;
     g_static_ptr[device] = p;
-    *fresh = true;
   }
   *out = g_static_ptr[device];
   return TSR_OK;
@@ -403,8 +399,7 @@ int spec_verify_noalloc(int device, uint64_t seed, const void* target_logits,
   const tsr::KParams kp = make_kparams(seed, params, vocab, step, false);
   return on_device(device, [&]() -> int {
     void* base = nullptr;
-    bool fresh = false;
-    const int src = static_workspace(device, &base, &fresh);
+    const int src = static_workspace(device, &base);
     if (src != TSR_OK) return src;
     int32_t* b = (int32_t*)base;
     tsr::VerifyWs ws;
@@ -412,15 +407,11 @@ int spec_verify_noalloc(int device, uint64_t seed, const void* target_logits,
     ws.tok = b + kStaticSlots;
     ws.st_t = b + 2 * kStaticSlots;
     ws.st_d = b + 3 * kStaticSlots;
-    ws.counter = (uint32_t*)(b + 4 * kStaticSlots);
+    ws.counter = nullptr;   // the two-row verify keeps no arrival counters
     ws.kmax1 = K + 1;
     ws.rec = nullptr;   // the array holds no row records: register-pair rows only
     ws.recs = 0;
     ws.part = nullptr;
-    if (fresh) {   // the arrival counters start at zero (each call leaves them at zero)
-      if (tsr::launch_fill_u32(ws.counter, kStaticSeqs, 0u, (hipStream_t)hip_stream) != hipSuccess)
-        return TSR_EDEVICE;
-    }
     return launch_verify_checked(target_logits, draft_logits, dtype, draft_tokens, rows, K, vocab,
                                  kp, ws, out_tokens, out_accepted, out_status, hip_stream);
   });

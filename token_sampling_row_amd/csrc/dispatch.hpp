@@ -48,7 +48,7 @@ constexpr int kVerifyWideNcs[] = {24, 32, 38};
 #define TSR_DECLARE_VERIFY_DT(D, N)                                                           \
   extern template __global__ void verify_kernel<D, N>(                                        \
       const unsigned char*, const unsigned char*, const int32_t*, int, int, int, KParams,      \
-      VerifyWs, int32_t*, int32_t*, int32_t*);                                                 \
+      VerifyWs);                                                                               \
   extern template __global__ void tree_kernel<D, N>(                                          \
       const unsigned char*, const unsigned char*, const int32_t*, const int32_t*, int, int,    \
       int, KParams, VerifyWs, int32_t*, int32_t*, int32_t*, int32_t*);

@@ -40,7 +40,7 @@ hipError_t launch_verify_dt1(const unsigned char* tp, const unsigned char* dp, c
 #define TSR_CASE(N)                                                                          \
   case N:                                                                                    \
     hipLaunchKernelGGL((verify_kernel<1, N>), grid, dim3(kBlock), 0, s, tp, dp, xs, K, V, ragged, \
-                       kp, ws, out_tokens, out_acc, out_status);                             \
+                       kp, ws);                                                               \
     break;
   switch (nc) {
     TSR_VERIFY_NCS(TSR_CASE)

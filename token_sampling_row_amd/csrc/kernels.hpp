@@ -89,8 +89,9 @@ struct RowRec {
   int tok;
 };
 
-// Per-handle workspace of the verify step: per (sequence, position) results
-// and one arrival counter per sequence (zero between calls); for rows wider
+// Per-handle workspace of the verify step: per (sequence, position) results,
+// one arrival counter per sequence for the tree kernel (zero between calls;
+// null where no tree verify runs); for rows wider
 // than two register rows per workgroup, `recs` row records per sequence (its
 // target rows from 0, its draft rows from recs / 2).
 struct VerifyWs {
@@ -134,7 +135,5 @@ hipError_t launch_beam(const void* logits, int dtype, int groups, int beam, int 
 int max_vocab_beam(int dtype);
 hipError_t launch_philox(const uint32_t* ctr, int n, uint32_t k0, uint32_t k1, uint32_t* out,
                          hipStream_t s);
-// p[0, n) = v (a kernel, so it can be captured in a graph).
-hipError_t launch_fill_u32(uint32_t* p, int n, uint32_t v, hipStream_t s);
 
 }  // namespace tsr

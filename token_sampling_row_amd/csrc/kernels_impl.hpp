@@ -899,8 +899,7 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt
                                                         const unsigned char* dft,
                                                         const int32_t* xs, int K, int V,
                                                         int ragged, KParams kp,
-                                                        VerifyWs ws, int32_t* out_tokens,
-                                                        int32_t* out_acc, int32_t* out_status) {
+                                                        VerifyWs ws) {
   constexpr int EPC = Fmt<DT>::EPC;
   Lds& L = tsr_lds;
   TSR_TRACE_INIT(nullptr);
@@ -964,48 +963,12 @@ __global__ __launch_bounds__(kBlock) void verify_kernel(const unsigned char* tgt
       }
     }
   }
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0) {   // the position's results, for the finish kernel
     const int slot = b * ws.kmax1 + j;
-    __hip_atomic_store(&ws.acc[slot], acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&ws.tok[slot], tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&ws.st_t[slot], st_t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&ws.st_d[slot], st_d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t prev = __hip_atomic_fetch_add(&ws.counter[b], 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    L.si[0] = prev == (uint32_t)K;
-  }
-  __syncthreads();
-  if (!L.si[0] || threadIdx.x >= kWave) return;
-  // last of the K+1 workgroups of this sequence, wave 0: every position's
-  // results read at once (lane q: position q), then the output
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int q = threadIdx.x;
-  const int s0 = b * ws.kmax1;
-  const bool inq = q <= K, dq = q < K;
-  const int qt = inq ? __hip_atomic_load(&ws.st_t[s0 + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-  const int qd = dq ? __hip_atomic_load(&ws.st_d[s0 + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-  const int qa = dq ? __hip_atomic_load(&ws.acc[s0 + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1;
-  const int qk = inq ? __hip_atomic_load(&ws.tok[s0 + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -1;
-  const int xq = dq ? xs[(long long)b * K + q] : 0;
-  // status: the target's of the first position that has one, else the
-  // draft's, else a draft token out of range
-  const unsigned long long bt = __ballot(qt != 0), bd = __ballot(qd != 0);
-  const unsigned long long bx = __ballot(dq && (xq < 0 || xq >= V));
-  const int status = bt ? readlane_u32((uint32_t)qt, __ffsll((long long)bt) - 1)
-                        : bd ? readlane_u32((uint32_t)qd, __ffsll((long long)bd) - 1)
-                             : (bx ? 3 : 0);
-  // accepted prefix: up to the first rejection
-  const unsigned long long rej = __ballot(dq && !qa);
-  const int n = rej ? __ffsll((long long)rej) - 1 : K;
-  const int tn = readlane_u32((uint32_t)qk, n);
-  if (inq) {
-    int32_t* o = out_tokens + (long long)b * (K + 1);
-    o[q] = status ? -1 : (q < n ? xq : (q == n ? tn : -1));
-  }
-  if (q == 0) {
-    out_acc[b] = status ? 0 : n;
-    if (out_status) out_status[b] = status;
-    __hip_atomic_store(&ws.counter[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ws.acc[slot] = acc;
+    ws.tok[slot] = tok;
+    ws.st_t[slot] = st_t;
+    ws.st_d[slot] = st_d;
   }
 }
 
