@@ -140,10 +140,27 @@ def _dtype_code(t) -> int:
     raise TypeError(f"logits must be float32 or bfloat16, not {t.dtype}")
 
 
+_raw_stream = None
+
+
+def _current_stream_handle() -> int:
+    """The current device's current stream as a raw handle. torch's C getter
+    returns it without building a Stream object (a few microseconds a call,
+    which bound small batches); the public API where that getter is absent."""
+    global _raw_stream
+    if _raw_stream is None:
+        import torch
+        getter = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        get_dev = getattr(torch._C, "_cuda_getDevice", None)
+        if getter is not None and get_dev is not None:
+            _raw_stream = lambda: getter(get_dev())
+        else:
+            _raw_stream = lambda: torch.cuda.current_stream().cuda_stream
+    return _raw_stream()
+
+
 def _stream_ptr(stream):
-    import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(_current_stream_handle() if stream is None else stream.cuda_stream)
 
 
 def _ptr(t):
