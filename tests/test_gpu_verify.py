@@ -119,6 +119,31 @@ def test_verify_edges(dtype, V):
         check(tv, dv, xs, prm, seed, i, got)
 
 
+@pytest.mark.parametrize("dtype,K", [("f32", 1), ("bf16", 1), ("f32", 32), ("bf16", 17)])
+def test_verify_draft_lengths(dtype, K):
+    """One draft position and the longest drafts (K + 1 lanes of the finishing
+    wavefront), on many sequences: drafts mostly the target's own draws, so
+    long accepted prefixes occur, with some rows' drafts far from the target."""
+    rng = np.random.default_rng(300 + K)
+    B, V = 200 if K == 1 else 24, 2000
+    tgt = rng.normal(0, 1.5, (B, K + 1, V)).astype(np.float32)
+    noise = np.where(rng.random((B, 1, 1)) < 0.8, 0.05, 1.5)
+    dft = (tgt[:, :K] + rng.normal(0, 1.0, (B, K, V)) * noise).astype(np.float32)
+    if dtype == "bf16":
+        tgt_d, dft_d = wl.f32_to_bf16_bits(tgt), wl.f32_to_bf16_bits(dft)
+    else:
+        tgt_d, dft_d = tgt, dft
+    tv = oracle.values_from_stored(tgt_d, dtype)
+    dv = oracle.values_from_stored(dft_d, dtype)
+    seed = 600 + K
+    for i, prm in enumerate([dict(temperature=1.0), dict(temperature=0.0)]):
+        xs = oracle_drafts(dv, {"temperature": 1.0}, seed, 70 + i)
+        print_case("verify_draft_lengths", dtype=dtype, K=K, params=prm)
+        got = run_verify(seed, tgt_d, dft_d, xs, prm, i, dtype)
+        check(tv, dv, xs, prm, seed, i, got)
+        assert got[1].max() <= K and (got[2] == 0).all()
+
+
 def test_verify_marginal_equals_target():
     """First emitted token follows p whatever the draft (page 4's three-token
     example, 100k sequences)."""
